@@ -1,0 +1,208 @@
+"""Throughput of the block-scaled (grouped) GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--tile ID] [--no-cpu-baseline]
+
+One step = one call of the library entry point for the workload (the whole
+hot path: routing discovery, LDS staging, MFMA, per-block rescale, BF16
+epilogue) on inputs already resident in HBM.  W untimed steps, then exactly
+K timed steps between two synchronisations, timed with HIP events recorded
+on the stream the kernels run on.  Prints one JSON line.
+
+Default workload: grouped FP8 MoE prefill, G=8, M=8192 routed rows in sorted
+runs (multinomial counts, unaligned to 128), N=4096, K=7168.
+
+TFLOPS = 2 * (real rows) * N * K / time; padding rows (m_indices = -1) are
+excluded.  `roofline` prices the kernel against MI355X's published dense
+MFMA peak for the arithmetic it uses.  `cpu_baseline` is the float64 CPU
+oracle timed on a bounded row sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOPS and % of MFMA peak, grouped FP8 / NVFP4 block-scaled GEMM"
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
+PEAK = {"fp8": 5000.0, "fp4": 10100.0, "fp16": 2500.0, "bf16": 2500.0}
+HBM_PEAK = 8000.0
+
+WORKLOADS = {
+    "c2_moe_fp8": dict(kind="fp8", desc="grouped FP8 MoE prefill, G=8, M=8192, N=4096, K=7168"),
+    "c3_skewed_fp8": dict(kind="fp8", desc="skewed grouped FP8, G=32 Zipf(1.2), M=16384 incl. "
+                          "padding, N=2048, K=7168"),
+    "c4_dense_nvfp4": dict(kind="fp4", desc="dense NVFP4, M=2048, N=36864, K=4608"),
+    "c5_moe_nvfp4": dict(kind="fp4", desc="grouped NVFP4 W4A4 MoE prefill, G=8x8192 rows, "
+                         "N=8192, K=8192"),
+    "c1_tiny_fp8": dict(kind="fp8", desc="tiny grouped FP8, G=2, M=256, N=256, K=512"),
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp4_grouped_gemm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != src_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def algorithmic_bytes(p: dict) -> float:
+    """Bytes a launch must move at least once: A rows and scales of real
+    rows, B and its scales of non-empty experts, all of C."""
+    M, N, K, G = p["M"], p["N"], p["K"], p["G"]
+    ids = p.get("m_indices")
+    if p["kind"] == "fp8":
+        real = M if ids is None else int(np.count_nonzero((ids >= 0) & (ids < G)))
+        used = G if ids is None else len(set(ids[(ids >= 0) & (ids < G)].tolist()))
+        return real * K + real * (K // 128) * 4 + used * N * K + used * (N // 128) * (K // 128) * 4 \
+            + M * 4 + M * N * 2
+    real = M if ids is None else int(np.count_nonzero((ids >= 0) & (ids < G)))
+    used = 1 if ids is None else len(set(ids[(ids >= 0) & (ids < G)].tolist()))
+    return real * (K // 2 + K // 16) + used * N * (K // 2 + K // 16) + M * N * 2 + \
+        (0 if ids is None else M * 4)
+
+
+def cpu_baseline(p: dict, C_gpu, budget_rows: int):
+    """Time the oracle on a row sample; also check those rows of the GPU
+    output against it."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    from tests.gpu_util import c_to_f64, row_ids, sample_rows
+    rows = sample_rows(p, budget_rows, seed=1)
+    rows = rows[: budget_rows]
+    ids = row_ids(p, rows)
+    t0 = time.perf_counter()
+    if p["kind"] == "fp8":
+        ref = oracle.grouped_fp8_gemm(p["A"], p["B"], p["a_scale"], p["b_scale"],
+                                      row_ids(p), rows=rows)
+    elif p.get("m_indices") is None:
+        ref = oracle.fp4_gemm(p["A"], p["B"], p["a_scale"], p["b_scale"], p["alpha"], rows=rows)
+    else:
+        ref = oracle.grouped_fp4_gemm(p["A"], p["B"], p["a_scale"], p["b_scale"], row_ids(p),
+                                      p["alpha"], rows=rows)
+    dt = time.perf_counter() - t0
+    real = int(rows.size if ids is None else np.count_nonzero(ids >= 0))
+    flops = 2.0 * real * p["N"] * p["K"]
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    res = oracle.check_tolerance(c_to_f64(C_gpu)[rows], ref, ids)
+    base = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOPS", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows.size} rows ({real} non-padding) x all {p['N']} columns of the same "
+                      f"workload, float64 NumPy/BLAS, {dt:.2f} s"}
+    parity = {"rows": int(rows.size), "ok": bool(res["ok"]), "worst_ratio": round(res["worst_ratio"], 4)}
+    return base, parity
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2_moe_fp8", choices=sorted(WORKLOADS))
+    ap.add_argument("--tile", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of the oracle sample (default: sized for ~10-30 s)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has "
+              "no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fp4_grouped_gemm_amd as fgg
+    from tests.gpu_util import run, to_dev
+    from workloads import make
+    from workloads.gen import real_rows
+
+    if not os.path.exists(fgg.library_path()):
+        from fp4_grouped_gemm_amd.build import build
+        build()
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    p = make(args.workload)
+    d = to_dev(p)
+    kind = WORKLOADS[args.workload]["kind"]
+    M, N, K, G = p["M"], p["N"], p["K"], p["G"]
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    kw = {} if args.tile is None else {"tile_id": args.tile}
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        run(p, d, out=C, **kw)
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        run(p, d, out=C, **kw)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    rr = real_rows(p)
+    flops = 2.0 * rr * N * K
+    tflops = flops / (ms * 1e-3) / 1e12
+    mma = "fp8" if kind == "fp8" else "fp16"
+    src = kernel_source_hash()
+    traffic = measured_traffic(args.workload, src)
+    tiles = fgg.rank_tiles(fgg.FP8 if kind == "fp8" else fgg.FP4, M, N, K, G,
+                           num_cus=fgg.device_info()["num_cus"])
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3" if kind == "fp8" else "nvfp4_e2m1",
+        "data": "synthetic (seeded NumPy; quantised on the host, resident in HBM)",
+        "config": {"workload": args.workload, "desc": WORKLOADS[args.workload]["desc"],
+                   "M": M, "N": N, "K": K, "G": G, "real_rows": rr,
+                   "tile": args.tile if args.tile is not None else tiles[0]["id"],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK[mma],
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK[mma], 4),
+                     "traffic": traffic, "mfma_dtype": mma,
+                     "algorithmic_bytes": algorithmic_bytes(p),
+                     "hbm_gbps_algorithmic": round(algorithmic_bytes(p) / (ms * 1e-3) / 1e9, 1)},
+        "kernel_source_sha": src,
+    }
+    if kind == "fp4":
+        out["roofline"]["frac_of_fp4_peak"] = round(tflops / PEAK["fp4"], 4)
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
+        budget = args.cpu_rows or {"fp8": 1024, "fp4": 512}[kind]
+        base, parity = cpu_baseline(p, C, budget)
+        out["cpu_baseline"] = base
+        out["parity_sample"] = parity
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

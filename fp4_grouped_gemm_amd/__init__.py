@@ -1,0 +1,254 @@
+"""Block-scaled FP8 / NVFP4 (grouped) GEMM for AMD MI355X (gfx950).
+
+Thin Python binding of ``libfgg.so`` (C ABI in include/fgg.h).  The functions
+take PyTorch tensors only as device memory and streams: they check dtypes,
+shapes and devices, derive the sizes, and pass raw pointers plus the current
+HIP stream to the library.  Every step of the computation runs in the
+library's HIP kernels; there is no other code path.  If the library is not
+built, every call raises ``ImportError`` (build it with
+``python -m fp4_grouped_gemm_amd.build``).
+
+Errors reported by the library (bad sizes, alignment, device) raise
+``ValueError`` with the library's message.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "grouped_fp8_gemm", "fp4_gemm", "grouped_fp4_gemm", "rank_tiles", "num_tiles",
+    "device_info", "library_path", "load_library", "FP8", "FP4",
+]
+
+FP8, FP4 = 0, 1
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libfgg.so")
+
+
+class _Tile(ctypes.Structure):
+    _fields_ = [("id", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
+                ("waves", ctypes.c_int), ("wg_per_cu", ctypes.c_int), ("score", ctypes.c_float)]
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [("tile_id", ctypes.c_int), ("max_workgroups", ctypes.c_int)]
+
+
+def load_library():
+    """Load libfgg.so once and declare its C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m fp4_grouped_gemm_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    OPT = ctypes.POINTER(_Options)
+    lib.fgg_last_error.restype = ctypes.c_char_p
+    lib.fgg_last_error.argtypes = []
+    for name, args in (
+        ("grouped_fp8_gemm", [P, P, P, P, P, P, I, I, I, I, P]),
+        ("grouped_fp8_gemm_ex", [P, P, P, P, P, P, I, I, I, I, OPT, P]),
+        ("fp4_gemm", [P, P, P, P, F, P, I, I, I, P]),
+        ("fp4_gemm_ex", [P, P, P, P, F, P, I, I, I, OPT, P]),
+        ("grouped_fp4_gemm", [P, P, P, P, P, F, P, I, I, I, I, P]),
+        ("grouped_fp4_gemm_ex", [P, P, P, P, P, F, P, I, I, I, I, OPT, P]),
+    ):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = args
+    lib.fgg_num_tiles.restype = I
+    lib.fgg_num_tiles.argtypes = [I]
+    lib.fgg_rank_tiles.restype = I
+    lib.fgg_rank_tiles.argtypes = [I, I, I, I, I, I, ctypes.POINTER(_Tile), I]
+    lib.fgg_device_info.restype = I
+    lib.fgg_device_info.argtypes = [ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I),
+                                    ctypes.c_char_p, I]
+    _LIB = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load_library().fgg_last_error().decode(errors="replace")
+        raise ValueError(msg or f"fgg status {status}")
+
+
+def _opts(tile_id, max_workgroups):
+    if tile_id is None and not max_workgroups:
+        return None
+    return ctypes.byref(_Options(-1 if tile_id is None else int(tile_id), int(max_workgroups or 0)))
+
+
+def _torch():
+    import torch  # imported lazily: the C-ABI checks need no torch
+    return torch
+
+
+def _bytes(t, name):
+    """A device tensor of 8-bit codes viewed as uint8 (E4M3 / packed E2M1)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.dtype not in (torch.uint8, torch.int8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+        raise ValueError(f"{name} must hold 8-bit codes (uint8 / float8_e4m3fn), got {t.dtype}")
+    return t.view(torch.uint8)
+
+
+def _dev(t, name, device):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream_ptr(stream, device):
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _out(out, M, N, device):
+    torch = _torch()
+    if out is None:
+        return torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    if out.shape != (M, N) or out.dtype != torch.bfloat16:
+        raise ValueError(f"out must be a bfloat16 tensor of shape ({M}, {N})")
+    return _dev(out, "out", device)
+
+
+def grouped_fp8_gemm(A, B, a_scale, b_scale, m_indices, out=None, *, tile_id=None,
+                     max_workgroups=0, stream=None):
+    """C[M, N] (bfloat16) of the grouped block-scaled FP8 GEMM.
+
+    A [M, K] and B [G, N, K] hold E4M3FN codes; a_scale [M, K/128] and
+    b_scale [G, N/128, K/128] are float32; m_indices [M] is int32 (expert id or
+    -1).  See include/fgg.h for the exact definition.
+    """
+    torch = _torch()
+    A, B = _bytes(A, "A"), _bytes(B, "B")
+    dev = A.device
+    if A.dim() != 2 or B.dim() != 3:
+        raise ValueError("A must be [M, K] and B [G, N, K]")
+    M, K = A.shape
+    G, N, Kb = B.shape
+    if Kb != K:
+        raise ValueError(f"A has K={K} but B has K={Kb}")
+    if a_scale.dtype != torch.float32 or b_scale.dtype != torch.float32:
+        raise ValueError("a_scale and b_scale must be float32")
+    if tuple(a_scale.shape) != (M, K // 128) or tuple(b_scale.shape) != (G, N // 128, K // 128):
+        raise ValueError(f"scale shapes must be ({M}, {K // 128}) and ({G}, {N // 128}, {K // 128})")
+    if m_indices.dtype != torch.int32 or tuple(m_indices.shape) != (M,):
+        raise ValueError(f"m_indices must be int32 of shape ({M},)")
+    for t, n in ((A, "A"), (B, "B"), (a_scale, "a_scale"), (b_scale, "b_scale"),
+                 (m_indices, "m_indices")):
+        _dev(t, n, dev)
+    C = _out(out, M, N, dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _check(lib.grouped_fp8_gemm_ex(A.data_ptr(), B.data_ptr(), a_scale.data_ptr(),
+                                       b_scale.data_ptr(), m_indices.data_ptr(), C.data_ptr(),
+                                       M, N, K, G, _opts(tile_id, max_workgroups),
+                                       _stream_ptr(stream, dev)))
+    return C
+
+
+def _fp4_shapes(A, a_scale, b_scale):
+    torch = _torch()
+    if a_scale.dtype not in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+        raise ValueError("NVFP4 scales must be E4M3 bytes (uint8 / float8_e4m3fn)")
+    if b_scale.dtype != a_scale.dtype:
+        raise ValueError("a_scale and b_scale must have the same dtype")
+    M, K2 = A.shape
+    return M, 2 * K2
+
+
+def fp4_gemm(A, B, a_scale, b_scale, alpha, out=None, *, tile_id=None, max_workgroups=0,
+             stream=None):
+    """C[M, N] (bfloat16) of the dense NVFP4 GEMM: A [M, K/2] and B [N, K/2]
+    packed E2M1, a_scale [M, K/16] and b_scale [N, K/16] E4M3 bytes, alpha =
+    product of the two global scales."""
+    torch = _torch()
+    A, B = _bytes(A, "A"), _bytes(B, "B")
+    dev = A.device
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A must be [M, K/2] and B [N, K/2]")
+    M, K = _fp4_shapes(A, a_scale, b_scale)
+    N = B.shape[0]
+    if B.shape[1] * 2 != K:
+        raise ValueError("A and B disagree on K")
+    sa, sb = _bytes(a_scale, "a_scale"), _bytes(b_scale, "b_scale")
+    if tuple(sa.shape) != (M, K // 16) or tuple(sb.shape) != (N, K // 16):
+        raise ValueError(f"scale shapes must be ({M}, {K // 16}) and ({N}, {K // 16})")
+    for t, n in ((A, "A"), (B, "B"), (sa, "a_scale"), (sb, "b_scale")):
+        _dev(t, n, dev)
+    C = _out(out, M, N, dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _check(lib.fp4_gemm_ex(A.data_ptr(), B.data_ptr(), sa.data_ptr(), sb.data_ptr(),
+                               float(alpha), C.data_ptr(), M, N, K,
+                               _opts(tile_id, max_workgroups), _stream_ptr(stream, dev)))
+    return C
+
+
+def grouped_fp4_gemm(A, B, a_scale, b_scale, m_indices, alpha, out=None, *, tile_id=None,
+                     max_workgroups=0, stream=None):
+    """C[M, N] (bfloat16) of the grouped NVFP4 GEMM: B [G, N, K/2], b_scale
+    [G, N, K/16]; m_indices int32 [M] routes rows (-1 = padding)."""
+    torch = _torch()
+    A, B = _bytes(A, "A"), _bytes(B, "B")
+    dev = A.device
+    if A.dim() != 2 or B.dim() != 3:
+        raise ValueError("A must be [M, K/2] and B [G, N, K/2]")
+    M, K = _fp4_shapes(A, a_scale, b_scale)
+    G, N, K2 = B.shape
+    if K2 * 2 != K:
+        raise ValueError("A and B disagree on K")
+    sa, sb = _bytes(a_scale, "a_scale"), _bytes(b_scale, "b_scale")
+    if tuple(sa.shape) != (M, K // 16) or tuple(sb.shape) != (G, N, K // 16):
+        raise ValueError(f"scale shapes must be ({M}, {K // 16}) and ({G}, {N}, {K // 16})")
+    if m_indices.dtype != torch.int32 or tuple(m_indices.shape) != (M,):
+        raise ValueError(f"m_indices must be int32 of shape ({M},)")
+    for t, n in ((A, "A"), (B, "B"), (sa, "a_scale"), (sb, "b_scale"), (m_indices, "m_indices")):
+        _dev(t, n, dev)
+    C = _out(out, M, N, dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _check(lib.grouped_fp4_gemm_ex(A.data_ptr(), B.data_ptr(), sa.data_ptr(), sb.data_ptr(),
+                                       m_indices.data_ptr(), float(alpha), C.data_ptr(), M, N, K,
+                                       G, _opts(tile_id, max_workgroups), _stream_ptr(stream, dev)))
+    return C
+
+
+def num_tiles(kind: int) -> int:
+    return load_library().fgg_num_tiles(kind)
+
+
+def rank_tiles(kind: int, M: int, N: int, K: int, G: int = 1, num_cus: int = 256):
+    """The ranker's ordered tile configs for a problem (host logic only)."""
+    lib = load_library()
+    n = max(1, lib.fgg_num_tiles(kind))
+    arr = (_Tile * n)()
+    k = lib.fgg_rank_tiles(kind, M, N, K, G, num_cus, arr, n)
+    if k < 0:
+        _check(1)
+    return [dict(id=t.id, block_m=t.block_m, block_n=t.block_n, waves=t.waves,
+                 wg_per_cu=t.wg_per_cu, score=t.score) for t in arr[:k]]
+
+
+def device_info():
+    lib = load_library()
+    cu, lds, clk = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    arch = ctypes.create_string_buffer(64)
+    _check(lib.fgg_device_info(ctypes.byref(cu), ctypes.byref(lds), ctypes.byref(clk), arch, 64))
+    return dict(num_cus=cu.value, lds_per_block=lds.value, clock_khz=clk.value,
+                arch=arch.value.decode())

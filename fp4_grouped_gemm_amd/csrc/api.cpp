@@ -1,0 +1,274 @@
+// C ABI of the block-scaled GEMM library: argument validation, device facts,
+// the tile ranker and dispatch.  Declared in include/fgg.h.
+//
+// Validation follows the pattern of the flashinfer#7877 page's host binding
+// ("Code analysis 1"): every check names the entry point and the violated
+// condition (K a multiple of 128, 16-byte aligned addresses and strides,
+// 1 <= M <= 2^24, 64 <= N <= 2^19 from the launch contract in "Code analysis
+// 2"); here a failed check returns a status and sets a per-thread message
+// instead of raising.  The device check caches gcnArchName once per device,
+// the runtime detection pattern of the sglang#27745 page ("Code analysis 1").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/fgg.h"
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+fgg_status fail(fgg_status st, const char* fn, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = std::string(fn) + ": " + buf;
+  return st;
+}
+
+struct DeviceFacts {
+  bool probed = false;
+  bool ok = false;
+  int num_cus = 0;
+  int lds = 0;
+  int clock_khz = 0;
+  char arch[64] = {0};
+  std::string err;
+};
+
+std::mutex g_dev_mu;
+std::vector<DeviceFacts> g_devs;
+
+// Facts of the current device, probed once.  Returns nullptr and sets the
+// message when no gfx950 device is current.
+const DeviceFacts* current_device(const char* fn, fgg_status* st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    *st = fail(FGG_EDEVICE, fn, "no HIP device available (%s)", hipGetErrorString(e));
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if ((int)g_devs.size() <= dev) g_devs.resize(dev + 1);
+  DeviceFacts& f = g_devs[dev];
+  if (!f.probed) {
+    f.probed = true;
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) {
+      f.err = std::string("hipGetDeviceProperties failed: ") + hipGetErrorString(e);
+    } else {
+      std::snprintf(f.arch, sizeof(f.arch), "%s", p.gcnArchName);
+      f.num_cus = p.multiProcessorCount;
+      f.lds = (int)p.sharedMemPerBlock;
+      f.clock_khz = p.clockRate;
+      f.ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+      if (!f.ok) f.err = std::string("device architecture is ") + p.gcnArchName + ", need gfx950";
+    }
+  }
+  if (!f.ok) {
+    *st = fail(FGG_EDEVICE, fn, "%s", f.err.c_str());
+    return nullptr;
+  }
+  return &f;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape and pointer checks shared by every entry point.  Pure host logic.
+fgg_status check_common(const char* fn, const void* A, const void* B, const void* sa,
+                        const void* sb, const void* C, int M, int N, int K, int G,
+                        bool grouped, const void* m_indices, uintptr_t scale_align) {
+  if (!A || !B || !sa || !sb || !C) return fail(FGG_EINVAL, fn, "null pointer among A, B, a_scale, b_scale, C");
+  if (grouped && !m_indices) return fail(FGG_EINVAL, fn, "m_indices is null");
+  if (M < 1 || M > (1 << 24)) return fail(FGG_EINVAL, fn, "requires 1 <= M <= 2^24, got M=%d", M);
+  if (N < 128 || N > (1 << 19)) return fail(FGG_EINVAL, fn, "requires 128 <= N <= 2^19, got N=%d", N);
+  if (N % 128) return fail(FGG_EINVAL, fn, "requires N %% 128 == 0 (whole b_scale blocks), got N=%d", N);
+  if (K < 128 || K > (1 << 20)) return fail(FGG_EINVAL, fn, "requires 128 <= K <= 2^20, got K=%d", K);
+  if (K % 128) return fail(FGG_EINVAL, fn, "requires K %% 128 == 0, got K=%d", K);
+  if (G < 1 || G > (1 << 16)) return fail(FGG_EINVAL, fn, "requires 1 <= G <= 2^16, got G=%d", G);
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16))
+    return fail(FGG_EALIGN, fn, "A, B and C must be 16-byte aligned");
+  if (!aligned(sa, scale_align) || !aligned(sb, scale_align))
+    return fail(FGG_EALIGN, fn, "a_scale and b_scale must be %d-byte aligned", (int)scale_align);
+  if (grouped && !aligned(m_indices, 4)) return fail(FGG_EALIGN, fn, "m_indices must be 4-byte aligned");
+  return FGG_OK;
+}
+
+// ------------------------------------------------------------------ ranker
+// Score of a tile config, the tile-efficiency x wave-quantisation form of
+// the flashinfer#3948 page ("Code analysis 2"): m_eff * n_eff * throughput /
+// num_waves, with the terms defined for this device:
+//   row_tiles = ceil(M / BM) + (G - 1): every expert boundary that falls
+//               inside a window adds one pass over that window (the routing
+//               is unknown on the host, so each boundary is assumed to);
+//   m_eff     = M / (row_tiles * BM)   useful rows per computed row;
+//   n_eff     = N / (ceil(N / BN) * BN);
+//   num_waves = ceil(tiles / (CUs * wg_per_cu)), and the page's division by
+//               num_waves is normalised to the fraction of workgroup slots
+//               busy, tiles / (num_waves * CUs * wg_per_cu);
+//   throughput= per-CU efficiency of the tile shape.
+// The page's 2-CTA and cluster-multicast factors have no gfx950 counterpart.
+float score_tile(const fgg::TileCfg& t, int M, int N, int G, int num_cus) {
+  const long long windows = (M + t.block_m - 1) / t.block_m;
+  const long long row_tiles = windows + std::min<long long>(G - 1, windows * 4);
+  const long long ntiles = (N + t.block_n - 1) / t.block_n;
+  const double m_eff = (double)M / (double)(row_tiles * t.block_m);
+  const double n_eff = (double)N / (double)(ntiles * t.block_n);
+  const long long tiles = row_tiles * ntiles;
+  const long long slots = (long long)std::max(1, num_cus) * t.wg_per_cu;
+  const long long num_waves = (tiles + slots - 1) / slots;
+  const double busy = (double)tiles / (double)(num_waves * slots);
+  return (float)(std::min(1.0, m_eff) * n_eff * busy * t.tput);
+}
+
+int rank(int kind, int M, int N, int G, int num_cus, fgg_tile* out, int max_out) {
+  const int n = kind == FGG_KIND_FP8 ? fgg::fp8_num_tiles() : fgg::fp4_num_tiles();
+  std::vector<fgg_tile> v;
+  for (int i = 0; i < n; ++i) {
+    const fgg::TileCfg& t = kind == FGG_KIND_FP8 ? fgg::fp8_tile(i) : fgg::fp4_tile(i);
+    fgg_tile r{t.id, t.block_m, t.block_n, t.waves, t.wg_per_cu, score_tile(t, M, N, G, num_cus)};
+    v.push_back(r);
+  }
+  std::stable_sort(v.begin(), v.end(), [](const fgg_tile& a, const fgg_tile& b) { return a.score > b.score; });
+  const int k = std::min<int>(max_out, (int)v.size());
+  for (int i = 0; i < k; ++i) out[i] = v[i];
+  return k;
+}
+
+fgg_status pick_tile(const char* fn, int kind, int M, int N, int G, int num_cus,
+                     const fgg_options* opt, int* tile_id) {
+  const int n = kind == FGG_KIND_FP8 ? fgg::fp8_num_tiles() : fgg::fp4_num_tiles();
+  if (opt && opt->tile_id >= 0) {
+    if (opt->tile_id >= n) return fail(FGG_EINVAL, fn, "tile_id %d out of range [0, %d)", opt->tile_id, n);
+    *tile_id = opt->tile_id;
+    return FGG_OK;
+  }
+  fgg_tile best;
+  rank(kind, M, N, G, num_cus, &best, 1);
+  *tile_id = best.id;
+  return FGG_OK;
+}
+
+fgg_status launched(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(FGG_EHIP, fn, "kernel launch failed: %s", hipGetErrorString(e));
+  g_err.clear();
+  return FGG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fgg_last_error(void) { return g_err.c_str(); }
+
+int fgg_num_tiles(int kind) {
+  if (kind == FGG_KIND_FP8) return fgg::fp8_num_tiles();
+  if (kind == FGG_KIND_FP4) return fgg::fp4_num_tiles();
+  return -1;
+}
+
+int fgg_rank_tiles(int kind, int M, int N, int K, int G, int num_cus, fgg_tile* out, int max_out) {
+  const char* fn = "fgg_rank_tiles";
+  (void)K;
+  if (kind != FGG_KIND_FP8 && kind != FGG_KIND_FP4) return (fail(FGG_EINVAL, fn, "bad kind %d", kind), -1);
+  if (!out || max_out < 1) return (fail(FGG_EINVAL, fn, "need an output array"), -1);
+  if (M < 1 || N < 1 || G < 1) return (fail(FGG_EINVAL, fn, "sizes must be positive"), -1);
+  if (num_cus <= 0) {
+    fgg_status st;
+    const DeviceFacts* d = current_device(fn, &st);
+    if (!d) return -1;
+    num_cus = d->num_cus;
+  }
+  return rank(kind, M, N, G, num_cus, out, max_out);
+}
+
+fgg_status fgg_device_info(int* num_cus, int* lds_per_block, int* clock_khz, char* arch,
+                           int arch_len) {
+  fgg_status st;
+  const DeviceFacts* d = current_device("fgg_device_info", &st);
+  if (!d) return st;
+  if (num_cus) *num_cus = d->num_cus;
+  if (lds_per_block) *lds_per_block = d->lds;
+  if (clock_khz) *clock_khz = d->clock_khz;
+  if (arch && arch_len > 0) std::snprintf(arch, arch_len, "%s", d->arch);
+  return FGG_OK;
+}
+
+fgg_status grouped_fp8_gemm_ex(const void* A, const void* B, const float* a_scale,
+                               const float* b_scale, const int32_t* m_indices, void* C, int M,
+                               int N, int K, int G, const fgg_options* opt, void* stream) {
+  const char* fn = "grouped_fp8_gemm";
+  fgg_status st = check_common(fn, A, B, a_scale, b_scale, C, M, N, K, G, true, m_indices, 4);
+  if (st != FGG_OK) return st;
+  const DeviceFacts* d = current_device(fn, &st);
+  if (!d) return st;
+  int tile;
+  if ((st = pick_tile(fn, FGG_KIND_FP8, M, N, G, d->num_cus, opt, &tile)) != FGG_OK) return st;
+  fgg::Fp8Args a{static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), a_scale, b_scale,
+                 m_indices, static_cast<uint16_t*>(C), M, N, K, G};
+  return launched(fn, fgg::launch_fp8(a, tile, opt ? opt->max_workgroups : 0, d->num_cus,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+fgg_status grouped_fp8_gemm(const void* A, const void* B, const float* a_scale,
+                            const float* b_scale, const int32_t* m_indices, void* C, int M, int N,
+                            int K, int G, void* stream) {
+  return grouped_fp8_gemm_ex(A, B, a_scale, b_scale, m_indices, C, M, N, K, G, nullptr, stream);
+}
+
+static fgg_status fp4_common(const char* fn, const void* A, const void* B, const void* a_scale,
+                             const void* b_scale, const int32_t* m_indices, float alpha, void* C,
+                             int M, int N, int K, int G, bool grouped, const fgg_options* opt,
+                             void* stream) {
+  fgg_status st = check_common(fn, A, B, a_scale, b_scale, C, M, N, K, G, grouped, m_indices, 16);
+  if (st != FGG_OK) return st;
+  if (!std::isfinite(alpha)) return fail(FGG_EINVAL, fn, "alpha must be finite");
+  const DeviceFacts* d = current_device(fn, &st);
+  if (!d) return st;
+  int tile;
+  if ((st = pick_tile(fn, FGG_KIND_FP4, M, N, G, d->num_cus, opt, &tile)) != FGG_OK) return st;
+  fgg::Fp4Args a{static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B),
+                 static_cast<const uint8_t*>(a_scale), static_cast<const uint8_t*>(b_scale),
+                 grouped ? m_indices : nullptr, alpha, static_cast<uint16_t*>(C), M, N, K, G};
+  return launched(fn, fgg::launch_fp4(a, tile, opt ? opt->max_workgroups : 0, d->num_cus,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+fgg_status fp4_gemm_ex(const void* A, const void* B, const void* a_scale, const void* b_scale,
+                       float alpha, void* C, int M, int N, int K, const fgg_options* opt,
+                       void* stream) {
+  return fp4_common("fp4_gemm", A, B, a_scale, b_scale, nullptr, alpha, C, M, N, K, 1, false, opt,
+                    stream);
+}
+
+fgg_status fp4_gemm(const void* A, const void* B, const void* a_scale, const void* b_scale,
+                    float alpha, void* C, int M, int N, int K, void* stream) {
+  return fp4_gemm_ex(A, B, a_scale, b_scale, alpha, C, M, N, K, nullptr, stream);
+}
+
+fgg_status grouped_fp4_gemm_ex(const void* A, const void* B, const void* a_scale,
+                               const void* b_scale, const int32_t* m_indices, float alpha, void* C,
+                               int M, int N, int K, int G, const fgg_options* opt, void* stream) {
+  return fp4_common("grouped_fp4_gemm", A, B, a_scale, b_scale, m_indices, alpha, C, M, N, K, G,
+                    true, opt, stream);
+}
+
+fgg_status grouped_fp4_gemm(const void* A, const void* B, const void* a_scale,
+                            const void* b_scale, const int32_t* m_indices, float alpha, void* C,
+                            int M, int N, int K, int G, void* stream) {
+  return grouped_fp4_gemm_ex(A, B, a_scale, b_scale, m_indices, alpha, C, M, N, K, G, nullptr,
+                             stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+/*
+ * fgg.h -- block-scaled low-precision (grouped) GEMM for AMD MI355X (gfx950).
+ *
+ * C ABI of libfgg.so.  Every pointer argument named A, B, a_scale, b_scale,
+ * m_indices or C is a DEVICE pointer (HIP global memory of the current
+ * device); sizes are plain ints; `stream` is a hipStream_t passed as void*
+ * (NULL = the default stream).  The library reads A, B, the scales and
+ * m_indices, writes every element of C (C need not be initialised), keeps no
+ * pointer after the call returns, allocates no device memory and never
+ * synchronises: work is enqueued on `stream` and the call returns.  It never
+ * reads m_indices on the host, so a call can be captured in a HIP graph and
+ * replayed after the contents of m_indices change.
+ *
+ * Errors: each entry point validates its arguments on the host before
+ * touching the GPU and returns a status; on a non-OK status nothing is
+ * enqueued and fgg_last_error() returns a message (per calling thread) that
+ * names the entry point and the violated condition.  Device faults from bad
+ * pointer *contents* (e.g. a buffer shorter than the sizes say) are not
+ * detectable and are the caller's responsibility.
+ *
+ * Definitions come from the pages on the method (cited by page and section):
+ *  - grouped FP8: flashinfer#7877 page ("cake_grouped_fp8_gemm" window-segment
+ *    program), "Intro" and "Code analysis 1": FP8 E4M3 inputs, BF16 output,
+ *    rows grouped by m_indices, FP32 per-128 block scales, kernel arguments
+ *    A, B, C, a_scale, b_scale, m_indices, M, N, K, G; A is a row-major byte
+ *    matrix whose inner extent K is a multiple of 128 and whose rows may run
+ *    past a tile (tail rows are masked), strides and addresses 16-byte
+ *    aligned; launch contract 1 <= M <= 2^24, 64 <= N <= 2^19.
+ *  - E4M3FN with largest finite value 448 on gfx950: sglang#27745 page,
+ *    "Code analysis 1: FP8 quantisation".
+ *  - NVFP4 W4A4 (E2M1 values, an E4M3 scale per 16 elements, FP32 global
+ *    scale): onnxruntime#29824 page, "Code analysis 1"; dense mm_fp4:
+ *    flashinfer#3948 page.
+ */
+#ifndef FGG_H
+#define FGG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FGG_OK = 0,
+  FGG_EINVAL = 1,   /* null pointer, size out of range, divisibility violated */
+  FGG_EALIGN = 2,   /* a pointer is not 16-byte aligned                        */
+  FGG_EDEVICE = 3,  /* no HIP device, or the current device is not gfx950      */
+  FGG_EHIP = 4      /* a HIP runtime call or kernel launch failed              */
+} fgg_status;
+
+/* Message for the last non-OK status returned on this thread ("" if none).
+ * The pointer stays valid until the next fgg call on the same thread. */
+const char* fgg_last_error(void);
+
+/*
+ * grouped_fp8_gemm -- C = grouped block-scaled FP8 GEMM, BF16 out.
+ *
+ *   A         [M, K]       E4M3FN bytes, row-major (K contiguous)
+ *   B         [G, N, K]    E4M3FN bytes, expert g's weights B[g] row-major
+ *   a_scale   [M, K/128]   float32, row-major: scale of row i, K block kb
+ *   b_scale   [G, N/128, K/128] float32, row-major: scale of the 128x128
+ *                          block (n/128, kb) of B[g]
+ *   m_indices [M]          int32: expert of row i, or -1 for a padding row.
+ *                          Any value outside [-1, G) is treated as -1.  Rows
+ *                          need not be sorted; contiguous runs are fastest.
+ *   C         [M, N]       BF16 (uint16 bits), row-major, written in full
+ *
+ *   C[i, n] = bf16( sum_kb a_scale[i,kb] * b_scale[g,n/128,kb]
+ *                          * sum_{k in kb} A[i,k] * B[g,n,k] ),  g = m_indices[i]
+ *   C[i, :] = 0 when g is -1 (or out of range).
+ *   Accumulation is FP32; the BF16 conversion rounds to nearest even.
+ *
+ * Requirements (else FGG_EINVAL / FGG_EALIGN): 1 <= M <= 2^24,
+ * 128 <= N <= 2^19 with N % 128 == 0, 128 <= K <= 2^20 with K % 128 == 0,
+ * 1 <= G <= 2^16, every pointer non-null and 16-byte aligned (a_scale,
+ * b_scale and m_indices: 4-byte aligned).
+ */
+fgg_status grouped_fp8_gemm(const void* A, const void* B, const float* a_scale,
+                            const float* b_scale, const int32_t* m_indices, void* C,
+                            int M, int N, int K, int G, void* stream);
+
+/*
+ * fp4_gemm -- dense NVFP4 GEMM, BF16 out.
+ *
+ *   A        [M, K/2]   packed E2M1 (element 2j in the low nibble of byte j)
+ *   B        [N, K/2]   packed E2M1, row n holds column n of the product
+ *   a_scale  [M, K/16]  E4M3FN bytes: scale of A's 16-element K block
+ *   b_scale  [N, K/16]  E4M3FN bytes
+ *   alpha    float      product of the two per-tensor FP32 global scales
+ *   C        [M, N]     BF16, row-major, written in full
+ *
+ *   C[i, n] = bf16( alpha * sum_k (A[i,k] a_scale[i,k/16]) (B[n,k] b_scale[n,k/16]) )
+ *
+ * Requirements: 1 <= M <= 2^24, 128 <= N <= 2^19 with N % 128 == 0,
+ * 128 <= K <= 2^20 with K % 128 == 0, pointers non-null and 16-byte aligned.
+ */
+fgg_status fp4_gemm(const void* A, const void* B, const void* a_scale, const void* b_scale,
+                    float alpha, void* C, int M, int N, int K, void* stream);
+
+/*
+ * grouped_fp4_gemm -- grouped NVFP4 GEMM (MoE W4A4), BF16 out.
+ *
+ *   A        [M, K/2]      packed E2M1;   a_scale [M, K/16] E4M3FN bytes
+ *   B        [G, N, K/2]   packed E2M1;   b_scale [G, N, K/16] E4M3FN bytes
+ *   m_indices[M]           int32 expert id or -1 (as for grouped_fp8_gemm)
+ *   alpha                  product of the global scales of A and of B (one
+ *                          global scale for all experts' B)
+ *   C        [M, N]        BF16, written in full; -1 rows are zero
+ *
+ * Requirements: as fp4_gemm plus 1 <= G <= 2^16.
+ */
+fgg_status grouped_fp4_gemm(const void* A, const void* B, const void* a_scale,
+                            const void* b_scale, const int32_t* m_indices, float alpha,
+                            void* C, int M, int N, int K, int G, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Tile configurations and the ranker.
+ *
+ * The kernels are compiled for a small set of tile shapes.  For each call
+ * the host ranks them with a tile-efficiency x wave-quantisation score sized
+ * to the device's compute-unit count (the heuristic-ranking idea of the
+ * flashinfer#3948 page, "Code analysis 2": score = m_eff * n_eff *
+ * throughput / num_waves, with terms defined for this device) and launches
+ * the top one.  These calls are pure host logic and need no GPU.
+ * ------------------------------------------------------------------------ */
+
+typedef enum { FGG_KIND_FP8 = 0, FGG_KIND_FP4 = 1 } fgg_kind;
+
+typedef struct {
+  int id;          /* index of the compiled tile config                     */
+  int block_m;     /* rows per work tile (the row window)                   */
+  int block_n;     /* columns per work tile                                 */
+  int waves;       /* 64-lane wavefronts per workgroup                      */
+  int wg_per_cu;   /* workgroups resident per compute unit                  */
+  float score;     /* ranker score (higher is better); 0 = not applicable   */
+} fgg_tile;
+
+/* Number of compiled tile configs for `kind`, or -1 for a bad kind. */
+int fgg_num_tiles(int kind);
+
+/* Rank every tile config of `kind` for a problem.  `rows_hint` is the
+ * expected number of row tiles' worth of work (pass M when the routing is
+ * unknown); `num_cus` the compute units (256 on MI355X; <= 0 means query the
+ * current device).  Writes up to `max_out` entries, best first, and returns
+ * how many were written, or -1 with fgg_last_error() set. */
+int fgg_rank_tiles(int kind, int M, int N, int K, int G, int num_cus, fgg_tile* out,
+                   int max_out);
+
+/* Optional overrides for the *_ex entry points (NULL = defaults). */
+typedef struct {
+  int tile_id;         /* -1: use the ranker's top choice                    */
+  int max_workgroups;  /* > 0: cap the persistent grid (testing / tuning)    */
+} fgg_options;
+
+fgg_status grouped_fp8_gemm_ex(const void* A, const void* B, const float* a_scale,
+                               const float* b_scale, const int32_t* m_indices, void* C,
+                               int M, int N, int K, int G, const fgg_options* opt,
+                               void* stream);
+fgg_status fp4_gemm_ex(const void* A, const void* B, const void* a_scale, const void* b_scale,
+                       float alpha, void* C, int M, int N, int K, const fgg_options* opt,
+                       void* stream);
+fgg_status grouped_fp4_gemm_ex(const void* A, const void* B, const void* a_scale,
+                               const void* b_scale, const int32_t* m_indices, float alpha,
+                               void* C, int M, int N, int K, int G, const fgg_options* opt,
+                               void* stream);
+
+/* Device facts cached once per device (gfx950 check, CU count, LDS bytes per
+ * workgroup).  Returns FGG_EDEVICE when no usable device is present. */
+fgg_status fgg_device_info(int* num_cus, int* lds_per_block, int* clock_khz, char* arch,
+                           int arch_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FGG_H */

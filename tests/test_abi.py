@@ -1,0 +1,112 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/fgg.h declares, rejects bad arguments before touching a device, and
+ranks tile configs.  No test here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp4_grouped_gemm_amd as fgg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "fgg.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("grouped_fp8_gemm", "fp4_gemm", "grouped_fp4_gemm", "fgg_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(fgg.library_path())
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing
+
+
+P = 0x10000  # a 16-byte aligned non-null address; never dereferenced: each
+# call below fails validation before anything touches a device.
+
+
+def _fp8(A=P, B=P, sa=P, sb=P, mi=P, C=P, M=256, N=256, K=512, G=2):
+    lib = fgg.load_library()
+    st = lib.grouped_fp8_gemm(A, B, sa, sb, mi, C, M, N, K, G, None)
+    return st, lib.fgg_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(A=0), 1, "null"),
+    (dict(mi=0), 1, "m_indices"),
+    (dict(M=0), 1, "M"),
+    (dict(M=(1 << 24) + 1), 1, "M"),
+    (dict(N=64), 1, "N"),
+    (dict(N=200), 1, "N % 128"),
+    (dict(K=200), 1, "K % 128"),
+    (dict(K=64), 1, "K"),
+    (dict(G=0), 1, "G"),
+    (dict(A=P + 8), 2, "aligned"),
+    (dict(C=P + 2), 2, "aligned"),
+    (dict(sa=P + 2), 2, "aligned"),
+])
+def test_fp8_validation(kw, status, needle):
+    st, msg = _fp8(**kw)
+    assert st == status
+    assert msg.startswith("grouped_fp8_gemm:") and needle in msg
+
+
+def test_fp4_validation():
+    lib = fgg.load_library()
+    st = lib.fp4_gemm(P, P, P, P, 1.0, P, 100, 256, 144, None)
+    assert st == 1 and "K % 128" in lib.fgg_last_error().decode()
+    st = lib.fp4_gemm(P, P, P, P, float("inf"), P, 100, 256, 128, None)
+    assert st == 1 and "alpha" in lib.fgg_last_error().decode()
+    st = lib.grouped_fp4_gemm(P, P, P, P, 0, 1.0, P, 100, 256, 128, 2, None)
+    assert st == 1 and "m_indices" in lib.fgg_last_error().decode()
+    st = lib.grouped_fp4_gemm(P, P, P + 4, P, P, 1.0, P, 100, 256, 128, 2, None)
+    assert st == 2
+
+
+def test_python_binding_raises_value_error():
+    torch = pytest.importorskip("torch")
+    A = torch.zeros((4, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        fgg.grouped_fp8_gemm(A, torch.zeros((1, 128, 128), dtype=torch.uint8),
+                             torch.ones((4, 1)), torch.ones((1, 1, 1)),
+                             torch.zeros(4, dtype=torch.int32))  # CPU tensors
+
+
+def test_ranker_orders_and_scores():
+    for kind in (fgg.FP8, fgg.FP4):
+        r = fgg.rank_tiles(kind, 8192, 4096, 7168, 8, num_cus=256)
+        assert len(r) == fgg.num_tiles(kind) >= 1
+        scores = [t["score"] for t in r]
+        assert scores == sorted(scores, reverse=True)
+        assert all(0 < s <= 1 for s in scores)
+
+
+def test_ranker_prefers_full_waves():
+    """With 256 CUs and one workgroup per CU, a problem of exactly 256
+    256x256 tiles fills one wave; the same problem in 128x128 tiles (1024
+    tiles, two per CU) also fills whole waves, so only tile efficiency
+    separates them and the large tile wins.  At 257 tiles the large tile
+    pays a second, nearly empty wave."""
+    full = fgg.rank_tiles(fgg.FP8, 256 * 16, 256 * 16, 1024, 1, num_cus=256)
+    assert (full[0]["block_m"], full[0]["block_n"]) == (256, 256)
+    ragged = fgg.rank_tiles(fgg.FP8, 256 * 16 + 1, 256 * 16, 1024, 1, num_cus=256)
+    top = ragged[0]
+    assert (top["block_m"], top["block_n"]) != (256, 256)
+
+
+def test_device_info_without_gpu():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(ValueError):
+        fgg.device_info()
