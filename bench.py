@@ -91,35 +91,47 @@ def algorithmic_bytes(p: dict) -> float:
         (0 if ids is None else M * 4)
 
 
-def cpu_baseline(p: dict, C_gpu, budget_rows: int):
-    """Time the oracle on a row sample; also check those rows of the GPU
-    output against it."""
+def cpu_baseline(p: dict, C_gpu, seconds: float):
+    """Time the oracle on a bounded row sample of the workload (chunks of
+    rows in a seeded random order until ``seconds`` of CPU work or all rows),
+    and check those rows of the GPU output against it."""
     import oracle
     from threadpoolctl import threadpool_info
 
-    from tests.gpu_util import c_to_f64, row_ids, sample_rows
-    rows = sample_rows(p, budget_rows, seed=1)
-    rows = rows[: budget_rows]
-    ids = row_ids(p, rows)
+    from tests.gpu_util import c_to_f64, row_ids
+    M = p["M"]
+    order = np.random.default_rng(1).permutation(M)
+    ids_all = row_ids(p)
+    done, refs = [], []
     t0 = time.perf_counter()
-    if p["kind"] == "fp8":
-        ref = oracle.grouped_fp8_gemm(p["A"], p["B"], p["a_scale"], p["b_scale"],
-                                      row_ids(p), rows=rows)
-    elif p.get("m_indices") is None:
-        ref = oracle.fp4_gemm(p["A"], p["B"], p["a_scale"], p["b_scale"], p["alpha"], rows=rows)
-    else:
-        ref = oracle.grouped_fp4_gemm(p["A"], p["B"], p["a_scale"], p["b_scale"], row_ids(p),
-                                      p["alpha"], rows=rows)
+    for c0 in range(0, M, 256):
+        rows = np.sort(order[c0:c0 + 256])
+        if p["kind"] == "fp8":
+            r = oracle.grouped_fp8_gemm(p["A"], p["B"], p["a_scale"], p["b_scale"], ids_all,
+                                        rows=rows)
+        elif p.get("m_indices") is None:
+            r = oracle.fp4_gemm(p["A"], p["B"], p["a_scale"], p["b_scale"], p["alpha"], rows=rows)
+        else:
+            r = oracle.grouped_fp4_gemm(p["A"], p["B"], p["a_scale"], p["b_scale"], ids_all,
+                                        p["alpha"], rows=rows)
+        done.append(rows)
+        refs.append(r)
+        if time.perf_counter() - t0 >= seconds:
+            break
     dt = time.perf_counter() - t0
+    rows = np.concatenate(done)
+    ref = np.concatenate(refs)
+    ids = None if ids_all is None else ids_all[rows]
     real = int(rows.size if ids is None else np.count_nonzero(ids >= 0))
     flops = 2.0 * real * p["N"] * p["K"]
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     res = oracle.check_tolerance(c_to_f64(C_gpu)[rows], ref, ids)
     base = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOPS", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{rows.size} rows ({real} non-padding) x all {p['N']} columns of the same "
-                      f"workload, float64 NumPy/BLAS, {dt:.2f} s"}
-    parity = {"rows": int(rows.size), "ok": bool(res["ok"]), "worst_ratio": round(res["worst_ratio"], 4)}
+            "sample": f"{rows.size} of {M} rows ({real} non-padding) x all {p['N']} columns of "
+                      f"the same workload, float64 NumPy/BLAS, {dt:.1f} s"}
+    parity = {"rows": int(rows.size), "ok": bool(res["ok"]),
+              "worst_ratio": round(res["worst_ratio"], 4)}
     return base, parity
 
 
@@ -131,8 +143,8 @@ def main():
     ap.add_argument("--workload", default="c2_moe_fp8", choices=sorted(WORKLOADS))
     ap.add_argument("--tile", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=0,
-                    help="rows of the oracle sample (default: sized for ~10-30 s)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU time budget of the oracle baseline sample")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has "
@@ -197,8 +209,7 @@ def main():
         out["roofline"]["frac_of_fp4_peak"] = round(tflops / PEAK["fp4"], 4)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
-        budget = args.cpu_rows or {"fp8": 1024, "fp4": 512}[kind]
-        base, parity = cpu_baseline(p, C, budget)
+        base, parity = cpu_baseline(p, C, args.cpu_seconds)
         out["cpu_baseline"] = base
         out["parity_sample"] = parity
     print(json.dumps(out), flush=True)
