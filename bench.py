@@ -145,6 +145,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of the GEMM, time a plain 1 GiB device-to-device copy; its "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch calibrate the HBM "
+                         "traffic counters (1 GiB read + 1 GiB written per launch)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has "
@@ -152,6 +156,22 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(7)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 4),
+                          "gbps": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+        return
 
     import fp4_grouped_gemm_amd as fgg
     from tests.gpu_util import run, to_dev

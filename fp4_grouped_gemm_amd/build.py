@@ -3,7 +3,8 @@
     python -m fp4_grouped_gemm_amd.build        (or fp4_grouped_gemm_amd.build.build())
 
 Every source is compiled with hipcc for gfx950 only; packed FP32 VALU
-instructions are disabled (-packed-fp32-ops).  Objects go to _build/ at the
+instructions are disabled (-packed-fp32-ops) and MFMA results are kept in
+VGPRs (-amdgpu-mfma-vgpr-form).  Objects go to _build/ at the
 repository root, the shared library next to this file.
 """
 from __future__ import annotations
@@ -24,6 +25,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the FP8 kernel promotes every partial with VALU
+    # FMAs, which cannot read AGPRs directly.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-command-line-argument",
     "-I" + os.path.join(ROOT, "include"),
 ]

@@ -56,12 +56,17 @@ struct Fp8Cfg {
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one b_scale block");
   static_assert(BM % (16 * WAVES_M) == 0 && BN % (16 * WAVES_N) == 0, "tile shape");
   static_assert(BM % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "load split");
+  static_assert(WAVES % 2 == 0, "the staging swizzle assumes an even wave count");
+  static_assert(WM == 64 && BM <= 512, "one row per lane in the pass masks");
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// LDS byte offset of 16-byte chunk `c` (0..7) of tile row `r`.
-__device__ __forceinline__ int swz(int r, int c) { return (r << 7) | ((c ^ (r & 7)) << 4); }
+// LDS byte offset of 16-byte chunk `c` (0..7) of tile row `r`.  The chunk
+// is XOR-swizzled with bits 1..3 of the row, so the 16 rows that one
+// fragment read touches (128-byte rows, two per 256-byte bank line) land on
+// 16 distinct bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return (r << 7) | ((c ^ ((r >> 1) & 7)) << 4); }
 
 // Fragment of 16 rows x 128 K bytes for v_mfma_*_16x16x128 with 8-bit
 // operands: lane l holds row (l % 16) and K bytes [32 q, 32 q + 32), q = l / 16.
@@ -76,26 +81,109 @@ __device__ __forceinline__ i32x8 read_frag(const uint8_t* tile, int row0, int la
 }
 
 // Wait for this wave's outstanding vector-memory operations (including the
-// direct-to-LDS loads), so that a following barrier publishes their data.
+// loads into LDS), so that a following barrier publishes their data.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Stage the A and B tiles of K step `kb` into LDS stage `st` with direct
-// global->LDS loads (no VGPR staging).
+// Raw buffer resource over [base, base + bytes): loads at offsets past the
+// end return zeros, the out-of-range fill the tail tiles rely on.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Per-pass state: buffer resources, offsets, next scales, accumulators.
+//  * A/B staging: a tile row is K bytes for both operands; lane l of a
+//    1 KB load writes LDS bytes [16 l, 16 l + 16) = tile row 8 b + l / 8,
+//    physical chunk l % 8, so it fetches logical chunk (l % 8) ^ (row % 8).
+//    Load s of wave w covers rows 8 (s W + w) .. + 7, i.e. the lane offset
+//    plus the uniform s * W * 8 * K, plus the step's kb * 128.
 template <class T>
-__device__ __forceinline__ void stage_in(uint8_t* st, const uint8_t* a_base, const uint8_t* b_base,
-                                         const uint32_t (&a_off)[T::A_LOADS],
-                                         const uint32_t (&b_off)[T::B_LOADS], int kb, int wave) {
-  const uint8_t* ga = a_base + (kb << 7);
-  const uint8_t* gb = b_base + (kb << 7);
+struct Pass {
+  __amdgpu_buffer_rsrc_t ra, rb;  // A window rows, B[e] column-tile rows
+  __amdgpu_buffer_rsrc_t rsa;     // a_scale rows of the window
+  uint32_t lane_off;              // (8 w + l / 8) K + 16 chunk
+  uint32_t sa_off;                // (this lane's first row) * nkb * 4
+  uint32_t K;
+  int nkb;
+  const float* bs_row;            // b_scale row of this wave's 128-column block
+  float sa_next[T::TM];
+  float sb_next;
+  uint64_t a_groups;              // 8-row groups of A holding a row of this pass
+  bool active;                    // this wave's 64 rows hold a row of this pass
+  f32x4 acc[T::TM][T::TN];
+
+  __device__ __forceinline__ void stage_in(uint8_t* st, int kb, int wave) const {
 #pragma unroll
-  for (int s = 0; s < T::A_LOADS; ++s)
-    __builtin_amdgcn_global_load_lds(ga + a_off[s], (lds_ptr)(st + (s * T::WAVES + wave) * 1024),
-                                     16, 0, 0);
+    for (int s = 0; s < T::A_LOADS; ++s)
+      if ((a_groups >> (s * T::WAVES + wave)) & 1)  // rows of other experts are not needed
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(st + (s * T::WAVES + wave) * 1024),
+                                                 16, lane_off, s * T::WAVES * 8 * K + kb * 128,
+                                                 0, 0);
 #pragma unroll
-  for (int s = 0; s < T::B_LOADS; ++s)
-    __builtin_amdgcn_global_load_lds(gb + b_off[s],
-                                     (lds_ptr)(st + T::A_BYTES + (s * T::WAVES + wave) * 1024), 16,
-                                     0, 0);
+    for (int s = 0; s < T::B_LOADS; ++s)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (lds_ptr)(st + T::A_BYTES + (s * T::WAVES + wave) * 1024), 16, lane_off,
+          s * T::WAVES * 8 * K + kb * 128, 0, 0);
+  }
+
+  __device__ __forceinline__ void load_scales(int kb) {
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+      sa_next[i] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rsa, sa_off, (i * 16 * nkb + kb) * 4, 0));
+    sb_next = bs_row[kb];
+  }
+};
+
+// One K step: start staging step kb+1 into `wr` (if any), then compute step
+// kb from `rd`.  `rd` and `wr` are distinct __shared__ arrays, which lets the
+// compiler see that the LDS reads of `rd` do not depend on the loads still
+// filling `wr`.  The partial of column subtile j is promoted into the FP32
+// accumulator while the MFMAs of subtile j+1 run.
+template <class T>
+__device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* wr, int kb,
+                                      int lane, int wave, int wm, int wn) {
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  float s[T::TM];
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i) s[i] = ps.sa_next[i] * ps.sb_next;
+  if (kb + 1 < ps.nkb) {
+    ps.stage_in(wr, kb + 1, wave);
+    ps.load_scales(kb + 1);
+  }
+  if (ps.active) {
+  i32x8 af[T::TM];
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i) af[i] = read_frag(rd, wm * T::WM + i * 16, lane);
+  const uint8_t* rb = rd + T::A_BYTES;
+  i32x8 bf = read_frag(rb, wn * T::WN, lane);
+  i32x8 bnext = bf;
+  // MFMA t = (column subtile j, row subtile i) in j-major order; its partial
+  // is promoted LAG MFMAs later, from a small ring, so the FMAs overlap the
+  // following MFMAs and few partials are live at once.
+  constexpr int NT = T::TM * T::TN;
+  constexpr int LAG = 3;
+  f32x4 ring[LAG + 1];
+#pragma unroll
+  for (int t = 0; t < NT + LAG; ++t) {
+    if (t < NT) {
+      const int j = t / T::TM, i = t % T::TM;
+      if (i == 0) {
+        if (j > 0) bf = bnext;
+        if (j + 1 < T::TN) bnext = read_frag(rb, wn * T::WN + (j + 1) * 16, lane);
+      }
+      ring[t % (LAG + 1)] =
+          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], zero, 0, 0, 0, 127, 0, 127);
+    }
+    if (t >= LAG) {
+      const int u = t - LAG;
+      const int j = u / T::TM, i = u % T::TM;
+      ps.acc[i][j] += ring[u % (LAG + 1)] * s[i];
+    }
+  }
+  }
+  wait_vmem();
+  __syncthreads();
 }
 
 template <class T>
@@ -104,16 +192,29 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
     const float* __restrict__ a_scale, const float* __restrict__ b_scale,
     const int32_t* __restrict__ m_indices, uint16_t* __restrict__ C, int M, int N, int K, int G,
     int num_windows, int num_ntiles, int total_tiles, int group_w) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[T::STAGE];
   __shared__ int ids[T::BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / T::WAVES_N;
   const int wn = wave % T::WAVES_N;
   const int nkb = K >> 7;
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+  Pass<T> ps;
+  ps.K = (uint32_t)K;
+  ps.nkb = nkb;
+  // row of this lane inside its load's 8-row group, and its swizzled chunk;
+  // the group's first row 8 (s W + w) has bits 1..3 equal to 4 (w % 2)
+  // because W is even, so the swizzle does not depend on s.
+  {
+    const int r8 = lane >> 3;
+    const int chunk = (lane & 7) ^ ((((wave & 1) << 3) + r8) >> 1 & 7);
+    ps.lane_off = (uint32_t)(wave * 8 + r8) * (uint32_t)K + (uint32_t)(chunk << 4);
+  }
+  ps.sa_off = (uint32_t)(wm * T::WM + (lane & 15)) * (uint32_t)nkb * 4u;
 
   for (int tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
     int window, ntile;
@@ -121,7 +222,7 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
     const int row0 = window * T::BM;
     const int col0 = ntile * T::BN;
 
-    __syncthreads();  // the previous tile is done with ids[] and smem
+    __syncthreads();  // the previous tile is done with ids[] and the stages
     for (int r = tid; r < T::BM; r += T::THREADS) {
       const int gr = row0 + r;
       int e = -2;  // past the end of A: never stored
@@ -142,23 +243,13 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
         *reinterpret_cast<uint4*>(C + (size_t)(row0 + r) * N + col) = make_uint4(0, 0, 0, 0);
     }
 
-    // Per-lane byte offsets of the staged chunks inside the window / column
-    // tile (rows past the end are clamped to the last row: they are loaded
-    // but never stored).  Lane l of a load writes LDS bytes [16 l, 16 l + 16)
-    // of its 1 KB block = tile row 8 b + l / 8, physical chunk l % 8, so it
-    // fetches logical chunk (l % 8) ^ (row % 8) of that row.
-    uint32_t a_off[T::A_LOADS], b_off[T::B_LOADS];
-    const int last_a = M - 1 - row0, last_b = N - 1 - col0;
-#pragma unroll
-    for (int s = 0; s < T::A_LOADS; ++s) {
-      const int r = (s * T::WAVES + wave) * 8 + (lane >> 3);
-      a_off[s] = (uint32_t)min(r, last_a) * (uint32_t)K + (uint32_t)(((lane & 7) ^ (r & 7)) << 4);
-    }
-#pragma unroll
-    for (int s = 0; s < T::B_LOADS; ++s) {
-      const int r = (s * T::WAVES + wave) * 8 + (lane >> 3);
-      b_off[s] = (uint32_t)min(r, last_b) * (uint32_t)K + (uint32_t)(((lane & 7) ^ (r & 7)) << 4);
-    }
+    // Rows (A) and columns (B) of this tile that exist; loads past them
+    // read zeros and those rows / columns are never stored.
+    const int rows_a = min(T::BM, M - row0);
+    const int rows_b = min(T::BN, N - col0);
+    ps.ra = rsrc(A + (size_t)row0 * K, (uint32_t)rows_a * (uint32_t)K);
+    ps.rsa = rsrc(a_scale + (size_t)row0 * nkb, (uint32_t)rows_a * (uint32_t)nkb * 4u);
+    const int wcol0 = col0 + wn * T::WN;
 
     // One pass per distinct expert present in the window, in increasing id.
     int cur = -1;
@@ -168,65 +259,38 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
         const int v = ids[r];
         if (v > cur && v < e) e = v;
       }
-      e = wave_min(e);  // identical in every wave: all take the same passes
+      // identical in every wave, so every wave takes the same passes
+      e = __builtin_amdgcn_readfirstlane(wave_min(e));
       if (e == INT_MAX) break;
       cur = e;
 
-      const uint8_t* a_base = A + (size_t)row0 * K;
-      const uint8_t* b_base = B + ((size_t)e * N + col0) * K;
-      // b_scale row of this wave's 128-column block (wave-uniform).
-      const int wcol0 = col0 + wn * T::WN;
-      const float* bs_row =
-          b_scale + ((size_t)e * (N >> 7) + (min(wcol0, N - 1) >> 7)) * nkb;
-      // a_scale rows of this lane (one per 16-row subtile).
-      uint32_t as_off[T::TM];
+      // Which rows this pass needs: A loads of 8-row groups without a row of
+      // expert e are skipped, and a wave whose 64 rows hold none computes
+      // nothing (a window that straddles a run boundary then costs little
+      // more than its useful rows).
+      {
+        bool g = false;
+        if (lane < T::BM / 8) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) g |= ids[lane * 8 + q] == e;
+        }
+        ps.a_groups = __ballot(g);
+        ps.active = __ballot(ids[wm * T::WM + lane] == e) != 0;
+      }
+      ps.rb = rsrc(B + ((size_t)e * N + col0) * K, (uint32_t)rows_b * (uint32_t)K);
+      ps.bs_row = b_scale + ((size_t)e * (N >> 7) + (min(wcol0, N - 1) >> 7)) * nkb;
 #pragma unroll
       for (int i = 0; i < T::TM; ++i)
-        as_off[i] = (uint32_t)min(wm * T::WM + i * 16 + (lane & 15), last_a) * (uint32_t)nkb;
-      const float* as_base = a_scale + (size_t)row0 * nkb;
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) ps.acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-      f32x4 acc[T::TM][T::TN];
-#pragma unroll
-      for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) acc[i][j] = zero;
-
-      stage_in<T>(smem, a_base, b_base, a_off, b_off, 0, wave);
-      float sa_next[T::TM];
-#pragma unroll
-      for (int i = 0; i < T::TM; ++i) sa_next[i] = as_base[as_off[i]];
-      float sb_next = bs_row[0];
+      ps.stage_in(lds0, 0, wave);
+      ps.load_scales(0);
       wait_vmem();
       __syncthreads();
-
-      for (int kb = 0; kb < nkb; ++kb) {
-        const bool more = kb + 1 < nkb;
-        float s[T::TM];
-#pragma unroll
-        for (int i = 0; i < T::TM; ++i) s[i] = sa_next[i] * sb_next;
-        if (more) {
-          stage_in<T>(smem + ((kb + 1) & 1) * T::STAGE, a_base, b_base, a_off, b_off, kb + 1, wave);
-#pragma unroll
-          for (int i = 0; i < T::TM; ++i) sa_next[i] = as_base[as_off[i] + kb + 1];
-          sb_next = bs_row[kb + 1];
-        }
-        const uint8_t* sA = smem + (kb & 1) * T::STAGE;
-        const uint8_t* sB = sA + T::A_BYTES;
-        i32x8 af[T::TM];
-#pragma unroll
-        for (int i = 0; i < T::TM; ++i) af[i] = read_frag(sA, wm * T::WM + i * 16, lane);
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) {
-          const i32x8 bf = read_frag(sB, wn * T::WN + j * 16, lane);
-#pragma unroll
-          for (int i = 0; i < T::TM; ++i) {
-            const f32x4 p =
-                __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], zero, 0, 0, 0, 127, 0, 127);
-            acc[i][j] += p * s[i];
-          }
-        }
-        wait_vmem();
-        __syncthreads();
+      for (int kb = 0; kb < nkb; kb += 2) {
+        kstep<T>(ps, lds0, lds1, kb, lane, wave, wm, wn);
+        if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, kb + 1, lane, wave, wm, wn);
       }
 
       // Epilogue: this expert's rows only.  Lane holds C[m][n .. n+3].
@@ -241,15 +305,17 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
           const int n = wcol0 + j * 16 + 4 * (lane >> 4);
           if (n < N)
             *reinterpret_cast<uint2*>(crow + n) =
-                pack_bf16x4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+                pack_bf16x4(ps.acc[i][j][0], ps.acc[i][j][1], ps.acc[i][j][2], ps.acc[i][j][3]);
         }
       }
     }
   }
 }
 
-// Compiled tile shapes.  tput is the relative per-CU efficiency the ranker
-// uses; wg_per_cu follows from LDS use (2 stages x (BM + BN) x 128 bytes).
+// Compiled tile shapes.  `tput` is the relative per-CU efficiency the ranker
+// uses, measured once on MI355X from whole-kernel runs of the grouped MoE
+// workloads (256x256 fastest per CU; the 4-wave shapes run one wave per SIMD
+// and hide less latency).  wg_per_cu follows from LDS and VGPR use.
 using Cfg0 = Fp8Cfg<256, 256, 4, 2>;  // 8 waves, 64x128 per wave, 128 KB LDS
 using Cfg1 = Fp8Cfg<256, 128, 4, 1>;  // 4 waves, 64x128 per wave,  96 KB LDS
 using Cfg2 = Fp8Cfg<128, 256, 2, 2>;  // 4 waves, 64x128 per wave,  96 KB LDS
@@ -257,9 +323,9 @@ using Cfg3 = Fp8Cfg<128, 128, 2, 2>;  // 4 waves, 64x64 per wave,   64 KB LDS
 
 const TileCfg kFp8Tiles[] = {
     {0, 256, 256, 8, 1, 1.00f},
-    {1, 256, 128, 4, 1, 0.90f},
-    {2, 128, 256, 4, 1, 0.90f},
-    {3, 128, 128, 4, 2, 0.80f},
+    {1, 256, 128, 4, 1, 0.70f},
+    {2, 128, 256, 4, 1, 0.80f},
+    {3, 128, 128, 4, 2, 0.72f},
 };
 
 template <class T>
