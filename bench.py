@@ -135,6 +135,68 @@ def cpu_baseline(p: dict, C_gpu, seconds: float):
     return base, parity
 
 
+def _csv_rows(path_glob):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(path_glob)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def rocprof_summary(root: str, workload: str, kernel: str, command: str) -> str:
+    """Summarise rocprofv3 CSV output under `root` (subdirectories trace/,
+    fetch/, write/, cfetch/, cwrite/ as written by the profiling commands in
+    the returned text) for kernels whose name contains `kernel`.  Returns the
+    text summary and writes profiles/traffic_<workload>.txt."""
+    def mean(xs):
+        return sum(xs) / len(xs) if xs else float("nan")
+    trace = [r for r in _csv_rows(f"{root}/trace/*kernel_trace.csv") if kernel in r["Kernel_Name"]]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace]
+    stats = [r for r in _csv_rows(f"{root}/trace/*kernel_stats.csv") if kernel in r["Name"]]
+
+    def counter(sub, name, kname):
+        rows = [r for r in _csv_rows(f"{root}/{sub}/*counter_collection.csv")
+                if r["Counter_Name"] == name and kname in r["Kernel_Name"]]
+        return [float(r["Counter_Value"]) for r in rows]
+    fetch = counter("fetch", "FETCH_SIZE", kernel)
+    write = counter("write", "WRITE_SIZE", kernel)
+    cf = counter("cfetch", "FETCH_SIZE", "copyBuffer")
+    cw = counter("cwrite", "WRITE_SIZE", "copyBuffer")
+    gib_kib = float(1 << 20)
+    f_scale = gib_kib / mean(cf) if cf else float("nan")
+    w_scale = gib_kib / mean(cw) if cw else float("nan")
+    hbm = mean(fetch) * 1024 * f_scale + mean(write) * 1024 * w_scale
+    lines = [
+        f"# rocprofv3 summary: {kernel} on {workload}",
+        "",
+        f"command: {command}",
+        f"kernel_source_sha={kernel_source_hash()}",
+        f"dispatches traced: {len(durs)}; mean duration {mean(durs):.2f} us; "
+        f"min {min(durs) if durs else float('nan'):.2f} us; max {max(durs) if durs else float('nan'):.2f} us",
+    ]
+    for r in stats:
+        lines.append("kernel_stats: " + ", ".join(f"{k}={v}" for k, v in r.items()))
+    lines += [
+        f"FETCH_SIZE per dispatch (KiB): mean {mean(fetch):.1f} over {len(fetch)}",
+        f"WRITE_SIZE per dispatch (KiB): mean {mean(write):.1f} over {len(write)}",
+        f"copy calibration (1 GiB read + 1 GiB written): FETCH_SIZE {mean(cf):.1f} KiB, "
+        f"WRITE_SIZE {mean(cw):.1f} KiB -> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}",
+        f"hbm_bytes_per_launch={hbm:.0f}",
+    ]
+    text = "\n".join(lines) + "\n"
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.txt"), "w") as fh:
+        fh.write(f"# HBM traffic of {kernel} on {workload}, from rocprofv3 FETCH_SIZE/WRITE_SIZE\n")
+        fh.write(f"# scaled by a 1 GiB copy calibration (fetch x{f_scale:.4f}, write x{w_scale:.4f})\n")
+        fh.write(f"# command: {command}\n")
+        fh.write(f"kernel_source_sha={kernel_source_hash()}\n")
+        fh.write(f"mean_duration_us={mean(durs):.3f}\n")
+        fh.write(f"hbm_bytes_per_launch={hbm:.0f}\n")
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,11 +207,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample")
+    ap.add_argument("--rocprof-summary", default=None, metavar="DIR",
+                    help="summarise rocprofv3 CSV output in DIR (see rocprof_summary) and exit")
+    ap.add_argument("--kernel", default="fp8_grouped_kernel",
+                    help="kernel-name substring for --rocprof-summary")
+    ap.add_argument("--command", default="", help="profiling command recorded by --rocprof-summary")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the GEMM, time a plain 1 GiB device-to-device copy; its "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch calibrate the HBM "
                          "traffic counters (1 GiB read + 1 GiB written per launch)")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        print(rocprof_summary(args.rocprof_summary, args.workload, args.kernel, args.command))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has "
               "no multi-GPU path.", file=sys.stderr)
