@@ -56,6 +56,9 @@ struct Fp8Cfg {
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one b_scale block");
   static_assert(BM % (16 * WAVES_M) == 0 && BN % (16 * WAVES_N) == 0, "tile shape");
   static_assert(BM % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "load split");
+  // a_scale chunk: BM rows x 8 floats, 64 floats per load instruction
+  static constexpr int SA_LOADS = BM * 8 / 64 / WAVES;
+  static_assert((BM * 8) % (64 * WAVES) == 0, "a_scale chunk split");
   static_assert(WAVES % 2 == 0, "the staging swizzle assumes an even wave count");
   static_assert(WM == 64 && BM <= 512, "one row per lane in the pass masks");
 };
@@ -102,11 +105,9 @@ struct Pass {
   __amdgpu_buffer_rsrc_t ra, rb;  // A window rows, B[e] column-tile rows
   __amdgpu_buffer_rsrc_t rsa;     // a_scale rows of the window
   uint32_t lane_off;              // (8 w + l / 8) K + 16 chunk
-  uint32_t sa_off;                // (this lane's first row) * nkb * 4
   uint32_t K;
   int nkb;
   const float* bs_row;            // b_scale row of this wave's 128-column block
-  float sa_next[T::TM];
   float sb_next;
   uint64_t a_groups;              // 8-row groups of A holding a row of this pass
   bool active;                    // this wave's 64 rows hold a row of this pass
@@ -126,13 +127,20 @@ struct Pass {
           s * T::WAVES * 8 * K + kb * 128, 0, 0);
   }
 
-  __device__ __forceinline__ void load_scales(int kb) {
+  // a_scale values of K blocks [8c, 8c + 8) of every window row, as
+  // [row][8] floats: one 4-byte direct-to-LDS load per lane, 8 lanes per row
+  // (one 32-byte piece per row instead of one cache line per row per step).
+  __device__ __forceinline__ void stage_scales(float* buf, int c, int wave, int lane) const {
 #pragma unroll
-    for (int i = 0; i < T::TM; ++i)
-      sa_next[i] = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(rsa, sa_off, (i * 16 * nkb + kb) * 4, 0));
-    sb_next = bs_row[kb];
+    for (int s = 0; s < T::SA_LOADS; ++s) {
+      const int g = (s * T::WAVES + wave) * 64 + lane;  // row g / 8, block 8c + g % 8
+      const uint32_t off = (uint32_t)(g >> 3) * (uint32_t)nkb * 4u + (uint32_t)(g & 7) * 4u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr)(buf + (s * T::WAVES + wave) * 64), 4,
+                                               off, c * 32, 0, 0);
+    }
   }
+
+  __device__ __forceinline__ void load_b_scale(int kb) { sb_next = bs_row[kb]; }
 };
 
 // One K step: start staging step kb+1 into `wr` (if any), then compute step
@@ -141,15 +149,19 @@ struct Pass {
 // filling `wr`.  The partial of column subtile j is promoted into the FP32
 // accumulator while the MFMAs of subtile j+1 run.
 template <class T>
-__device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* wr, int kb,
-                                      int lane, int wave, int wm, int wn) {
+__device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* wr,
+                                      const float* sa_rd, float* sa_wr, int kb, int lane, int wave,
+                                      int wm, int wn) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  // this step's combined scales; read before any load of this step is issued
   float s[T::TM];
 #pragma unroll
-  for (int i = 0; i < T::TM; ++i) s[i] = ps.sa_next[i] * ps.sb_next;
+  for (int i = 0; i < T::TM; ++i)
+    s[i] = sa_rd[(wm * T::WM + i * 16 + (lane & 15)) * 8 + (kb & 7)] * ps.sb_next;
   if (kb + 1 < ps.nkb) {
     ps.stage_in(wr, kb + 1, wave);
-    ps.load_scales(kb + 1);
+    if ((kb & 7) == 0 && kb + 8 < ps.nkb) ps.stage_scales(sa_wr, (kb >> 3) + 1, wave, lane);
+    ps.load_b_scale(kb + 1);
   }
   if (ps.active) {
   i32x8 af[T::TM];
@@ -194,6 +206,8 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
     int num_windows, int num_ntiles, int total_tiles, int group_w) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[T::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[T::STAGE];
+  __shared__ __attribute__((aligned(256))) float sa0[T::BM * 8];
+  __shared__ __attribute__((aligned(256))) float sa1[T::BM * 8];
   __shared__ int ids[T::BM];
 
   const int tid = threadIdx.x;
@@ -214,7 +228,6 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
     const int chunk = (lane & 7) ^ ((((wave & 1) << 3) + r8) >> 1 & 7);
     ps.lane_off = (uint32_t)(wave * 8 + r8) * (uint32_t)K + (uint32_t)(chunk << 4);
   }
-  ps.sa_off = (uint32_t)(wm * T::WM + (lane & 15)) * (uint32_t)nkb * 4u;
 
   for (int tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
     int window, ntile;
@@ -285,12 +298,18 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
         for (int j = 0; j < T::TN; ++j) ps.acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
       ps.stage_in(lds0, 0, wave);
-      ps.load_scales(0);
+      ps.stage_scales(sa0, 0, wave, lane);
+      ps.load_b_scale(0);
       wait_vmem();
       __syncthreads();
+      // K steps two at a time (LDS stage parity), scale chunks of 8 steps
+      // alternate between sa0 and sa1.
       for (int kb = 0; kb < nkb; kb += 2) {
-        kstep<T>(ps, lds0, lds1, kb, lane, wave, wm, wn);
-        if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, kb + 1, lane, wave, wm, wn);
+        const bool odd_chunk = (kb >> 3) & 1;
+        float* sa_rd = odd_chunk ? sa1 : sa0;
+        float* sa_wr = odd_chunk ? sa0 : sa1;
+        kstep<T>(ps, lds0, lds1, sa_rd, sa_wr, kb, lane, wave, wm, wn);
+        if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa_rd, sa_wr, kb + 1, lane, wave, wm, wn);
       }
 
       // Epilogue: this expert's rows only.  Lane holds C[m][n .. n+3].
@@ -323,9 +342,9 @@ using Cfg3 = Fp8Cfg<128, 128, 2, 2>;  // 4 waves, 64x64 per wave,   64 KB LDS
 
 const TileCfg kFp8Tiles[] = {
     {0, 256, 256, 8, 1, 1.00f},
-    {1, 256, 128, 4, 1, 0.70f},
+    {1, 256, 128, 4, 1, 0.67f},
     {2, 128, 256, 4, 1, 0.80f},
-    {3, 128, 128, 4, 2, 0.72f},
+    {3, 128, 128, 4, 2, 0.80f},
 };
 
 template <class T>
@@ -337,11 +356,10 @@ hipError_t launch_cfg(const Fp8Args& a, int max_wg, int num_cus, hipStream_t s) 
   if (total > INT_MAX) return hipErrorInvalidValue;
   int grid = (int)total;
   if (max_wg > 0 && max_wg < grid) grid = max_wg;
-  // Row windows per tile group: enough that one XCD's resident workgroups
-  // cover a compact block of windows x column tiles.
-  const int per_xcd = (num_cus > 0 ? num_cus : 256) / kXcds;
-  int group_w = per_xcd / (num_ntiles < 8 ? num_ntiles : 8);
-  if (group_w < 1) group_w = 1;
+  // Row windows per tile group (all column tiles of a group run in one XCD,
+  // window fastest): 8 windows measured best on MI355X for the MoE shapes.
+  (void)num_cus;
+  const int group_w = 8;
   hipLaunchKernelGGL(fp8_grouped_kernel<T>, dim3(grid), dim3(T::THREADS), 0, s, a.A, a.B,
                      a.a_scale, a.b_scale, a.m_indices, a.C, a.M, a.N, a.K, a.G, num_windows,
                      num_ntiles, (int)total, group_w);
