@@ -25,6 +25,7 @@
 #include "common.h"
 
 #include <climits>
+#include <utility>
 
 namespace fgg {
 namespace fp4_detail {
@@ -51,37 +52,35 @@ struct Fp4Cfg {
   static constexpr int B_UNITS = BN * 2 / THREADS;
   static_assert((BM * 2) % THREADS == 0 && (BN * 2) % THREADS == 0, "staging split");
   static_assert(BM % (16 * WAVES_M) == 0 && BN % (16 * WAVES_N) == 0, "tile shape");
+  static_assert(WM == 64, "one row per lane in the pass masks");
 };
 
 __device__ __forceinline__ int swz(int r, int c) { return (r << 7) | ((c ^ (r & 7)) << 4); }
 
-// E4M3FN code -> its value as FP16 (exact: 4 significant bits, 2^-9..448).
-__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t c) {
-  const uint32_t E = (c >> 3) & 15u, M = c & 7u;
-  float f = E ? __uint_as_float(((E + 120u) << 23) | (M << 20)) : (float)M * 0.001953125f;
-  if (c & 0x80u) f = -f;
-  return (_Float16)f;
+// Two E4M3FN codes (bytes 0 and 1 of `sc`) -> their values as an FP16 pair.
+// Exact: E4M3 has 4 significant bits and spans 2^-9..448.  The code's bits
+// are placed into the FP16 fields (exponent bits at the bottom of FP16's
+// exponent, mantissa at the top of its mantissa, subnormals to subnormals),
+// which gives the value times 2^-8 in both the normal and the subnormal
+// range; one multiply by 256 restores it.
+__device__ __forceinline__ f16x2 e4m3x2_to_f16x2(uint32_t sc) {
+  const uint32_t x = (sc & 0xFFu) | ((sc & 0xFF00u) << 8);
+  const uint32_t bits = ((x & 0x007F007Fu) << 7) | ((x & 0x00800080u) << 8);
+  return __builtin_bit_cast(f16x2, bits) * (f16x2){(_Float16)256.0f, (_Float16)256.0f};
 }
 
-// 16 packed bytes (32 E2M1 codes) and the two E4M3 scale codes of their
-// 16-element blocks (bytes 0-7 -> scale0, bytes 8-15 -> scale1) -> 32 FP16
-// values q * s in 4 x 16 bytes.  The hardware convert decodes two E2M1
-// codes of one byte (scale 1.0, so it is exact whatever the convert does with
-// a scale's mantissa); the multiply by the block scale is exact in FP16.
-__device__ __forceinline__ void dequant32(const i32x4 packed, uint32_t sc, i32x4 out[4]) {
-  const _Float16 s0 = e4m3_to_f16(sc & 0xFFu), s1 = e4m3_to_f16((sc >> 8) & 0xFFu);
-  const f16x2 ss0 = {s0, s0}, ss1 = {s1, s1};
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t word = (uint32_t)packed[w];
-    const f16x2 ss = w < 2 ? ss0 : ss1;
-    f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * ss;
-    f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * ss;
-    f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * ss;
-    f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * ss;
-    out[w] = (i32x4){__builtin_bit_cast(int, v0), __builtin_bit_cast(int, v1),
-                     __builtin_bit_cast(int, v2), __builtin_bit_cast(int, v3)};
-  }
+// One 32-bit word (8 E2M1 codes, low nibble first) times its block scale ->
+// 8 FP16 values in 16 bytes.  The hardware convert decodes the two codes of
+// one byte; its scale operand contributes only a power of two, so it is 1.0
+// here and the block scale is applied by an FP16 multiply, exact because
+// q * s has at most 6 significant bits and lies in [2^-10, 2688].
+__device__ __forceinline__ i32x4 dequant_word(uint32_t word, f16x2 ss) {
+  const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * ss;
+  const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * ss;
+  const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * ss;
+  const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * ss;
+  return (i32x4){__builtin_bit_cast(int, v0), __builtin_bit_cast(int, v1),
+                 __builtin_bit_cast(int, v2), __builtin_bit_cast(int, v3)};
 }
 
 // Fragment for v_mfma_f32_16x16x32_f16: lane l holds row (l % 16) and the
@@ -92,24 +91,162 @@ __device__ __forceinline__ f16x8 read_frag(const uint8_t* tile, int row0, int la
   return *reinterpret_cast<const f16x8*>(tile + swz(r, kk * 4 + (lane >> 4)));
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// A buffer offset past every buffer's end (buffers are below 2^31 bytes):
+// a load there returns zeros.
+constexpr uint32_t kSkip = 0x80000000u;
+
+// Packed E2M1 bytes and E4M3 scale pair of one staging unit, in registers.
+struct Unit {
+  i32x4 q;
+  uint16_t sc;  // kept 16-bit: a widening at the loop back edge would wait for the load
+};
+
+// Per-pass state.  Staging units: unit u of this thread covers tile row
+// u / 2, elements [32 (u % 2), 32 (u % 2) + 32) of the K step.
+template <class T>
+struct Pass {
+  __amdgpu_buffer_rsrc_t ra, rsa, rb, rsb;  // window rows of A / a_scale, tile rows of B / b_scale
+  uint32_t a_off[T::A_UNITS], as_off[T::A_UNITS], b_off[T::B_UNITS], bs_off[T::B_UNITS];
+  // This pass's A offsets: those of rows of other experts are moved past the
+  // end of the buffer, so their loads return zeros without touching memory
+  // (a branch-free skip; the zeros are never stored).
+  uint32_t pa_off[T::A_UNITS], pas_off[T::A_UNITS];
+  Unit ua[2][T::A_UNITS], ub[2][T::B_UNITS];  // two tiles in flight
+  f32x4 acc[T::TM][T::TN];
+
+  // Issue the loads of K step ks into register set `set`.
+  __device__ __forceinline__ void load(int set, int ks) {
+#pragma unroll
+    for (int u = 0; u < T::A_UNITS; ++u) {
+      ua[set][u].q = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, pa_off[u], ks * (T::BK / 2), 0));
+      ua[set][u].sc = __builtin_amdgcn_raw_buffer_load_b16(rsa, pas_off[u], ks * (T::BK / 16), 0);
+    }
+#pragma unroll
+    for (int u = 0; u < T::B_UNITS; ++u) {
+      ub[set][u].q = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[u], ks * (T::BK / 2), 0));
+      ub[set][u].sc = __builtin_amdgcn_raw_buffer_load_b16(rsb, bs_off[u], ks * (T::BK / 16), 0);
+    }
+  }
+
+  // Chunk c of this thread's staging work for register set `set`: unit
+  // c / 4 (A units first, then B units), 16-byte word c % 4 of it,
+  // dequantised and written to LDS stage `st`.  Word 0 also decodes the
+  // unit's two block scales (words 0-1 use the first, words 2-3 the second).
+  f16x2 sdec[T::A_UNITS + T::B_UNITS];
+  __device__ __forceinline__ void stage_chunk(int set, int c, uint8_t* st, int tid) {
+    const int u = c >> 2, w = c & 3;
+    const bool is_a = u < T::A_UNITS;
+    const Unit& un = is_a ? ua[set][u] : ub[set][u - T::A_UNITS];
+    if (w == 0) sdec[u] = e4m3x2_to_f16x2(un.sc);
+    const _Float16 s = w < 2 ? sdec[u][0] : sdec[u][1];
+    const int g = tid + (is_a ? u : u - T::A_UNITS) * T::THREADS;
+    uint8_t* dst = st + (is_a ? 0 : T::A_BYTES) + swz(g >> 1, (g & 1) * 4 + w);
+    *reinterpret_cast<i32x4*>(dst) = dequant_word((uint32_t)un.q[w], (f16x2){s, s});
+  }
+  static constexpr int CHUNKS = 4 * (T::A_UNITS + T::B_UNITS);
+  __device__ __forceinline__ void stage_all(int set, uint8_t* st, int tid) {
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) stage_chunk(set, c, st, tid);
+  }
+};
+
+// Workgroup barrier ordering LDS accesses only.  __syncthreads() orders
+// global memory too, which waits for every load in flight, the look-ahead
+// loads included; nothing here shares global memory between waves.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// The MFMAs of one K step from LDS stage `rd`, as 2 x TN slots (a K=32 half,
+// one 16-column block of B: TM MFMAs).  With STAGE, slot k also stages chunks
+// [k C / S, (k+1) C / S) of the next step (C chunks, S slots) from register
+// set `set` into `wr`, so the dequantisation VALU work and LDS writes are
+// spread evenly between the MFMAs of the wave; the scheduling fence after
+// each slot keeps that spread.
+template <class T, bool STAGE>
+__device__ __forceinline__ void mma_step(Pass<T>& ps, const uint8_t* rd, uint8_t* wr, int set,
+                                         int tid, int lane, int wm, int wn) {
+  constexpr int S = 2 * T::TN, C = Pass<T>::CHUNKS;
+  const uint8_t* rb = rd + T::A_BYTES;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    f16x8 af[T::TM];
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) af[i] = read_frag(rd, wm * T::WM + i * 16, lane, h);
+    f16x8 bnext = read_frag(rb, wn * T::WN, lane, h);
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) {
+      const f16x8 bf = bnext;
+      if (j + 1 < T::TN) bnext = read_frag(rb, wn * T::WN + (j + 1) * 16, lane, h);
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i)
+        ps.acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, af[i], ps.acc[i][j], 0, 0, 0);
+      if constexpr (STAGE) {
+        const int k = h * T::TN + j;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+          if (c * S / C == k) ps.stage_chunk(set, c, wr, tid);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// One K step from `rd` that also stages the next one: issue the loads of
+// step `ks_load` into register set `set` (free: its previous contents were
+// staged in the previous step), then the MFMAs with the next step (register
+// set set ^ 1, loaded one step ago) staged into `wr` between them.  Every
+// step issues the same loads (the last ones reload the last step), so the
+// waits before the dequantisation count only the loads of set ^ 1.
+template <class T>
+__device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* wr, int set,
+                                      int ks_load, int tid, int lane, int wm, int wn) {
+  ps.load(set, ks_load);
+  mma_step<T, true>(ps, rd, wr, set ^ 1, tid, lane, wm, wn);
+  lds_barrier();
+}
+
 template <class T>
 __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ a_scale, const uint8_t* __restrict__ b_scale,
     const int32_t* __restrict__ m_indices, float alpha, uint16_t* __restrict__ C, int M, int N,
     int K, int G, int num_windows, int num_ntiles, int total_tiles, int group_w) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[T::STAGE];
   __shared__ int ids[T::BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / T::WAVES_N;
   const int wn = wave % T::WAVES_N;
   const int nks = K / T::BK;
-  const int Kp = K >> 1;   // packed bytes per row
-  const int Ks = K >> 4;   // scale bytes per row
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t Kp = (uint32_t)K >> 1;  // packed bytes per row
+  const uint32_t Ks = (uint32_t)K >> 4;  // scale bytes per row
+
+  Pass<T> ps;
+#pragma unroll
+  for (int u = 0; u < T::A_UNITS; ++u) {
+    const int g = tid + u * T::THREADS;
+    ps.a_off[u] = (uint32_t)(g >> 1) * Kp + (uint32_t)(g & 1) * 16u;
+    ps.as_off[u] = (uint32_t)(g >> 1) * Ks + (uint32_t)(g & 1) * 2u;
+  }
+#pragma unroll
+  for (int u = 0; u < T::B_UNITS; ++u) {
+    const int g = tid + u * T::THREADS;
+    ps.b_off[u] = (uint32_t)(g >> 1) * Kp + (uint32_t)(g & 1) * 16u;
+    ps.bs_off[u] = (uint32_t)(g >> 1) * Ks + (uint32_t)(g & 1) * 2u;
+  }
 
   for (int tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
     int window, ntile;
@@ -117,10 +254,10 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
     const int row0 = window * T::BM;
     const int col0 = ntile * T::BN;
 
-    __syncthreads();
+    __syncthreads();  // the previous tile is done with ids[] and the stages
     for (int r = tid; r < T::BM; r += T::THREADS) {
       const int gr = row0 + r;
-      int e = -2;
+      int e = -2;  // past the end of A: never stored
       if (gr < M) {
         e = m_indices ? m_indices[gr] : 0;
         if (e < -1 || e >= G) e = -1;
@@ -137,22 +274,13 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
         *reinterpret_cast<uint4*>(C + (size_t)(row0 + r) * N + col) = make_uint4(0, 0, 0, 0);
     }
 
-    // Staging units of this thread: tile row and half (0: elements 0-31 of
-    // the step, 1: 32-63).  Rows past the end are clamped (never stored).
-    int a_row[T::A_UNITS], b_row[T::B_UNITS], a_half[T::A_UNITS], b_half[T::B_UNITS];
-#pragma unroll
-    for (int s = 0; s < T::A_UNITS; ++s) {
-      const int u = tid + s * T::THREADS;
-      a_row[s] = u >> 1;
-      a_half[s] = u & 1;
-    }
-#pragma unroll
-    for (int s = 0; s < T::B_UNITS; ++s) {
-      const int u = tid + s * T::THREADS;
-      b_row[s] = u >> 1;
-      b_half[s] = u & 1;
-    }
-    const int last_a = M - 1 - row0, last_b = N - 1 - col0;
+    // Rows (A) and columns (B) of this tile that exist: loads past them read
+    // zeros, and those rows / columns are never stored.
+    const uint32_t rows_a = (uint32_t)min(T::BM, M - row0);
+    const uint32_t rows_b = (uint32_t)min(T::BN, N - col0);
+    ps.ra = rsrc(A + (size_t)row0 * Kp, rows_a * Kp);
+    ps.rsa = rsrc(a_scale + (size_t)row0 * Ks, rows_a * Ks);
+    const int wcol0 = col0 + wn * T::WN;
 
     int cur = -1;
     while (true) {
@@ -161,119 +289,35 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
         const int v = ids[r];
         if (v > cur && v < e) e = v;
       }
-      e = wave_min(e);
+      e = __builtin_amdgcn_readfirstlane(wave_min(e));  // same in every wave
       if (e == INT_MAX) break;
       cur = e;
 
-      const uint8_t* Bg = B + (size_t)e * N * Kp;
-      const uint8_t* Sg = b_scale + (size_t)e * N * Ks;
-      const uint8_t* a_src[T::A_UNITS];
-      const uint8_t* as_src[T::A_UNITS];
-      const uint8_t* b_src[T::B_UNITS];
-      const uint8_t* bs_src[T::B_UNITS];
 #pragma unroll
-      for (int s = 0; s < T::A_UNITS; ++s) {
-        const size_t gr = (size_t)(row0 + min(a_row[s], last_a));
-        a_src[s] = A + gr * Kp + a_half[s] * 16;
-        as_src[s] = a_scale + gr * Ks + a_half[s] * 2;
+      for (int u = 0; u < T::A_UNITS; ++u) {
+        const bool need = ids[(tid + u * T::THREADS) >> 1] == e;
+        ps.pa_off[u] = need ? ps.a_off[u] : kSkip;
+        ps.pas_off[u] = need ? ps.as_off[u] : kSkip;
       }
-#pragma unroll
-      for (int s = 0; s < T::B_UNITS; ++s) {
-        const size_t gn = (size_t)(col0 + min(b_row[s], last_b));
-        b_src[s] = Bg + gn * Kp + b_half[s] * 16;
-        bs_src[s] = Sg + gn * Ks + b_half[s] * 2;
-      }
-
-      f32x4 acc[T::TM][T::TN];
+      ps.rb = rsrc(B + ((size_t)e * N + col0) * Kp, rows_b * Kp);
+      ps.rsb = rsrc(b_scale + ((size_t)e * N + col0) * Ks, rows_b * Ks);
 #pragma unroll
       for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < T::TN; ++j) acc[i][j] = zero;
+        for (int j = 0; j < T::TN; ++j) ps.acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-      i32x4 ra[T::A_UNITS], rb[T::B_UNITS];
-      uint32_t rsa[T::A_UNITS], rsb[T::B_UNITS];
-#pragma unroll
-      for (int s = 0; s < T::A_UNITS; ++s) {
-        ra[s] = *reinterpret_cast<const i32x4*>(a_src[s]);
-        rsa[s] = *reinterpret_cast<const uint16_t*>(as_src[s]);
-      }
-#pragma unroll
-      for (int s = 0; s < T::B_UNITS; ++s) {
-        rb[s] = *reinterpret_cast<const i32x4*>(b_src[s]);
-        rsb[s] = *reinterpret_cast<const uint16_t*>(bs_src[s]);
-      }
-      // dequantise step 0 into stage 0
-#pragma unroll
-      for (int s = 0; s < T::A_UNITS; ++s) {
-        i32x4 o[4];
-        dequant32(ra[s], rsa[s], o);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          *reinterpret_cast<i32x4*>(smem + swz(a_row[s], a_half[s] * 4 + c)) = o[c];
-      }
-#pragma unroll
-      for (int s = 0; s < T::B_UNITS; ++s) {
-        i32x4 o[4];
-        dequant32(rb[s], rsb[s], o);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          *reinterpret_cast<i32x4*>(smem + T::A_BYTES + swz(b_row[s], b_half[s] * 4 + c)) = o[c];
-      }
-      __syncthreads();
-
-      for (int ks = 0; ks < nks; ++ks) {
-        const bool more = ks + 1 < nks;
-        if (more) {
-          const int po = (ks + 1) * (T::BK / 2), so = (ks + 1) * (T::BK / 16);
-#pragma unroll
-          for (int s = 0; s < T::A_UNITS; ++s) {
-            ra[s] = *reinterpret_cast<const i32x4*>(a_src[s] + po);
-            rsa[s] = *reinterpret_cast<const uint16_t*>(as_src[s] + so);
-          }
-#pragma unroll
-          for (int s = 0; s < T::B_UNITS; ++s) {
-            rb[s] = *reinterpret_cast<const i32x4*>(b_src[s] + po);
-            rsb[s] = *reinterpret_cast<const uint16_t*>(bs_src[s] + so);
-          }
-        }
-        const uint8_t* sA = smem + (ks & 1) * T::STAGE;
-        const uint8_t* sB = sA + T::A_BYTES;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          f16x8 af[T::TM];
-#pragma unroll
-          for (int i = 0; i < T::TM; ++i) af[i] = read_frag(sA, wm * T::WM + i * 16, lane, kk);
-#pragma unroll
-          for (int j = 0; j < T::TN; ++j) {
-            const f16x8 bf = read_frag(sB, wn * T::WN + j * 16, lane, kk);
-#pragma unroll
-            for (int i = 0; i < T::TM; ++i)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, af[i], acc[i][j], 0, 0, 0);
-          }
-        }
-        if (more) {
-          uint8_t* nxt = smem + ((ks + 1) & 1) * T::STAGE;
-#pragma unroll
-          for (int s = 0; s < T::A_UNITS; ++s) {
-            i32x4 o[4];
-            dequant32(ra[s], rsa[s], o);
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-              *reinterpret_cast<i32x4*>(nxt + swz(a_row[s], a_half[s] * 4 + c)) = o[c];
-          }
-#pragma unroll
-          for (int s = 0; s < T::B_UNITS; ++s) {
-            i32x4 o[4];
-            dequant32(rb[s], rsb[s], o);
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-              *reinterpret_cast<i32x4*>(nxt + T::A_BYTES + swz(b_row[s], b_half[s] * 4 + c)) = o[c];
-          }
-        }
-        __syncthreads();
+      ps.load(0, 0);
+      ps.load(1, min(1, nks - 1));
+      ps.stage_all(0, lds0, tid);
+      lds_barrier();
+      // Steps in pairs so that register set and LDS stage are known at
+      // compile time.  The last step also stages (a reload of itself, into
+      // the stage nobody reads any more), which keeps one loop body.
+      for (int ks = 0; ks < nks; ks += 2) {
+        kstep<T>(ps, lds0, lds1, 0, min(ks + 2, nks - 1), tid, lane, wm, wn);
+        if (ks + 1 < nks) kstep<T>(ps, lds1, lds0, 1, min(ks + 3, nks - 1), tid, lane, wm, wn);
       }
 
-      const int wcol0 = col0 + wn * T::WN;
 #pragma unroll
       for (int i = 0; i < T::TM; ++i) {
         const int rl = wm * T::WM + i * 16 + (lane & 15);
@@ -285,8 +329,8 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
           const int n = wcol0 + j * 16 + 4 * (lane >> 4);
           if (n < N)
             *reinterpret_cast<uint2*>(crow + n) =
-                pack_bf16x4(alpha * acc[i][j][0], alpha * acc[i][j][1], alpha * acc[i][j][2],
-                            alpha * acc[i][j][3]);
+                pack_bf16x4(alpha * ps.acc[i][j][0], alpha * ps.acc[i][j][1],
+                            alpha * ps.acc[i][j][2], alpha * ps.acc[i][j][3]);
         }
       }
     }
@@ -314,9 +358,8 @@ hipError_t launch_cfg(const Fp4Args& a, int max_wg, int num_cus, hipStream_t s) 
   if (total > INT_MAX) return hipErrorInvalidValue;
   int grid = (int)total;
   if (max_wg > 0 && max_wg < grid) grid = max_wg;
-  const int per_xcd = (num_cus > 0 ? num_cus : 256) / kXcds;
-  int group_w = per_xcd / (num_ntiles < 8 ? num_ntiles : 8);
-  if (group_w < 1) group_w = 1;
+  (void)num_cus;
+  const int group_w = 8;  // row windows per XCD tile group
   hipLaunchKernelGGL(fp4_gemm_kernel<T>, dim3(grid), dim3(T::THREADS), 0, s, a.A, a.B, a.a_scale,
                      a.b_scale, a.m_indices, a.alpha, a.C, a.M, a.N, a.K, a.G, num_windows,
                      num_ntiles, (int)total, group_w);
