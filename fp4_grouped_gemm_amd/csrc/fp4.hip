@@ -344,9 +344,9 @@ using Cfg3 = Fp4Cfg<128, 128, 2, 2>;  // 4 waves, 64x64 per wave,   64 KB LDS
 
 const TileCfg kFp4Tiles[] = {
     {0, 256, 256, 8, 1, 1.00f},
-    {1, 256, 128, 4, 1, 0.90f},
-    {2, 128, 256, 4, 1, 0.90f},
-    {3, 128, 128, 4, 2, 0.80f},
+    {1, 256, 128, 4, 1, 0.80f},
+    {2, 128, 256, 4, 1, 0.80f},
+    {3, 128, 128, 4, 2, 0.76f},
 };
 
 template <class T>

@@ -14,10 +14,12 @@
 //    launch, never on the host -- and runs one pass of the K loop per
 //    expert, storing only that expert's rows.  Padding rows are zero-filled.
 //  * K step = 128 = one scale block.  Each step stages a BM x 128 A tile and
-//    a BN x 128 B tile in LDS (two stages: the next step's global loads are
-//    in flight while the current step computes), 16-byte coalesced loads, an
-//    XOR swizzle of 16-byte chunks by row so fragment reads hit distinct
-//    banks.
+//    a BN x 128 B tile in LDS through a ring of 2 or 3 stages: the loads of
+//    step k + STAGES - 1 are issued at the start of step k, so with 3 stages
+//    every load has two steps to arrive and the latency of the next batch
+//    overlaps the transfer of the previous one (the 256x256 shape only fits
+//    2 stages in LDS).  Direct global->LDS 16-byte loads, an XOR swizzle of
+//    16-byte chunks by row so fragment reads hit distinct banks.
 //  * One v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 x E4M3, unit E8M0 scales)
 //    per 16x16 output tile per K step covers exactly one 128-K scale block,
 //    giving a fresh FP32 partial that is promoted into the FP32 accumulator
@@ -36,9 +38,13 @@
 namespace fgg {
 namespace fp8_detail {
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int SA_BLK_, int SA_ROW_>
 struct Fp8Cfg {
   static constexpr int BM = BM_, BN = BN_;
+  static constexpr int STAGES = STAGES_;  // LDS stages of the A/B ring (2 or 3)
+  // a_scale is staged in chunks of SA_BLK K blocks, SA_ROW floats per row in
+  // LDS (SA_ROW >= SA_BLK, a power of two; the extra values are unused).
+  static constexpr int SA_BLK = SA_BLK_, SA_ROW = SA_ROW_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = 64 * WAVES;
@@ -56,9 +62,12 @@ struct Fp8Cfg {
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one b_scale block");
   static_assert(BM % (16 * WAVES_M) == 0 && BN % (16 * WAVES_N) == 0, "tile shape");
   static_assert(BM % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "load split");
-  // a_scale chunk: BM rows x 8 floats, 64 floats per load instruction
-  static constexpr int SA_LOADS = BM * 8 / 64 / WAVES;
-  static_assert((BM * 8) % (64 * WAVES) == 0, "a_scale chunk split");
+  // a_scale chunk: BM rows x SA_ROW floats, 64 floats per load instruction
+  static constexpr int SA_LOADS = BM * SA_ROW / 64 / WAVES;
+  static_assert((BM * SA_ROW) % (64 * WAVES) == 0, "a_scale chunk split");
+  static_assert(SA_BLK <= SA_ROW && (SA_ROW & (SA_ROW - 1)) == 0, "a_scale chunk layout");
+  static_assert(STAGES == 2 || (STAGES == 3 && SA_BLK == 3), "the 3-stage loop pairs chunks with stages");
+  static constexpr int VM_TILE = A_LOADS + B_LOADS;  // loads per step into the A/B ring
   static_assert(WAVES % 2 == 0, "the staging swizzle assumes an even wave count");
   static_assert(WM == 64 && BM <= 512, "one row per lane in the pass masks");
 };
@@ -83,15 +92,51 @@ __device__ __forceinline__ i32x8 read_frag(const uint8_t* tile, int row0, int la
   return (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Wait for this wave's outstanding vector-memory operations (including the
-// loads into LDS), so that a following barrier publishes their data.
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory operations (including
+// the loads into LDS) are outstanding; they complete in issue order, so a
+// following barrier publishes the data of every earlier load.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
-// Raw buffer resource over [base, base + bytes): loads at offsets past the
-// end return zeros, the out-of-range fill the tail tiles rely on.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
+// Workgroup barrier after this wave's LDS reads have completed.  Unlike
+// __syncthreads() it does not also wait for every global load in flight
+// (the look-ahead stages must stay in flight across it).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// A buffer offset past every buffer's end (buffers are below 2^31 bytes):
+// a load there returns zeros without touching memory.
+constexpr uint32_t kSkip = 0x80000000u;
+
+// Raw buffer resource over [base, base + bytes), as its four descriptor
+// words (base address, stride 0, size, raw-access flags): loads at offsets
+// past the end return zeros, the out-of-range fill the tail tiles rely on.
+__device__ __forceinline__ i32x4 rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return (i32x4){(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr)(const_cast<void*>(p));
+}
+
+// Direct global->LDS loads of 16 (or 4) bytes per lane at buffer offset
+// voff + soff; lane l's bytes land at LDS address lds + 16 l (or 4 l).
+// Inline assembly, so that the compiler does not track these LDS writes and
+// add waits of its own for them: the pipeline orders them with its explicit
+// vmcnt waits and barriers.
+__device__ __forceinline__ void dma16(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds),
+               "v"(voff), "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(lds), "v"(voff),
+               "s"(rs), "s"(soff)
+               : "memory", "m0");
 }
 
 // Per-pass state: buffer resources, offsets, next scales, accumulators.
@@ -102,8 +147,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 //    plus the uniform s * W * 8 * K, plus the step's kb * 128.
 template <class T>
 struct Pass {
-  __amdgpu_buffer_rsrc_t ra, rb;  // A window rows, B[e] column-tile rows
-  __amdgpu_buffer_rsrc_t rsa;     // a_scale rows of the window
+  i32x4 ra, rb;  // A window rows, B[e] column-tile rows
+  i32x4 rsa;     // a_scale rows of the window
   uint32_t lane_off;              // (8 w + l / 8) K + 16 chunk
   uint32_t K;
   int nkb;
@@ -114,40 +159,46 @@ struct Pass {
   f32x4 acc[T::TM][T::TN];
 
   __device__ __forceinline__ void stage_in(uint8_t* st, int kb, int wave) const {
+    // Groups of rows of other experts are not needed.  With 3 stages their
+    // loads go past the buffer end (zeros, no memory traffic), so that every
+    // step issues the same number of loads, which the waits count; with 2
+    // stages (the wait is for all loads) they are skipped.
 #pragma unroll
-    for (int s = 0; s < T::A_LOADS; ++s)
-      if ((a_groups >> (s * T::WAVES + wave)) & 1)  // rows of other experts are not needed
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(st + (s * T::WAVES + wave) * 1024),
-                                                 16, lane_off, s * T::WAVES * 8 * K + kb * 128,
-                                                 0, 0);
+    for (int s = 0; s < T::A_LOADS; ++s) {
+      const bool need = (a_groups >> (s * T::WAVES + wave)) & 1;
+      if (T::STAGES == 2 && !need) continue;
+      dma16(ra, lds_addr(st + (s * T::WAVES + wave) * 1024), need ? lane_off : kSkip,
+            s * T::WAVES * 8 * K + kb * 128);
+    }
 #pragma unroll
     for (int s = 0; s < T::B_LOADS; ++s)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (lds_ptr)(st + T::A_BYTES + (s * T::WAVES + wave) * 1024), 16, lane_off,
-          s * T::WAVES * 8 * K + kb * 128, 0, 0);
+      dma16(rb, lds_addr(st + T::A_BYTES + (s * T::WAVES + wave) * 1024), lane_off,
+            s * T::WAVES * 8 * K + kb * 128);
   }
 
-  // a_scale values of K blocks [8c, 8c + 8) of every window row, as
-  // [row][8] floats: one 4-byte direct-to-LDS load per lane, 8 lanes per row
-  // (one 32-byte piece per row instead of one cache line per row per step).
+  // a_scale values of K blocks [c SA_BLK, c SA_BLK + SA_ROW) of every window
+  // row, as [row][SA_ROW] floats: one 4-byte direct-to-LDS load per lane,
+  // SA_ROW lanes per row (one short piece per row instead of one cache line
+  // per row per step).  Values past the chunk or past the row are unused.
   __device__ __forceinline__ void stage_scales(float* buf, int c, int wave, int lane) const {
 #pragma unroll
     for (int s = 0; s < T::SA_LOADS; ++s) {
-      const int g = (s * T::WAVES + wave) * 64 + lane;  // row g / 8, block 8c + g % 8
-      const uint32_t off = (uint32_t)(g >> 3) * (uint32_t)nkb * 4u + (uint32_t)(g & 7) * 4u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr)(buf + (s * T::WAVES + wave) * 64), 4,
-                                               off, c * 32, 0, 0);
+      const int g = (s * T::WAVES + wave) * 64 + lane;  // row g / SA_ROW, block g % SA_ROW
+      const uint32_t off = ((uint32_t)g / T::SA_ROW) * (uint32_t)nkb * 4u +
+                           ((uint32_t)g % T::SA_ROW) * 4u;
+      dma4(rsa, lds_addr(buf + (s * T::WAVES + wave) * 64), off, c * T::SA_BLK * 4);
     }
   }
 
   __device__ __forceinline__ void load_b_scale(int kb) { sb_next = bs_row[kb]; }
 };
 
-// One K step: start staging step kb+1 into `wr` (if any), then compute step
-// kb from `rd`.  `rd` and `wr` are distinct __shared__ arrays, which lets the
-// compiler see that the LDS reads of `rd` do not depend on the loads still
-// filling `wr`.  The partial of column subtile j is promoted into the FP32
-// accumulator while the MFMAs of subtile j+1 run.
+// One K step: start staging step kb + STAGES - 1 into `wr` (if any), then
+// compute step kb from `rd`, then wait for step kb + 1's tiles and barrier.
+// `rd` and `wr` are distinct __shared__ arrays (likewise the a_scale chunk
+// buffers), which lets the compiler see that the LDS reads of `rd` do not
+// depend on the loads still filling `wr`.  The partial of column subtile j is
+// promoted into the FP32 accumulator while the MFMAs of subtile j+1 run.
 template <class T>
 __device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* wr,
                                       const float* sa_rd, float* sa_wr, int kb, int lane, int wave,
@@ -157,10 +208,17 @@ __device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* w
   float s[T::TM];
 #pragma unroll
   for (int i = 0; i < T::TM; ++i)
-    s[i] = sa_rd[(wm * T::WM + i * 16 + (lane & 15)) * 8 + (kb & 7)] * ps.sb_next;
-  if (kb + 1 < ps.nkb) {
-    ps.stage_in(wr, kb + 1, wave);
-    if ((kb & 7) == 0 && kb + 8 < ps.nkb) ps.stage_scales(sa_wr, (kb >> 3) + 1, wave, lane);
+    s[i] = sa_rd[(wm * T::WM + i * 16 + (lane & 15)) * T::SA_ROW + (unsigned)kb % T::SA_BLK] *
+           ps.sb_next;
+  const int kl = kb + T::STAGES - 1;  // the step whose tiles this step loads
+  const bool load = kl < ps.nkb;
+  // the next a_scale chunk, at the first step of a chunk (implies `load`)
+  const bool sload = (unsigned)kb % T::SA_BLK == 0 && kb + T::SA_BLK < ps.nkb;
+  if (kb + 1 < ps.nkb) {  // implied by `load`
+    if (load) {
+      ps.stage_in(wr, kl, wave);
+      if (sload) ps.stage_scales(sa_wr, (unsigned)kb / T::SA_BLK + 1, wave, lane);
+    }
     ps.load_b_scale(kb + 1);
   }
   if (ps.active) {
@@ -172,7 +230,8 @@ __device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* w
   i32x8 bnext = bf;
   // MFMA t = (column subtile j, row subtile i) in j-major order; its partial
   // is promoted LAG MFMAs later, from a small ring, so the FMAs overlap the
-  // following MFMAs and few partials are live at once.
+  // following MFMAs and few partials are live at once; the next column
+  // subtile's B fragment is read TM MFMAs before its first use.
   constexpr int NT = T::TM * T::TN;
   constexpr int LAG = 3;
   f32x4 ring[LAG + 1];
@@ -192,10 +251,23 @@ __device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* w
       const int j = u / T::TM, i = u % T::TM;
       ps.acc[i][j] += ring[u % (LAG + 1)] * s[i];
     }
+    // Keep this order: left to itself the scheduler moves the FMAs next to
+    // the MFMA whose result they read and the fragment reads next to their
+    // use, which stalls on both latencies.
+    __builtin_amdgcn_sched_barrier(0);
   }
   }
-  wait_vmem();
-  __syncthreads();
+  if constexpr (T::STAGES == 2) {
+    wait_vmem<0>();  // step kb + 1's tiles were issued in this step
+    __syncthreads();
+  } else {
+    // Step kb + 1's tiles were issued one step ago: only this step's loads
+    // may stay in flight.
+    if (!load) wait_vmem<0>();
+    else if (sload) wait_vmem<T::VM_TILE + T::SA_LOADS>();
+    else wait_vmem<T::VM_TILE>();
+    lds_barrier();
+  }
 }
 
 template <class T>
@@ -206,8 +278,9 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
     int num_windows, int num_ntiles, int total_tiles, int group_w) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[T::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[T::STAGE];
-  __shared__ __attribute__((aligned(256))) float sa0[T::BM * 8];
-  __shared__ __attribute__((aligned(256))) float sa1[T::BM * 8];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[T::STAGES > 2 ? T::STAGE : 16];
+  __shared__ __attribute__((aligned(256))) float sa0[T::BM * T::SA_ROW];
+  __shared__ __attribute__((aligned(256))) float sa1[T::BM * T::SA_ROW];
   __shared__ int ids[T::BM];
 
   const int tid = threadIdx.x;
@@ -300,16 +373,36 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
       ps.stage_in(lds0, 0, wave);
       ps.stage_scales(sa0, 0, wave, lane);
       ps.load_b_scale(0);
-      wait_vmem();
-      __syncthreads();
-      // K steps two at a time (LDS stage parity), scale chunks of 8 steps
-      // alternate between sa0 and sa1.
-      for (int kb = 0; kb < nkb; kb += 2) {
-        const bool odd_chunk = (kb >> 3) & 1;
-        float* sa_rd = odd_chunk ? sa1 : sa0;
-        float* sa_wr = odd_chunk ? sa0 : sa1;
-        kstep<T>(ps, lds0, lds1, sa_rd, sa_wr, kb, lane, wave, wm, wn);
-        if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa_rd, sa_wr, kb + 1, lane, wave, wm, wn);
+      if constexpr (T::STAGES == 2) {
+        wait_vmem<0>();
+        __syncthreads();
+        // K steps two at a time (LDS stage parity), scale chunks of SA_BLK
+        // steps alternate between sa0 and sa1.
+        for (int kb = 0; kb < nkb; kb += 2) {
+          const bool odd_chunk = ((unsigned)kb / T::SA_BLK) & 1;
+          float* sa_rd = odd_chunk ? sa1 : sa0;
+          float* sa_wr = odd_chunk ? sa0 : sa1;
+          kstep<T>(ps, lds0, lds1, sa_rd, sa_wr, kb, lane, wave, wm, wn);
+          if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa_rd, sa_wr, kb + 1, lane, wave, wm, wn);
+        }
+      } else {
+        if (nkb > 1) {
+          ps.stage_in(lds1, 1, wave);
+          wait_vmem<T::VM_TILE>();  // step 0 and the first scale chunk
+        } else {
+          wait_vmem<0>();
+        }
+        lds_barrier();
+        // Six steps per iteration: stage = kb % 3 and scale chunk kb / 3
+        // (alternating sa0 / sa1) are then known at compile time.
+        for (int kb = 0; kb < nkb; kb += 6) {
+          kstep<T>(ps, lds0, lds2, sa0, sa1, kb, lane, wave, wm, wn);
+          if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa0, sa1, kb + 1, lane, wave, wm, wn);
+          if (kb + 2 < nkb) kstep<T>(ps, lds2, lds1, sa0, sa1, kb + 2, lane, wave, wm, wn);
+          if (kb + 3 < nkb) kstep<T>(ps, lds0, lds2, sa1, sa0, kb + 3, lane, wave, wm, wn);
+          if (kb + 4 < nkb) kstep<T>(ps, lds1, lds0, sa1, sa0, kb + 4, lane, wave, wm, wn);
+          if (kb + 5 < nkb) kstep<T>(ps, lds2, lds1, sa1, sa0, kb + 5, lane, wave, wm, wn);
+        }
       }
 
       // Epilogue: this expert's rows only.  Lane holds C[m][n .. n+3].
@@ -334,17 +427,18 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
 // Compiled tile shapes.  `tput` is the relative per-CU efficiency the ranker
 // uses, measured once on MI355X from whole-kernel runs of the grouped MoE
 // workloads (256x256 fastest per CU; the 4-wave shapes run one wave per SIMD
-// and hide less latency).  wg_per_cu follows from LDS and VGPR use.
-using Cfg0 = Fp8Cfg<256, 256, 4, 2>;  // 8 waves, 64x128 per wave, 128 KB LDS
-using Cfg1 = Fp8Cfg<256, 128, 4, 1>;  // 4 waves, 64x128 per wave,  96 KB LDS
-using Cfg2 = Fp8Cfg<128, 256, 2, 2>;  // 4 waves, 64x128 per wave,  96 KB LDS
-using Cfg3 = Fp8Cfg<128, 128, 2, 2>;  // 4 waves, 64x64 per wave,   64 KB LDS
+// and hide less latency).  wg_per_cu follows from LDS use (the 3-stage
+// shapes take 100-153 KB, so one workgroup per CU).
+using Cfg0 = Fp8Cfg<256, 256, 4, 2, 2, 8, 8>;  // 8 waves, 64x128 per wave, 2 x 64 KB stages
+using Cfg1 = Fp8Cfg<256, 128, 4, 1, 3, 3, 4>;  // 4 waves, 64x128 per wave, 3 x 48 KB stages
+using Cfg2 = Fp8Cfg<128, 256, 2, 2, 3, 3, 4>;  // 4 waves, 64x128 per wave, 3 x 48 KB stages
+using Cfg3 = Fp8Cfg<128, 128, 2, 2, 3, 3, 4>;  // 4 waves, 64x64 per wave,  3 x 32 KB stages
 
 const TileCfg kFp8Tiles[] = {
     {0, 256, 256, 8, 1, 1.00f},
-    {1, 256, 128, 4, 1, 0.67f},
+    {1, 256, 128, 4, 1, 0.72f},
     {2, 128, 256, 4, 1, 0.80f},
-    {3, 128, 128, 4, 2, 0.80f},
+    {3, 128, 128, 4, 1, 0.68f},
 };
 
 template <class T>
