@@ -79,6 +79,81 @@ __device__ __forceinline__ void map_tile(int id, int total, int num_windows, int
   ntile = in / gw;
 }
 
+// Heavy-first tile order.  A row window whose first and last rows hold two
+// different valid experts needs (at least) two passes of the K loop, so its
+// tiles cost up to twice as much.  With a static stride assignment of tiles
+// to workgroups, a workgroup can draw two such tiles while others draw none,
+// and the launch lasts as long as that workgroup.  Each workgroup therefore
+// marks these windows (two reads of m_indices per window, into an LDS
+// bitmask) and orders their tiles first: with at most gridDim.x of them,
+// no workgroup gets two.  Each class keeps the XCD-aware order of map_tile.
+// Windows beyond kPlanWindows (large M: many tiles per workgroup, where the
+// order matters little) are not planned.  Only the order depends on this
+// estimate; which experts a tile processes is decided from all its rows.
+constexpr int kPlanWindows = 4096;
+constexpr int kPlanWords = kPlanWindows / 32;
+
+// All threads of the workgroup call this; `bits` (kPlanWords words) and
+// `count` are in LDS.  Ends with a barrier.
+template <int BM, int THREADS>
+__device__ __forceinline__ void build_plan(uint32_t* bits, int* count, const int32_t* m_indices,
+                                           int M, int G, int num_windows) {
+  const int tid = threadIdx.x;
+  for (int w = tid; w < kPlanWords; w += THREADS) bits[w] = 0u;
+  if (tid == 0) *count = 0;
+  __syncthreads();
+  if (m_indices != nullptr && num_windows <= kPlanWindows) {
+    for (int w = tid; w < num_windows; w += THREADS) {
+      const int r0 = w * BM;
+      const int r1 = min(r0 + BM, M) - 1;
+      const int a = m_indices[r0], b = m_indices[r1];
+      if (a != b && a >= 0 && a < G && b >= 0 && b < G) {
+        atomicOr(&bits[w >> 5], 1u << (w & 31));
+        atomicAdd(count, 1);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Index of the k-th window (from 0) whose bit equals `set`; k must be below
+// the number of such windows.
+__device__ __forceinline__ int nth_window(const uint32_t* bits, int num_windows, int k, bool set) {
+  const int words = (num_windows + 31) >> 5;
+  for (int wd = 0; wd < words; ++wd) {
+    uint32_t v = set ? bits[wd] : ~bits[wd];
+    const int left = num_windows - wd * 32;
+    if (left < 32) v &= (1u << left) - 1u;
+    const int c = __popc(v);
+    if (k < c) {
+      for (int i = 0; i < k; ++i) v &= v - 1u;
+      return wd * 32 + __ffs(v) - 1;
+    }
+    k -= c;
+  }
+  return num_windows - 1;  // not reached for k below the count
+}
+
+// Tile `id` of the heavy-first order -> (row window, column tile).  A
+// bijection on [0, num_windows * num_ntiles).
+__device__ __forceinline__ void plan_tile(const uint32_t* bits, int heavy, int id, int num_windows,
+                                          int num_ntiles, int group_w, int& window, int& ntile) {
+  const int total = num_windows * num_ntiles;
+  if (heavy <= 0) {
+    map_tile(id, total, num_windows, num_ntiles, group_w, window, ntile);
+    return;
+  }
+  const int th = heavy * num_ntiles;
+  int cw;
+  if (id < th) {
+    map_tile(id, th, heavy, num_ntiles, group_w, cw, ntile);
+    window = nth_window(bits, num_windows, cw, true);
+  } else {
+    map_tile(id - th, total - th, num_windows - heavy, num_ntiles, group_w, cw, ntile);
+    window = nth_window(bits, num_windows, cw, false);
+  }
+}
+
 // Round four FP32 values to BF16 (round to nearest even) and pack them.
 __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
   bf16x2 lo = __builtin_convertvector((f32x2){a, b}, bf16x2);

@@ -224,6 +224,8 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[T::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[T::STAGE];
   __shared__ int ids[T::BM];
+  __shared__ uint32_t plan_bits[kPlanWords];
+  __shared__ int plan_heavy;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -248,9 +250,12 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
     ps.bs_off[u] = (uint32_t)(g >> 1) * Ks + (uint32_t)(g & 1) * 2u;
   }
 
+  build_plan<T::BM, T::THREADS>(plan_bits, &plan_heavy, m_indices, M, G, num_windows);
+  const int heavy = plan_heavy;
+
   for (int tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
     int window, ntile;
-    map_tile(tile, total_tiles, num_windows, num_ntiles, group_w, window, ntile);
+    plan_tile(plan_bits, heavy, tile, num_windows, num_ntiles, group_w, window, ntile);
     const int row0 = window * T::BM;
     const int col0 = ntile * T::BN;
 
@@ -346,7 +351,7 @@ const TileCfg kFp4Tiles[] = {
     {0, 256, 256, 8, 1, 1.00f},
     {1, 256, 128, 4, 1, 0.80f},
     {2, 128, 256, 4, 1, 0.80f},
-    {3, 128, 128, 4, 2, 0.76f},
+    {3, 128, 128, 4, 2, 0.74f},
 };
 
 template <class T>

@@ -282,6 +282,8 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
   __shared__ __attribute__((aligned(256))) float sa0[T::BM * T::SA_ROW];
   __shared__ __attribute__((aligned(256))) float sa1[T::BM * T::SA_ROW];
   __shared__ int ids[T::BM];
+  __shared__ uint32_t plan_bits[kPlanWords];
+  __shared__ int plan_heavy;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -302,9 +304,12 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
     ps.lane_off = (uint32_t)(wave * 8 + r8) * (uint32_t)K + (uint32_t)(chunk << 4);
   }
 
+  build_plan<T::BM, T::THREADS>(plan_bits, &plan_heavy, m_indices, M, G, num_windows);
+  const int heavy = plan_heavy;
+
   for (int tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
     int window, ntile;
-    map_tile(tile, total_tiles, num_windows, num_ntiles, group_w, window, ntile);
+    plan_tile(plan_bits, heavy, tile, num_windows, num_ntiles, group_w, window, ntile);
     const int row0 = window * T::BM;
     const int col0 = ntile * T::BN;
 
@@ -436,9 +441,9 @@ using Cfg3 = Fp8Cfg<128, 128, 2, 2, 3, 3, 4>;  // 4 waves, 64x64 per wave,  3 x 
 
 const TileCfg kFp8Tiles[] = {
     {0, 256, 256, 8, 1, 1.00f},
-    {1, 256, 128, 4, 1, 0.72f},
+    {1, 256, 128, 4, 1, 0.78f},
     {2, 128, 256, 4, 1, 0.80f},
-    {3, 128, 128, 4, 1, 0.68f},
+    {3, 128, 128, 4, 1, 0.70f},
 };
 
 template <class T>
