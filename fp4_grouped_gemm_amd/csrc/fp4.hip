@@ -31,6 +31,7 @@ namespace fgg {
 namespace fp4_detail {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
@@ -100,14 +101,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 // a load there returns zeros.
 constexpr uint32_t kSkip = 0x80000000u;
 
-// Packed E2M1 bytes and E4M3 scale pair of one staging unit, in registers.
-struct Unit {
-  i32x4 q;
-  uint16_t sc;  // kept 16-bit: a widening at the loop back edge would wait for the load
-};
-
 // Per-pass state.  Staging units: unit u of this thread covers tile row
-// u / 2, elements [32 (u % 2), 32 (u % 2) + 32) of the K step.
+// g / 2 (g = tid + u * THREADS), elements [32 h, 32 h + 32) of the K step,
+// h = g % 2 = tid % 2.  Packed codes are loaded two steps ahead (two register
+// sets, step s in set s % 2).  The four E4M3 scale codes of a row and step
+// are contiguous, so the codes of four consecutive steps (16 bytes) are
+// loaded with one 16-byte load per lane once per four steps, one group
+// ahead (two groups, steps [4c, 4c + 4) in group c % 2), instead of four
+// 2-byte loads that each touch one cache line per row; both lanes of a row
+// load the same 16 bytes and each uses its half.
 template <class T>
 struct Pass {
   __amdgpu_buffer_rsrc_t ra, rsa, rb, rsb;  // window rows of A / a_scale, tile rows of B / b_scale
@@ -116,44 +118,61 @@ struct Pass {
   // end of the buffer, so their loads return zeros without touching memory
   // (a branch-free skip; the zeros are never stored).
   uint32_t pa_off[T::A_UNITS], pas_off[T::A_UNITS];
-  Unit ua[2][T::A_UNITS], ub[2][T::B_UNITS];  // two tiles in flight
+  i32x4 qa[2][T::A_UNITS], qb[2][T::B_UNITS];  // packed codes, two steps in flight
+  i32x4 sa4[2][T::A_UNITS], sb4[2][T::B_UNITS];  // scale codes of 4 steps, two groups
   f32x4 acc[T::TM][T::TN];
 
-  // Issue the loads of K step ks into register set `set`.
+  // Issue the loads of the packed codes of K step ks into register set `set`.
   __device__ __forceinline__ void load(int set, int ks) {
 #pragma unroll
-    for (int u = 0; u < T::A_UNITS; ++u) {
-      ua[set][u].q = __builtin_bit_cast(
+    for (int u = 0; u < T::A_UNITS; ++u)
+      qa[set][u] = __builtin_bit_cast(
           i32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, pa_off[u], ks * (T::BK / 2), 0));
-      ua[set][u].sc = __builtin_amdgcn_raw_buffer_load_b16(rsa, pas_off[u], ks * (T::BK / 16), 0);
-    }
 #pragma unroll
-    for (int u = 0; u < T::B_UNITS; ++u) {
-      ub[set][u].q = __builtin_bit_cast(
+    for (int u = 0; u < T::B_UNITS; ++u)
+      qb[set][u] = __builtin_bit_cast(
           i32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[u], ks * (T::BK / 2), 0));
-      ub[set][u].sc = __builtin_amdgcn_raw_buffer_load_b16(rsb, bs_off[u], ks * (T::BK / 16), 0);
-    }
   }
 
-  // Chunk c of this thread's staging work for register set `set`: unit
-  // c / 4 (A units first, then B units), 16-byte word c % 4 of it,
+  // Issue the loads of the scale codes of steps [4c, 4c + 4) into group
+  // `grp`.  A row's codes start 8-byte aligned (K / 16 bytes per row);
+  // codes past the last step are never used.
+  __device__ __forceinline__ void load_scales(int grp, int c) {
+#pragma unroll
+    for (int u = 0; u < T::A_UNITS; ++u)
+      sa4[grp][u] = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rsa, pas_off[u], c * 16, 0));
+#pragma unroll
+    for (int u = 0; u < T::B_UNITS; ++u)
+      sb4[grp][u] = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, bs_off[u], c * 16, 0));
+  }
+
+  // Chunk c of this thread's staging work for a step whose packed codes are
+  // in register set `set` and scale codes at position `pos` of group `grp`:
+  // unit c / 4 (A units first, then B units), 16-byte word c % 4 of it,
   // dequantised and written to LDS stage `st`.  Word 0 also decodes the
   // unit's two block scales (words 0-1 use the first, words 2-3 the second).
   f16x2 sdec[T::A_UNITS + T::B_UNITS];
-  __device__ __forceinline__ void stage_chunk(int set, int c, uint8_t* st, int tid) {
+  __device__ __forceinline__ void stage_chunk(int set, int grp, int pos, int c, uint8_t* st,
+                                              int tid) {
     const int u = c >> 2, w = c & 3;
     const bool is_a = u < T::A_UNITS;
-    const Unit& un = is_a ? ua[set][u] : ub[set][u - T::A_UNITS];
-    if (w == 0) sdec[u] = e4m3x2_to_f16x2(un.sc);
+    const int v = is_a ? u : u - T::A_UNITS;
+    const i32x4 q = is_a ? qa[set][v] : qb[set][v];
+    if (w == 0) {
+      const uint32_t codes = (uint32_t)(is_a ? sa4[grp][v][pos] : sb4[grp][v][pos]);
+      sdec[u] = e4m3x2_to_f16x2(codes >> (16 * (tid & 1)));
+    }
     const _Float16 s = w < 2 ? sdec[u][0] : sdec[u][1];
-    const int g = tid + (is_a ? u : u - T::A_UNITS) * T::THREADS;
+    const int g = tid + v * T::THREADS;
     uint8_t* dst = st + (is_a ? 0 : T::A_BYTES) + swz(g >> 1, (g & 1) * 4 + w);
-    *reinterpret_cast<i32x4*>(dst) = dequant_word((uint32_t)un.q[w], (f16x2){s, s});
+    *reinterpret_cast<i32x4*>(dst) = dequant_word((uint32_t)q[w], (f16x2){s, s});
   }
   static constexpr int CHUNKS = 4 * (T::A_UNITS + T::B_UNITS);
-  __device__ __forceinline__ void stage_all(int set, uint8_t* st, int tid) {
+  __device__ __forceinline__ void stage_all(int set, int grp, int pos, uint8_t* st, int tid) {
 #pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) stage_chunk(set, c, st, tid);
+    for (int c = 0; c < CHUNKS; ++c) stage_chunk(set, grp, pos, c, st, tid);
   }
 };
 
@@ -174,7 +193,7 @@ __device__ __forceinline__ void lds_barrier() {
 // each slot keeps that spread.
 template <class T, bool STAGE>
 __device__ __forceinline__ void mma_step(Pass<T>& ps, const uint8_t* rd, uint8_t* wr, int set,
-                                         int tid, int lane, int wm, int wn) {
+                                         int grp, int pos, int tid, int lane, int wm, int wn) {
   constexpr int S = 2 * T::TN, C = Pass<T>::CHUNKS;
   const uint8_t* rb = rd + T::A_BYTES;
 #pragma unroll
@@ -194,25 +213,39 @@ __device__ __forceinline__ void mma_step(Pass<T>& ps, const uint8_t* rd, uint8_t
         const int k = h * T::TN + j;
 #pragma unroll
         for (int c = 0; c < C; ++c)
-          if (c * S / C == k) ps.stage_chunk(set, c, wr, tid);
+          if (c * S / C == k) ps.stage_chunk(set, grp, pos, c, wr, tid);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-// One K step from `rd` that also stages the next one: issue the loads of
-// step `ks_load` into register set `set` (free: its previous contents were
-// staged in the previous step), then the MFMAs with the next step (register
-// set set ^ 1, loaded one step ago) staged into `wr` between them.  Every
-// step issues the same loads (the last ones reload the last step), so the
-// waits before the dequantisation count only the loads of set ^ 1.
-template <class T>
-__device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* wr, int set,
-                                      int ks_load, int tid, int lane, int wm, int wn) {
-  ps.load(set, ks_load);
-  mma_step<T, true>(ps, rd, wr, set ^ 1, tid, lane, wm, wn);
+// One K step s = ks + Q from `rd` that also stages step s + 1 into `wr`:
+// issue the packed-code loads of step min(s + 2, last) into register set
+// s % 2 (free: it held step s, dequantised in the previous step) and, at the
+// first step of a group of four, the scale codes of the next group; then the
+// MFMAs with step s + 1 (set (s + 1) % 2, scales at position (s + 1) % 4 of
+// group ((s + 1) / 4) % 2) dequantised between them.  ks is a multiple of 8,
+// so all these indices are compile-time constants.  Every step issues the
+// same loads (the last ones reload the last step), so the waits before the
+// dequantisation count only older loads.  Returns false past the last step.
+template <class T, int Q>
+__device__ __forceinline__ bool kstep(Pass<T>& ps, uint8_t* lds0, uint8_t* lds1, int ks, int nks,
+                                      int tid, int lane, int wm, int wn) {
+  if (Q > 0 && ks + Q >= nks) return false;
+  ps.load(Q & 1, min(ks + Q + 2, nks - 1));
+  if constexpr (Q % 4 == 0) ps.load_scales((Q / 4 + 1) & 1, (ks + Q) / 4 + 1);
+  mma_step<T, true>(ps, (Q & 1) ? lds1 : lds0, (Q & 1) ? lds0 : lds1, (Q + 1) & 1,
+                    ((Q + 1) / 4) & 1, (Q + 1) % 4, tid, lane, wm, wn);
   lds_barrier();
+  return true;
+}
+
+template <class T, int... Q>
+__device__ __forceinline__ void ksteps8(Pass<T>& ps, uint8_t* lds0, uint8_t* lds1, int ks, int nks,
+                                        int tid, int lane, int wm, int wn,
+                                        std::integer_sequence<int, Q...>) {
+  (kstep<T, Q>(ps, lds0, lds1, ks, nks, tid, lane, wm, wn) && ...);
 }
 
 template <class T>
@@ -241,13 +274,13 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
   for (int u = 0; u < T::A_UNITS; ++u) {
     const int g = tid + u * T::THREADS;
     ps.a_off[u] = (uint32_t)(g >> 1) * Kp + (uint32_t)(g & 1) * 16u;
-    ps.as_off[u] = (uint32_t)(g >> 1) * Ks + (uint32_t)(g & 1) * 2u;
+    ps.as_off[u] = (uint32_t)(g >> 1) * Ks;
   }
 #pragma unroll
   for (int u = 0; u < T::B_UNITS; ++u) {
     const int g = tid + u * T::THREADS;
     ps.b_off[u] = (uint32_t)(g >> 1) * Kp + (uint32_t)(g & 1) * 16u;
-    ps.bs_off[u] = (uint32_t)(g >> 1) * Ks + (uint32_t)(g & 1) * 2u;
+    ps.bs_off[u] = (uint32_t)(g >> 1) * Ks;
   }
 
   build_plan<T::BM, T::THREADS>(plan_bits, &plan_heavy, m_indices, M, G, num_windows);
@@ -313,15 +346,15 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
 
       ps.load(0, 0);
       ps.load(1, min(1, nks - 1));
-      ps.stage_all(0, lds0, tid);
+      ps.load_scales(0, 0);
+      ps.stage_all(0, 0, 0, lds0, tid);
       lds_barrier();
-      // Steps in pairs so that register set and LDS stage are known at
-      // compile time.  The last step also stages (a reload of itself, into
-      // the stage nobody reads any more), which keeps one loop body.
-      for (int ks = 0; ks < nks; ks += 2) {
-        kstep<T>(ps, lds0, lds1, 0, min(ks + 2, nks - 1), tid, lane, wm, wn);
-        if (ks + 1 < nks) kstep<T>(ps, lds1, lds0, 1, min(ks + 3, nks - 1), tid, lane, wm, wn);
-      }
+      // Eight steps per iteration (register set, LDS stage and scale group
+      // positions known at compile time).  The last step also stages (a
+      // reload, into the stage nobody reads any more).
+      for (int ks = 0; ks < nks; ks += 8)
+        ksteps8<T>(ps, lds0, lds1, ks, nks, tid, lane, wm, wn,
+                   std::make_integer_sequence<int, 8>{});
 
 #pragma unroll
       for (int i = 0; i < T::TM; ++i) {
