@@ -67,6 +67,12 @@ CASES = {
     "grouped_unsorted": lambda: _grouped(np.random.default_rng(5).integers(-1, 4, 301), G=4),
     "grouped_out_of_range": lambda: _grouped([0, 9, -3, 1] * 50, G=2),
     "grouped_run_of_one": lambda: _grouped([0] * 60 + [1] + [2] * 90, G=3),
+    # K loops of 6, 10, 14 and 12 steps of 64: every exit position of the
+    # eight-step unrolled loop and of the four-step scale groups
+    "dense_k384": lambda: _dense(130, 256, 384, seed=6),
+    "dense_k640": lambda: _dense(77, 128, 640, seed=7),
+    "grouped_k896": lambda: _grouped(runs_to_indices([40, 90, 0, 33]), N=256, K=896, seed=8),
+    "grouped_k768": lambda: _grouped(runs_to_indices([129, 127, 3]), N=384, K=768, seed=9),
 }
 
 

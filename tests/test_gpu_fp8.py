@@ -162,6 +162,28 @@ def test_full_size_sampled(name):
         assert_parity(p, C, rows=rows[::3], what=f"{name}/tile{tile}")
 
 
+@pytest.mark.slow
+def test_more_windows_than_the_tile_plan_tracks():
+    """Past 4096 row windows the heavy-first tile order is not built and
+    tiles go in the plain XCD order; 128-row windows of 600000 rows exceed
+    that.  Sampled rows against the oracle, every padding row zero."""
+    rng = np.random.default_rng(11)
+    counts = rng.integers(0, 40000, 24)
+    counts[5] = 0
+    ids = runs_to_indices(counts.tolist(), pad_to=1)
+    ids = np.concatenate([ids, np.full(600000 - ids.size, -1, np.int32)]) if ids.size < 600000 \
+        else ids[:600000]
+    p = _prob(ids, N=128, K=128, G=24, seed=12)
+    d = to_dev(p)
+    rows = sample_rows(p, 256)
+    for tile in (3, 0):
+        log(f"600000 rows, tile {tile}")
+        C = run(p, d, tile_id=tile)
+        assert_parity(p, C, rows=rows, what=f"many windows/tile{tile}")
+        out = c_to_f64(C)
+        assert np.all(out[row_ids(p) < 0] == 0.0)
+
+
 def test_every_e4m3_code_exact():
     """All 254 non-NaN E4M3 codes of A against an identity B: each output is
     one product decode(A[i, n]) * 1.0, exact in BF16, so it must match the
