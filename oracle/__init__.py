@@ -22,6 +22,11 @@ same value up to FP32 rounding order and the final BF16 rounding):
                 (onnxruntime#29824 page, "Code analysis 1": W4A4 grouped GEMM
                 for MoE prefill; flashinfer#3948 page: dense mm_fp4.)
 
+  quantisers   oracle.quant: BF16 activations -> FP8 E4M3FN codes with one
+                FP32 scale per row and 128-wide K block, and -> NVFP4 (E2M1
+                codes, E4M3 scale per 16 elements, FP32 global scale); see
+                that module for the definition and its precision.
+
 Pins: the test suite checks these functions against exhaustive format
 tables, exact integer / rational brute force, hand-computed worked examples
 and invariants.  Parity status of each function is stated in its docstring.
