@@ -17,7 +17,8 @@ import ctypes
 import os
 
 __all__ = [
-    "grouped_fp8_gemm", "fp4_gemm", "grouped_fp4_gemm", "rank_tiles", "num_tiles",
+    "grouped_fp8_gemm", "fp4_gemm", "grouped_fp4_gemm", "quantize_fp8_1x128",
+    "quantize_nvfp4", "rank_tiles", "num_tiles",
     "device_info", "library_path", "load_library", "FP8", "FP4",
 ]
 
@@ -59,6 +60,8 @@ def load_library():
         ("fp4_gemm_ex", [P, P, P, P, F, P, I, I, I, OPT, P]),
         ("grouped_fp4_gemm", [P, P, P, P, P, F, P, I, I, I, I, P]),
         ("grouped_fp4_gemm_ex", [P, P, P, P, P, F, P, I, I, I, I, OPT, P]),
+        ("quantize_fp8_1x128", [P, P, P, I, I, P]),
+        ("quantize_nvfp4", [P, P, P, P, I, I, P]),
     ):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
@@ -252,3 +255,43 @@ def device_info():
     _check(lib.fgg_device_info(ctypes.byref(cu), ctypes.byref(lds), ctypes.byref(clk), arch, 64))
     return dict(num_cus=cu.value, lds_per_block=lds.value, clock_khz=clk.value,
                 arch=arch.value.decode())
+
+
+def _bf16_matrix(X):
+    torch = _torch()
+    if not isinstance(X, torch.Tensor) or X.dtype != torch.bfloat16 or X.dim() != 2:
+        raise ValueError("X must be a 2-D torch.bfloat16 tensor [M, K]")
+    return _dev(X, "X", X.device)
+
+
+def quantize_fp8_1x128(X, stream=None):
+    """BF16 activations [M, K] -> (E4M3FN codes uint8 [M, K], FP32 scales
+    [M, K/128]): the A operand of grouped_fp8_gemm (C ABI quantize_fp8_1x128)."""
+    torch = _torch()
+    lib = load_library()
+    X = _bf16_matrix(X)
+    M, K = X.shape
+    Q = torch.empty((M, K), dtype=torch.uint8, device=X.device)
+    S = torch.empty((M, max(K // 128, 1)), dtype=torch.float32, device=X.device)
+    with torch.cuda.device(X.device):
+        _check(lib.quantize_fp8_1x128(X.data_ptr(), Q.data_ptr(), S.data_ptr(), M, K,
+                                      _stream_ptr(stream, X.device)))
+    return Q, S
+
+
+def quantize_nvfp4(X, stream=None):
+    """BF16 activations [M, K] -> (packed E2M1 uint8 [M, K/2], E4M3FN scale
+    codes uint8 [M, K/16], FP32 global scale as a 1-element device tensor):
+    the A operand of fp4_gemm / grouped_fp4_gemm, whose alpha is this global
+    scale times B's (C ABI quantize_nvfp4; no host synchronisation)."""
+    torch = _torch()
+    lib = load_library()
+    X = _bf16_matrix(X)
+    M, K = X.shape
+    Q = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+    S = torch.empty((M, max(K // 16, 1)), dtype=torch.uint8, device=X.device)
+    g = torch.empty((1,), dtype=torch.float32, device=X.device)
+    with torch.cuda.device(X.device):
+        _check(lib.quantize_nvfp4(X.data_ptr(), Q.data_ptr(), S.data_ptr(), g.data_ptr(), M, K,
+                                  _stream_ptr(stream, X.device)))
+    return Q, S, g

@@ -271,4 +271,44 @@ fgg_status grouped_fp4_gemm(const void* A, const void* B, const void* a_scale,
                              stream);
 }
 
+// Activation quantisers (the step before the GEMM).
+static fgg_status check_quant(const char* fn, const void* X, const void* Q, const void* S, int M,
+                              int K, uintptr_t scale_align) {
+  if (!X || !Q || !S) return fail(FGG_EINVAL, fn, "null pointer among X, Q, scale");
+  if (M < 1 || M > (1 << 24)) return fail(FGG_EINVAL, fn, "requires 1 <= M <= 2^24, got M=%d", M);
+  if (K < 128 || K > (1 << 20)) return fail(FGG_EINVAL, fn, "requires 128 <= K <= 2^20, got K=%d", K);
+  if (K % 128) return fail(FGG_EINVAL, fn, "requires K %% 128 == 0, got K=%d", K);
+  if (!aligned(X, 16) || !aligned(Q, 16))
+    return fail(FGG_EALIGN, fn, "X and Q must be 16-byte aligned");
+  if (!aligned(S, scale_align))
+    return fail(FGG_EALIGN, fn, "scale must be %d-byte aligned", (int)scale_align);
+  return FGG_OK;
+}
+
+fgg_status quantize_fp8_1x128(const void* X, void* Q, float* scale, int M, int K, void* stream) {
+  const char* fn = "quantize_fp8_1x128";
+  fgg_status st = check_quant(fn, X, Q, scale, M, K, 4);
+  if (st != FGG_OK) return st;
+  const DeviceFacts* d = current_device(fn, &st);
+  if (!d) return st;
+  return launched(fn, fgg::launch_quant_fp8(static_cast<const uint16_t*>(X), static_cast<uint8_t*>(Q),
+                                            scale, M, K, d->num_cus,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+fgg_status quantize_nvfp4(const void* X, void* Q, void* scale, float* global_scale, int M, int K,
+                          void* stream) {
+  const char* fn = "quantize_nvfp4";
+  fgg_status st = check_quant(fn, X, Q, scale, M, K, 1);
+  if (st != FGG_OK) return st;
+  if (!global_scale) return fail(FGG_EINVAL, fn, "global_scale is null");
+  if (!aligned(global_scale, 4)) return fail(FGG_EALIGN, fn, "global_scale must be 4-byte aligned");
+  const DeviceFacts* d = current_device(fn, &st);
+  if (!d) return st;
+  return launched(fn, fgg::launch_quant_nvfp4(static_cast<const uint16_t*>(X),
+                                              static_cast<uint8_t*>(Q), static_cast<uint8_t*>(scale),
+                                              global_scale, M, K, d->num_cus,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -46,6 +46,10 @@ const TileCfg& fp4_tile(int id);
 // Launchers: enqueue on `stream`, return hipSuccess or the launch error.
 hipError_t launch_fp8(const Fp8Args& a, int tile_id, int max_wg, int num_cus, hipStream_t s);
 hipError_t launch_fp4(const Fp4Args& a, int tile_id, int max_wg, int num_cus, hipStream_t s);
+hipError_t launch_quant_fp8(const uint16_t* X, uint8_t* Q, float* scale, int M, int K,
+                            int num_cus, hipStream_t s);
+hipError_t launch_quant_nvfp4(const uint16_t* X, uint8_t* Q, uint8_t* S, float* g, int M, int K,
+                              int num_cus, hipStream_t s);
 
 // --------------------------------------------------------- device helpers
 #ifdef __HIPCC__

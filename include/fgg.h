@@ -115,6 +115,34 @@ fgg_status grouped_fp4_gemm(const void* A, const void* B, const void* a_scale,
                             void* C, int M, int N, int K, int G, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Activation quantisers: the step before the GEMM, producing its A operand.
+ *
+ * quantize_fp8_1x128 -- BF16 X [M, K] -> E4M3FN codes Q [M, K] and one FP32
+ * scale per row and 128-wide K block, scale [M, K/128] (the a_scale layout of
+ * grouped_fp8_gemm).  scale = amax(block) / 448 (1.0 for an all-zero block);
+ * code = E4M3FN round-to-nearest-even of clamp(x / scale, -448, 448), every
+ * step an FP32 operation rounded to nearest even (sglang#27745 page, "Code
+ * analysis 1: FP8 quantisation": clamp to the gfx950 E4M3FN maximum 448, then
+ * encode; flashinfer#7877 page: FP32 per-128 block scales).
+ *
+ * quantize_nvfp4 -- BF16 X [M, K] -> packed E2M1 Q [M, K/2] (element 2j in the
+ * low nibble of byte j), E4M3FN block-scale codes scale [M, K/16] and the FP32
+ * global scale written to the device scalar *global_scale (the A-side factor
+ * of the GEMM's alpha; the W4A4 activations of the onnxruntime#29824 page).
+ * g = amax(X) / 2688 (1.0 for all-zero X), s = E4M3FN(min(amax(block) /
+ * (6 g), 448)), code = E2M1(clamp(x / (value(s) g), -6, 6)), 0 where
+ * value(s) g is 0.  Four kernel launches on `stream` (clear, amax, encode,
+ * finalise); no host synchronisation, no allocation.
+ *
+ * Requirements: X, Q 16-byte aligned (scale: 4-byte for FP8, any for NVFP4;
+ * global_scale 4-byte); 1 <= M <= 2^24; 128 <= K <= 2^20, K % 128 == 0; X
+ * finite.  Errors as for the GEMMs.
+ * ------------------------------------------------------------------------ */
+fgg_status quantize_fp8_1x128(const void* X, void* Q, float* scale, int M, int K, void* stream);
+fgg_status quantize_nvfp4(const void* X, void* Q, void* scale, float* global_scale, int M, int K,
+                          void* stream);
+
+/* ------------------------------------------------------------------------
  * Tile configurations and the ranker.
  *
  * The kernels are compiled for a small set of tile shapes.  For each call

@@ -73,6 +73,20 @@ def test_fp4_validation():
     assert st == 2
 
 
+def test_quantizer_validation():
+    lib = fgg.load_library()
+    st = lib.quantize_fp8_1x128(P, P, P, 8, 200, None)
+    assert st == 1 and lib.fgg_last_error().decode().startswith("quantize_fp8_1x128:")
+    assert lib.quantize_fp8_1x128(0, P, P, 8, 256, None) == 1
+    assert lib.quantize_fp8_1x128(P, P, P + 2, 8, 256, None) == 2
+    assert lib.quantize_fp8_1x128(P + 4, P, P, 8, 256, None) == 2
+    assert lib.quantize_fp8_1x128(P, P, P, 0, 256, None) == 1
+    st = lib.quantize_nvfp4(P, P, P, 0, 8, 256, None)
+    assert st == 1 and "global_scale" in lib.fgg_last_error().decode()
+    assert lib.quantize_nvfp4(P, P, P, P + 2, 8, 256, None) == 2
+    assert lib.quantize_nvfp4(P, P + 8, P, P, 8, 256, None) == 2
+
+
 def test_python_binding_raises_value_error():
     torch = pytest.importorskip("torch")
     A = torch.zeros((4, 128), dtype=torch.uint8)

@@ -1,0 +1,150 @@
+"""GPU parity of the activation quantisers against the oracle (through the
+C ABI).  Codes, scale codes and scales are integer / exact decisions taken in
+FP32 on both sides, so every comparison is bitwise."""
+import numpy as np
+import pytest
+
+import oracle.quant as oq
+from tests.gpu_util import log
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16(rng, M, K, scale=1.0, dist="normal"):
+    """Seeded BF16-representable float32 values (and the bf16 tensor)."""
+    import torch
+    if dist == "student_t3":
+        x = rng.standard_t(3, (M, K))
+    else:
+        x = rng.standard_normal((M, K))
+    x = (x * scale).astype(np.float32)
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    return t.float().numpy(), t
+
+
+def _gpu_fp8(t):
+    import fp4_grouped_gemm_amd as fgg
+    Q, S = fgg.quantize_fp8_1x128(t.cuda())
+    return Q.cpu().numpy(), S.cpu().numpy()
+
+
+def _gpu_nvfp4(t):
+    import fp4_grouped_gemm_amd as fgg
+    Q, S, g = fgg.quantize_nvfp4(t.cuda())
+    return Q.cpu().numpy(), S.cpu().numpy(), np.float32(g.cpu().numpy()[0])
+
+
+CASES = {
+    "small": (3, 128, 1.0, "normal"),
+    "ragged_rows": (37, 384, 3.0, "normal"),
+    "wide": (5, 4224, 0.01, "normal"),
+    "heavy_tail": (64, 1024, 1.0, "student_t3"),
+    "tiny_values": (16, 256, 1e-30, "normal"),
+    "big_values": (16, 256, 1e30, "normal"),
+    "one_row": (1, 7168, 1.0, "normal"),
+    "odd_segments": (3, 640, 2.0, "normal"),  # 15 blocks of 128: a partial wave segment
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_fp8_1x128_bitwise(case):
+    M, K, sc, dist = CASES[case]
+    x, t = _bf16(np.random.default_rng(100 + sorted(CASES).index(case)), M, K, sc, dist)
+    x[:, :128][0] = 0.0  # an all-zero block in the first row
+    import torch
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    log(f"quantize_fp8_1x128 {case} M={M} K={K}")
+    Q, S = _gpu_fp8(t)
+    q_ref, s_ref = oq.quantize_fp8_1x128(x)
+    assert np.array_equal(S.view(np.uint32), s_ref.view(np.uint32)), case
+    assert np.array_equal(Q, q_ref), (case, int((Q != q_ref).sum()))
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_nvfp4_bitwise(case):
+    M, K, sc, dist = CASES[case]
+    x, t = _bf16(np.random.default_rng(200 + sorted(CASES).index(case)), M, K, sc, dist)
+    x[0, 16:48] = 0.0  # all-zero 16-blocks
+    import torch
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    log(f"quantize_nvfp4 {case} M={M} K={K}")
+    Q, S, g = _gpu_nvfp4(t)
+    q_ref, s_ref, g_ref = oq.quantize_nvfp4(x)
+    assert g == g_ref, (case, g, g_ref)
+    assert np.array_equal(S, s_ref), (case, int((S != s_ref).sum()))
+    assert np.array_equal(Q, q_ref), (case, int((Q != q_ref).sum()))
+
+
+def test_every_bf16_value_through_fp8():
+    """Every finite BF16 bit pattern as an element next to a block maximum
+    of 448 (scale 1.0): each code is the E4M3FN rounding of the value itself
+    (covers rounding, ties, subnormals, signed zero and clamping)."""
+    import torch
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    v = (bits << 16).view(np.float32)
+    v = v[np.isfinite(v) & (np.abs(v) <= 448)]
+    n = -(-v.size // 127) * 127
+    vals = np.zeros(n, np.float32)
+    vals[:v.size] = v
+    blocks = vals.reshape(-1, 127)
+    x = np.concatenate([np.full((blocks.shape[0], 1), 448.0, np.float32), blocks], axis=1)
+    x = x.reshape(-1, 128 * 8) if x.shape[0] % 8 == 0 else x.reshape(-1, 128)
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    assert np.array_equal(t.float().numpy(), x)
+    log(f"every bf16 value through fp8: {v.size} values")
+    Q, S = _gpu_fp8(t)
+    q_ref, s_ref = oq.quantize_fp8_1x128(x)
+    assert np.all(S == 1.0)
+    assert np.array_equal(Q, q_ref), int((Q != q_ref).sum())
+
+
+def test_every_fp4_rounding_case():
+    """Values on a 1/64 grid through [-6.5, 6.5], each 16-block led by 6.0,
+    with the tensor maximum 2688: g = 1, every such block gets s = 1.0 and
+    d = 1, so each code is the E2M1 rounding of the value itself (ties,
+    signed zero and clamping included)."""
+    import torch
+    grid = (np.arange(-6.5 * 64, 6.5 * 64 + 1) / 64).astype(np.float32)
+    n = -(-grid.size // 15) * 15
+    vals = np.zeros(n, np.float32)
+    vals[:grid.size] = grid
+    blocks = vals.reshape(-1, 15)
+    x = np.concatenate([np.full((blocks.shape[0], 1), 6.0, np.float32), blocks], axis=1)
+    rows = -(-x.shape[0] // 8)
+    pad = np.zeros((rows * 8 - x.shape[0], 16), np.float32)
+    x = np.concatenate([x, pad]).reshape(rows, 128)
+    x[0, 0] = 2688.0  # tensor amax: g = 1
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    x = t.float().numpy()
+    log("fp4 rounding grid")
+    Q, S, g = _gpu_nvfp4(t)
+    q_ref, s_ref, g_ref = oq.quantize_nvfp4(x)
+    assert g == g_ref == 1.0
+    assert np.array_equal(S, s_ref)
+    assert np.array_equal(Q, q_ref), int((Q != q_ref).sum())
+
+
+def test_quantised_activations_feed_the_gemm():
+    """quantize_fp8_1x128 output is a valid A operand: the grouped FP8 GEMM on
+    it matches the oracle GEMM on the oracle-quantised A."""
+    import torch
+
+    import fp4_grouped_gemm_amd as fgg
+    import oracle
+    from workloads import runs_to_indices
+    rng = np.random.default_rng(21)
+    M, N, K, G = 300, 256, 512, 3
+    x, t = _bf16(rng, M, K)
+    ids = runs_to_indices([100, 0, 200], pad_to=1)
+    from workloads import fp8_problem
+    p = fp8_problem(ids, N, K, G, rng)
+    Q, S = fgg.quantize_fp8_1x128(t.cuda())
+    C = fgg.grouped_fp8_gemm(Q, torch.from_numpy(p["B"]).cuda(), S,
+                             torch.from_numpy(p["b_scale"]).cuda(),
+                             torch.from_numpy(ids).cuda())
+    torch.cuda.synchronize()
+    q_ref, s_ref = oq.quantize_fp8_1x128(x)
+    ref = oracle.grouped_fp8_gemm(q_ref, p["B"], s_ref, p["b_scale"], ids)
+    out = C.float().cpu().numpy().astype(np.float64)
+    res = oracle.check_tolerance(out, ref, ids)
+    assert res["ok"], res
