@@ -44,7 +44,14 @@ WORKLOADS = {
     "c5_moe_nvfp4": dict(kind="fp4", desc="grouped NVFP4 W4A4 MoE prefill, G=8x8192 rows, "
                          "N=8192, K=8192"),
     "c1_tiny_fp8": dict(kind="fp8", desc="tiny grouped FP8, G=2, M=256, N=256, K=512"),
+    # The activation quantisers (the step before the GEMM), on the A-operand
+    # shapes of c2 and c5: HBM-bound, reported in GB/s.
+    "q_fp8_c2": dict(kind="quant_fp8", M=8192, K=7168,
+                     desc="BF16 -> FP8 1x128 activations of c2, M=8192, K=7168"),
+    "q_nvfp4_c5": dict(kind="quant_nvfp4", M=65536, K=8192,
+                       desc="BF16 -> NVFP4 activations of c5, M=65536, K=8192"),
 }
+QUANT_METRIC = "GB/s (algorithmic bytes / time) and % of HBM peak, activation quantiser"
 
 
 def kernel_source_hash() -> str:
@@ -197,6 +204,81 @@ def rocprof_summary(root: str, workload: str, kernel: str, command: str) -> str:
     return text
 
 
+def quant_bytes(kind: str, M: int, K: int) -> int:
+    """Bytes a quantiser launch must move at least once: read X (BF16), write
+    the codes and the scales.  The NVFP4 path reads X twice (the global
+    amax comes before any code); the second read is not counted."""
+    if kind == "quant_fp8":
+        return M * K * 2 + M * K + M * (K // 128) * 4
+    return M * K * 2 + M * K // 2 + M * (K // 16) + 4
+
+
+def bench_quant(args, torch):
+    import fp4_grouped_gemm_amd as fgg
+    w = WORKLOADS[args.workload]
+    kind, M, K = w["kind"], w["M"], w["K"]
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    rng = np.random.default_rng(0)
+    X = torch.from_numpy(rng.standard_normal((M, K), dtype=np.float32)).to(torch.bfloat16)
+    Xd = X.cuda()
+    run = (lambda: fgg.quantize_fp8_1x128(Xd)) if kind == "quant_fp8" else \
+        (lambda: fgg.quantize_nvfp4(Xd))
+    for _ in range(args.warmup):
+        out = run()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        out = run()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    nbytes = quant_bytes(kind, M, K)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": QUANT_METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded NumPy N(0,1), BF16, resident in HBM)",
+        "config": {"workload": args.workload, "desc": w["desc"], "M": M, "K": K,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK, 4), "traffic": None,
+                     "algorithmic_bytes": nbytes},
+        "kernel_source_sha": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        import oracle.quant as oq
+        from threadpoolctl import threadpool_info
+        print("[bench] cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
+        Xf = X.float().numpy()
+        Q = [t.cpu().numpy() for t in out]
+        done, ok = 0, True
+        t0 = time.perf_counter()
+        for r0 in range(0, M, 64):
+            rows = Xf[r0:r0 + 64]
+            if kind == "quant_fp8":
+                q, sc = oq.quantize_fp8_1x128(rows)
+                ok &= bool(np.array_equal(q, Q[0][r0:r0 + 64]) and
+                           np.array_equal(sc, Q[1][r0:r0 + 64]))
+            else:
+                q, sc, _ = oq.quantize_nvfp4(rows, np.float32(Q[2][0]))
+                ok &= bool(np.array_equal(q, Q[0][r0:r0 + 64]) and np.array_equal(sc, Q[1][r0:r0 + 64]))
+            done += rows.shape[0]
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        res["cpu_baseline"] = {
+            "value": round(quant_bytes(kind, done, K) / dt / 1e9, 4), "unit": "GB/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {M} rows of the same workload (NumPy float32 decisions, "
+                      f"table-search encoders), {dt:.1f} s; the global scale from the GPU run"}
+        res["parity_sample"] = {"rows": done, "ok": ok, "bitwise": True}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +323,13 @@ def main():
         ms = (time.perf_counter() - t0) * 1e3 / args.steps
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 4),
                           "gbps": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+        return
+
+    if WORKLOADS[args.workload]["kind"].startswith("quant"):
+        if not os.path.exists(os.path.join(ROOT, "fp4_grouped_gemm_amd", "libfgg.so")):
+            from fp4_grouped_gemm_amd.build import build
+            build()
+        bench_quant(args, torch)
         return
 
     import fp4_grouped_gemm_amd as fgg
