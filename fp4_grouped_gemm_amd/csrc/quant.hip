@@ -20,7 +20,7 @@
 // Both kernels treat X as a flat array of M * K values: K is a multiple of
 // 128, so no block crosses a row, and the scale arrays are the blocks in
 // flat order.  They are HBM-bound: 2 bytes read and 1 (FP8) or 0.5 (NVFP4)
-// written per value, 16-byte loads per lane.
+// written per value.
 #include "common.h"
 
 #include <climits>
@@ -28,15 +28,25 @@
 namespace fgg {
 namespace quant_detail {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // 8 BF16 values (16 bytes) -> FP32 (exact: BF16 is the top half of FP32).
-__device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
-  const uint4 raw = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+__device__ __forceinline__ void bf16x8(u32x4 w, float v[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[2 * i] = __uint_as_float(w[i] << 16);
     v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
+}
+
+// 32 consecutive BF16 values (64 bytes) at p -> FP32: four 16-byte loads,
+// all issued before any is used.
+__device__ __forceinline__ void load32(const uint16_t* p, float v[4][8]) {
+  u32x4 w[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const u32x4*>(p + 8 * u);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) bf16x8(w[u], v[u]);
 }
 
 // Maximum over the lanes of aligned groups of `width` lanes (width <= 64).
@@ -47,45 +57,53 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
-// ------------------------------------------------------------- FP8 1x128
-// One wave per 512 values (four 128-value blocks); lane l holds values
-// [8 l, 8 l + 8) of the segment, block l / 16.
+// Both encoders give each lane 32 consecutive values (four 16-byte loads in
+// flight per lane, whole 16-byte code stores) and a wave 2048; the 32-value
+// pieces are independent of the rows, as blocks never cross a row.  Lanes
+// past the end load the last piece instead and store nothing: a block is
+// valid or not as a whole, so their values reach no valid block.
 constexpr int kQThreads = 256;
 
+// ------------------------------------------------------------- FP8 1x128
+// A 128-value block is 4 lanes.
 __global__ __launch_bounds__(kQThreads) void quant_fp8_kernel(const uint16_t* __restrict__ X,
                                                               uint8_t* __restrict__ Q,
                                                               float* __restrict__ scale,
                                                               long long nblocks) {
   const int lane = threadIdx.x & 63;
   const long long waves = (long long)gridDim.x * (kQThreads / 64);
-  for (long long seg = (long long)blockIdx.x * (kQThreads / 64) + (threadIdx.x >> 6);
-       seg * 4 < nblocks; seg += waves) {
-    const long long blk = seg * 4 + (lane >> 4);
-    const bool valid = blk < nblocks;  // the last segment may hold fewer blocks
-    const long long base = seg * 512 + lane * 8;
-    float v[8];
-    if (valid) {
-      load8(X + base, v);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.f;
-    }
+  const long long pieces = nblocks * 4;
+  for (long long w = (long long)blockIdx.x * (kQThreads / 64) + (threadIdx.x >> 6);
+       w * 64 < pieces; w += waves) {
+    const long long q = min(w * 64 + lane, pieces - 1);
+    float v[4][8];
+    load32(X + q * 32, v);
     float a = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
-    const float amax = group_max<16>(a);
-    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
-    float y[8];
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(v[i] / s, -448.0f), 448.0f);
-    // bytes 0,1 then 2,3 of each word, in value order
-    uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-    lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo, true);
-    uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-    hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)hi, true);
-    if (valid) {
-      *reinterpret_cast<uint2*>(Q + base) = make_uint2(lo, hi);
-      if ((lane & 15) == 0) scale[blk] = s;
+      for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[u][i]));
+    const float amax = group_max<4>(a);
+    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+    u32x4 out[2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(v[u][i] / s, -448.0f), 448.0f);
+      // bytes 0,1 then 2,3 of each word, in value order
+      uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo, true);
+      uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+      hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)hi, true);
+      out[u >> 1][2 * (u & 1)] = lo;
+      out[u >> 1][2 * (u & 1) + 1] = hi;
+    }
+    if (w * 64 + lane < pieces) {
+      u32x4* o = reinterpret_cast<u32x4*>(Q + q * 32);
+      o[0] = out[0];
+      o[1] = out[1];
+      if ((lane & 3) == 0) scale[q >> 2] = s;
     }
   }
 }
@@ -93,18 +111,30 @@ __global__ __launch_bounds__(kQThreads) void quant_fp8_kernel(const uint16_t* __
 // ------------------------------------------------------------------ NVFP4
 // Global amax: max over |x| of the flat array, as the bit pattern of a
 // non-negative float (ordered like the value) in amax_bits[0], which the
-// first kernel clears.
+// first kernel clears.  X is read once here and once by the encoder, far
+// apart, so these loads are non-temporal.
 __global__ void clear_kernel(uint32_t* p) { p[0] = 0u; }
 
 __global__ __launch_bounds__(kQThreads) void amax_kernel(const uint16_t* __restrict__ X,
                                                          long long n8, uint32_t* amax_bits) {
+  constexpr int kLoads = 4;  // 16-byte loads in flight per lane
   float a = 0.f;
-  const long long stride = (long long)gridDim.x * kQThreads;
-  for (long long i = (long long)blockIdx.x * kQThreads + threadIdx.x; i < n8; i += stride) {
-    float v[8];
-    load8(X + i * 8, v);
+  const long long stride = (long long)gridDim.x * kQThreads * kLoads;
+  for (long long i0 = (long long)blockIdx.x * kQThreads * kLoads + threadIdx.x; i0 < n8;
+       i0 += stride) {
+    // past the end: the last chunk again (a repeat cannot change the maximum)
+    u32x4 w[kLoads];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(v[k]));
+    for (int u = 0; u < kLoads; ++u)
+      w[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(X + min(i0 + (long long)u * kQThreads, n8 - 1) * 8));
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      float v[8];
+      bf16x8(w[u], v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(v[k]));
+    }
   }
   a = group_max<64>(a);
   __shared__ float wmax[kQThreads / 64];
@@ -123,8 +153,24 @@ __device__ __forceinline__ float global_scale(uint32_t amax_bits) {
   return amax > 0.f ? amax / 2688.0f : 1.0f;
 }
 
-// One wave per 512 values (32 blocks of 16); lane l holds values
-// [8 l, 8 l + 8), block l / 2.
+// 8 values -> 8 E2M1 codes (element 2j in the low nibble of byte j), given
+// the block's decode scale d (all zero codes when d is 0).
+__device__ __forceinline__ uint32_t e2m1x8(const float v[8], float d) {
+  uint32_t packed = 0;
+  if (d > 0.f) {
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float y0 = fminf(fmaxf(v[i] / d, -6.0f), 6.0f);
+      const float y1 = fminf(fmaxf(v[i + 1] / d, -6.0f), 6.0f);
+      const uint32_t two =
+          (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0, y0, y1, 1.0f, 0) & 0xFFu;
+      packed |= two << (4 * i);
+    }
+  }
+  return packed;
+}
+
+// A lane holds two whole 16-value blocks: no cross-lane reduction.
 __global__ __launch_bounds__(kQThreads) void quant_nvfp4_kernel(const uint16_t* __restrict__ X,
                                                                 uint8_t* __restrict__ Q,
                                                                 uint8_t* __restrict__ S,
@@ -134,39 +180,33 @@ __global__ __launch_bounds__(kQThreads) void quant_nvfp4_kernel(const uint16_t* 
   const float g = global_scale(amax_bits[0]);
   const float g6 = 6.0f * g;
   const long long waves = (long long)gridDim.x * (kQThreads / 64);
-  for (long long seg = (long long)blockIdx.x * (kQThreads / 64) + (threadIdx.x >> 6);
-       seg * 32 < nblocks; seg += waves) {
-    const long long blk = seg * 32 + (lane >> 1);
-    const bool valid = blk < nblocks;
-    const long long base = seg * 512 + lane * 8;
-    float v[8];
-    if (valid) {
-      load8(X + base, v);
-    } else {
+  const long long pieces = nblocks / 2;  // nblocks is even (K % 128 == 0)
+  for (long long w = (long long)blockIdx.x * (kQThreads / 64) + (threadIdx.x >> 6);
+       w * 64 < pieces; w += waves) {
+    const long long q = min(w * 64 + lane, pieces - 1);
+    float v[4][8];
+    load32(X + q * 32, v);
+    u32x4 codes;
+    uint32_t sc = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    for (int b = 0; b < 2; ++b) {
+      float a = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[2 * b + h][i]));
+      const float s_in = fminf(a / g6, 448.0f);
+      const uint32_t s_code =
+          (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s_in, 0.f, 0, false) & 0xFFu;
+      const float d = __builtin_amdgcn_cvt_f32_fp8((int)s_code, 0) * g;
+      codes[2 * b] = e2m1x8(v[2 * b], d);
+      codes[2 * b + 1] = e2m1x8(v[2 * b + 1], d);
+      sc |= s_code << (8 * b);
     }
-    float a = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
-    const float bamax = group_max<2>(a);
-    const float s_in = fminf(bamax / g6, 448.0f);
-    const uint32_t s_code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s_in, 0.f, 0, false) & 0xFFu;
-    const float d = __builtin_amdgcn_cvt_f32_fp8((int)s_code, 0) * g;
-    uint32_t packed = 0;
-    if (d > 0.f) {
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const float y0 = fminf(fmaxf(v[i] / d, -6.0f), 6.0f);
-        const float y1 = fminf(fmaxf(v[i + 1] / d, -6.0f), 6.0f);
-        const uint32_t two =
-            (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0, y0, y1, 1.0f, 0) & 0xFFu;
-        packed |= two << (4 * i);
-      }
-    }
-    if (valid) {
-      *reinterpret_cast<uint32_t*>(Q + base / 2) = packed;
-      if ((lane & 1) == 0) S[blk] = (uint8_t)s_code;
+    if (w * 64 + lane < pieces) {
+      *reinterpret_cast<u32x4*>(Q + q * 16) = codes;
+      S[q * 2] = (uint8_t)sc;  // byte stores: the scale array may have any alignment
+      S[q * 2 + 1] = (uint8_t)(sc >> 8);
     }
   }
 }
@@ -175,9 +215,11 @@ __global__ void finalize_kernel(uint32_t* g) {
   g[0] = __float_as_uint(global_scale(g[0]));
 }
 
-int grid_for(long long waves, int num_cus) {
+// Workgroups for `waves` waves of work, at most per_cu per compute unit
+// (the rest loop); measured best: 8 per CU for the streaming loops here.
+int grid_for(long long waves, int num_cus, int per_cu) {
   const long long wgs = (waves + kQThreads / 64 - 1) / (kQThreads / 64);
-  const long long cap = (long long)num_cus * 16;
+  const long long cap = (long long)num_cus * per_cu;
   return (int)(wgs < cap ? (wgs > 0 ? wgs : 1) : cap);
 }
 
@@ -189,9 +231,8 @@ hipError_t launch_quant_fp8(const uint16_t* X, uint8_t* Q, float* scale, int M, 
                             int num_cus, hipStream_t s) {
   const long long nblocks = (long long)M * (K / 128);
   if (nblocks <= 0) return hipSuccess;
-  const long long segs = (nblocks + 3) / 4;
-  hipLaunchKernelGGL(quant_fp8_kernel, dim3(grid_for(segs, num_cus)), dim3(kQThreads), 0, s, X, Q,
-                     scale, nblocks);
+  hipLaunchKernelGGL(quant_fp8_kernel, dim3(grid_for((nblocks * 4 + 63) / 64, num_cus, 8)),
+                     dim3(kQThreads), 0, s, X, Q, scale, nblocks);
   return hipGetLastError();
 }
 
@@ -202,12 +243,11 @@ hipError_t launch_quant_nvfp4(const uint16_t* X, uint8_t* Q, uint8_t* S, float* 
   uint32_t* gb = reinterpret_cast<uint32_t*>(g);
   hipLaunchKernelGGL(clear_kernel, dim3(1), dim3(1), 0, s, gb);
   const long long n8 = n / 8;
-  hipLaunchKernelGGL(amax_kernel, dim3(grid_for(n8 / 64 + 1, num_cus)), dim3(kQThreads), 0, s, X,
-                     n8, gb);
+  hipLaunchKernelGGL(amax_kernel, dim3(grid_for((n8 + 255) / 256, num_cus, 8)), dim3(kQThreads), 0,
+                     s, X, n8, gb);
   const long long nblocks = n / 16;
-  const long long segs = (nblocks + 31) / 32;
-  hipLaunchKernelGGL(quant_nvfp4_kernel, dim3(grid_for(segs, num_cus)), dim3(kQThreads), 0, s, X,
-                     Q, S, (const uint32_t*)gb, nblocks);
+  hipLaunchKernelGGL(quant_nvfp4_kernel, dim3(grid_for((nblocks / 2 + 63) / 64, num_cus, 16)),
+                     dim3(kQThreads), 0, s, X, Q, S, (const uint32_t*)gb, nblocks);
   hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1), 0, s, gb);
   return hipGetLastError();
 }
