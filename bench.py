@@ -44,6 +44,10 @@ WORKLOADS = {
     "c5_moe_nvfp4": dict(kind="fp4", desc="grouped NVFP4 W4A4 MoE prefill, G=8x8192 rows, "
                          "N=8192, K=8192"),
     "c1_tiny_fp8": dict(kind="fp8", desc="tiny grouped FP8, G=2, M=256, N=256, K=512"),
+    # Latency shapes of the flashinfer#7877 page's timing table: launch-bound,
+    # the interesting figure is ms_per_step.
+    "p2_unaligned": dict(kind="fp8", desc="small grouped FP8, G=2, M=65, N=128, K=128"),
+    "p2_m777_g8": dict(kind="fp8", desc="small grouped FP8, G=8, M=777, N=256, K=512"),
     # The activation quantisers (the step before the GEMM), on the A-operand
     # shapes of c2 and c5: HBM-bound, reported in GB/s.
     "q_fp8_c2": dict(kind="quant_fp8", M=8192, K=7168,
@@ -287,6 +291,11 @@ def main():
     ap.add_argument("--workload", default="c2_moe_fp8", choices=sorted(WORKLOADS))
     ap.add_argument("--tile", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the K timed launches in one HIP graph and time its replay "
+                         "(launch-bound small shapes: GPU time without host launch overhead)")
+    ap.add_argument("--run-split", type=int, default=0,
+                    help="fgg_options.run_split (0 automatic, -1 never, 1 always)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--rocprof-summary", default=None, metavar="DIR",
@@ -347,16 +356,29 @@ def main():
     M, N, K, G = p["M"], p["N"], p["K"], p["G"]
     C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     kw = {} if args.tile is None else {"tile_id": args.tile}
+    if args.run_split and p.get("m_indices") is not None:
+        kw["run_split"] = args.run_split
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         run(p, d, out=C, **kw)
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        run(p, d, out=C, **kw)
-    end.record(stream)
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                run(p, d, out=C, **kw)
+        graph.replay()  # untimed first replay
+        torch.cuda.synchronize()
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+    else:
+        start.record(stream)
+        for _ in range(args.steps):
+            run(p, d, out=C, **kw)
+        end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     rr = real_rows(p)
@@ -376,7 +398,8 @@ def main():
         "config": {"workload": args.workload, "desc": WORKLOADS[args.workload]["desc"],
                    "M": M, "N": N, "K": K, "G": G, "real_rows": rr,
                    "tile": args.tile if args.tile is not None else tiles[0]["id"],
-                   "parallelism": "single GPU"},
+                   "run_split": args.run_split, "timing": "hip graph of K launches" if args.graph
+                   else "K stream launches", "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK[mma],
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK[mma], 4),
                      "traffic": traffic, "mfma_dtype": mma,

@@ -37,7 +37,8 @@ class _Tile(ctypes.Structure):
 
 
 class _Options(ctypes.Structure):
-    _fields_ = [("tile_id", ctypes.c_int), ("max_workgroups", ctypes.c_int)]
+    _fields_ = [("tile_id", ctypes.c_int), ("max_workgroups", ctypes.c_int),
+                ("run_split", ctypes.c_int)]
 
 
 def load_library():
@@ -83,10 +84,11 @@ def _check(status: int):
         raise ValueError(msg or f"fgg status {status}")
 
 
-def _opts(tile_id, max_workgroups):
-    if tile_id is None and not max_workgroups:
+def _opts(tile_id, max_workgroups, run_split=0):
+    if tile_id is None and not max_workgroups and not run_split:
         return None
-    return ctypes.byref(_Options(-1 if tile_id is None else int(tile_id), int(max_workgroups or 0)))
+    return ctypes.byref(_Options(-1 if tile_id is None else int(tile_id), int(max_workgroups or 0),
+                                 int(run_split or 0)))
 
 
 def _torch():
@@ -130,12 +132,15 @@ def _out(out, M, N, device):
 
 
 def grouped_fp8_gemm(A, B, a_scale, b_scale, m_indices, out=None, *, tile_id=None,
-                     max_workgroups=0, stream=None):
+                     max_workgroups=0, run_split=0, stream=None):
     """C[M, N] (bfloat16) of the grouped block-scaled FP8 GEMM.
 
     A [M, K] and B [G, N, K] hold E4M3FN codes; a_scale [M, K/128] and
     b_scale [G, N/128, K/128] are float32; m_indices [M] is int32 (expert id or
-    -1).  See include/fgg.h for the exact definition.
+    -1).  See include/fgg.h for the exact definition.  tile_id,
+    max_workgroups and run_split are the fields of fgg_options (run_split: 0
+    automatic, -1 never, 1 always run each expert pass of a row window as its
+    own workgroup).
     """
     torch = _torch()
     A, B = _bytes(A, "A"), _bytes(B, "B")
@@ -160,7 +165,7 @@ def grouped_fp8_gemm(A, B, a_scale, b_scale, m_indices, out=None, *, tile_id=Non
     with torch.cuda.device(dev):
         _check(lib.grouped_fp8_gemm_ex(A.data_ptr(), B.data_ptr(), a_scale.data_ptr(),
                                        b_scale.data_ptr(), m_indices.data_ptr(), C.data_ptr(),
-                                       M, N, K, G, _opts(tile_id, max_workgroups),
+                                       M, N, K, G, _opts(tile_id, max_workgroups, run_split),
                                        _stream_ptr(stream, dev)))
     return C
 
@@ -204,7 +209,7 @@ def fp4_gemm(A, B, a_scale, b_scale, alpha, out=None, *, tile_id=None, max_workg
 
 
 def grouped_fp4_gemm(A, B, a_scale, b_scale, m_indices, alpha, out=None, *, tile_id=None,
-                     max_workgroups=0, stream=None):
+                     max_workgroups=0, run_split=0, stream=None):
     """C[M, N] (bfloat16) of the grouped NVFP4 GEMM: B [G, N, K/2], b_scale
     [G, N, K/16]; m_indices int32 [M] routes rows (-1 = padding)."""
     torch = _torch()
@@ -228,7 +233,8 @@ def grouped_fp4_gemm(A, B, a_scale, b_scale, m_indices, alpha, out=None, *, tile
     with torch.cuda.device(dev):
         _check(lib.grouped_fp4_gemm_ex(A.data_ptr(), B.data_ptr(), sa.data_ptr(), sb.data_ptr(),
                                        m_indices.data_ptr(), float(alpha), C.data_ptr(), M, N, K,
-                                       G, _opts(tile_id, max_workgroups), _stream_ptr(stream, dev)))
+                                       G, _opts(tile_id, max_workgroups, run_split),
+                                       _stream_ptr(stream, dev)))
     return C
 
 

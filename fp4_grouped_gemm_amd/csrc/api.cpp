@@ -160,6 +160,10 @@ fgg_status pick_tile(const char* fn, int kind, int M, int N, int G, int num_cus,
   return FGG_OK;
 }
 
+fgg::LaunchOpts launch_opts(const fgg_options* opt, const DeviceFacts* d) {
+  return fgg::LaunchOpts{opt ? opt->max_workgroups : 0, d->num_cus, opt ? opt->run_split : 0};
+}
+
 fgg_status launched(const char* fn, hipError_t e) {
   if (e != hipSuccess) return fail(FGG_EHIP, fn, "kernel launch failed: %s", hipGetErrorString(e));
   g_err.clear();
@@ -217,8 +221,7 @@ fgg_status grouped_fp8_gemm_ex(const void* A, const void* B, const float* a_scal
   if ((st = pick_tile(fn, FGG_KIND_FP8, M, N, G, d->num_cus, opt, &tile)) != FGG_OK) return st;
   fgg::Fp8Args a{static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), a_scale, b_scale,
                  m_indices, static_cast<uint16_t*>(C), M, N, K, G};
-  return launched(fn, fgg::launch_fp8(a, tile, opt ? opt->max_workgroups : 0, d->num_cus,
-                                      static_cast<hipStream_t>(stream)));
+  return launched(fn, fgg::launch_fp8(a, tile, launch_opts(opt, d), static_cast<hipStream_t>(stream)));
 }
 
 fgg_status grouped_fp8_gemm(const void* A, const void* B, const float* a_scale,
@@ -241,8 +244,7 @@ static fgg_status fp4_common(const char* fn, const void* A, const void* B, const
   fgg::Fp4Args a{static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B),
                  static_cast<const uint8_t*>(a_scale), static_cast<const uint8_t*>(b_scale),
                  grouped ? m_indices : nullptr, alpha, static_cast<uint16_t*>(C), M, N, K, G};
-  return launched(fn, fgg::launch_fp4(a, tile, opt ? opt->max_workgroups : 0, d->num_cus,
-                                      static_cast<hipStream_t>(stream)));
+  return launched(fn, fgg::launch_fp4(a, tile, launch_opts(opt, d), static_cast<hipStream_t>(stream)));
 }
 
 fgg_status fp4_gemm_ex(const void* A, const void* B, const void* a_scale, const void* b_scale,

@@ -43,9 +43,34 @@ const TileCfg& fp8_tile(int id);
 int fp4_num_tiles();
 const TileCfg& fp4_tile(int id);
 
+// Launch choices made on the host.
+struct LaunchOpts {
+  int max_wg;     // > 0: cap on the persistent grid
+  int num_cus;    // compute units of the device
+  int run_split;  // 0 automatic, < 0 never, > 0 whenever possible (see split_items)
+};
+
+// Work items per tile.  A row window holding several experts' rows takes one
+// K-loop pass per expert.  Normally one workgroup runs them one after the
+// other; in split mode each pass is its own work item, so the passes of a
+// window run side by side (the window-segment program of the flashinfer#7877
+// page, "Code analysis 2": one CTA per expert run of a 128-row window, used
+// when all of them fit in a single wave of the GPU).  The host cannot read
+// m_indices, so it sizes for the most passes a window can need, min(G, BM);
+// items past a window's last expert end at once.  Automatic mode splits only
+// when every item of the launch runs at once on the device (tiles * split
+// workgroups fit the CUs); then the launch lasts about one pass.
+inline int split_items(int mode, bool grouped, int G, int BM, long long tiles, int slots) {
+  if (!grouped || G < 2 || mode < 0) return 1;
+  const long long s = G < BM ? G : BM;
+  if (tiles * s > 0x7FFFFFFFLL) return 1;
+  if (mode == 0 && tiles * s > slots) return 1;
+  return (int)s;
+}
+
 // Launchers: enqueue on `stream`, return hipSuccess or the launch error.
-hipError_t launch_fp8(const Fp8Args& a, int tile_id, int max_wg, int num_cus, hipStream_t s);
-hipError_t launch_fp4(const Fp4Args& a, int tile_id, int max_wg, int num_cus, hipStream_t s);
+hipError_t launch_fp8(const Fp8Args& a, int tile_id, const LaunchOpts& o, hipStream_t s);
+hipError_t launch_fp4(const Fp4Args& a, int tile_id, const LaunchOpts& o, hipStream_t s);
 hipError_t launch_quant_fp8(const uint16_t* X, uint8_t* Q, float* scale, int M, int K,
                             int num_cus, hipStream_t s);
 hipError_t launch_quant_nvfp4(const uint16_t* X, uint8_t* Q, uint8_t* S, float* g, int M, int K,

@@ -253,7 +253,7 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ a_scale, const uint8_t* __restrict__ b_scale,
     const int32_t* __restrict__ m_indices, float alpha, uint16_t* __restrict__ C, int M, int N,
-    int K, int G, int num_windows, int num_ntiles, int total_tiles, int group_w) {
+    int K, int G, int num_windows, int num_ntiles, int total_tiles, int group_w, int split) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[T::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[T::STAGE];
   __shared__ int ids[T::BM];
@@ -283,10 +283,16 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
     ps.bs_off[u] = (uint32_t)(g >> 1) * Ks;
   }
 
-  build_plan<T::BM, T::THREADS>(plan_bits, &plan_heavy, m_indices, M, G, num_windows);
+  // With split > 1 every pass of a tile is its own work item (the tile
+  // order then needs no plan: no item costs more than one pass).
+  build_plan<T::BM, T::THREADS>(plan_bits, &plan_heavy, split > 1 ? nullptr : m_indices, M, G,
+                                num_windows);
   const int heavy = plan_heavy;
+  const int items = total_tiles * split;
 
-  for (int tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int tile = split > 1 ? item / split : item;
+    const int run_sel = split > 1 ? item % split : 0;  // which pass this item runs
     int window, ntile;
     plan_tile(plan_bits, heavy, tile, num_windows, num_ntiles, group_w, window, ntile);
     const int row0 = window * T::BM;
@@ -308,7 +314,7 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
       const int r = c / (T::BN / 8);
       const int cc = c % (T::BN / 8);
       const int col = col0 + cc * 8;
-      if (ids[r] == -1 && col < N)
+      if (ids[r] == -1 && col < N && run_sel == 0)
         *reinterpret_cast<uint4*>(C + (size_t)(row0 + r) * N + col) = make_uint4(0, 0, 0, 0);
     }
 
@@ -321,7 +327,7 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
     const int wcol0 = col0 + wn * T::WN;
 
     int cur = -1;
-    while (true) {
+    for (int pass = 0;; ++pass) {
       int e = INT_MAX;
       for (int r = lane; r < T::BM; r += 64) {
         const int v = ids[r];
@@ -330,6 +336,10 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
       e = __builtin_amdgcn_readfirstlane(wave_min(e));  // same in every wave
       if (e == INT_MAX) break;
       cur = e;
+      if (split > 1 && pass != run_sel) {
+        if (pass > run_sel) break;
+        continue;
+      }
 
 #pragma unroll
       for (int u = 0; u < T::A_UNITS; ++u) {
@@ -388,19 +398,19 @@ const TileCfg kFp4Tiles[] = {
 };
 
 template <class T>
-hipError_t launch_cfg(const Fp4Args& a, int max_wg, int num_cus, hipStream_t s) {
+hipError_t launch_cfg(const Fp4Args& a, const LaunchOpts& o, hipStream_t s) {
   const int num_windows = (a.M + T::BM - 1) / T::BM;
   const int num_ntiles = (a.N + T::BN - 1) / T::BN;
   const long long total = (long long)num_windows * num_ntiles;
   if (total <= 0) return hipSuccess;
   if (total > INT_MAX) return hipErrorInvalidValue;
-  int grid = (int)total;
-  if (max_wg > 0 && max_wg < grid) grid = max_wg;
-  (void)num_cus;
+  const int split = split_items(o.run_split, a.m_indices != nullptr, a.G, T::BM, total, o.num_cus);
+  int grid = (int)(total * split);
+  if (o.max_wg > 0 && o.max_wg < grid) grid = o.max_wg;
   const int group_w = 8;  // row windows per XCD tile group
   hipLaunchKernelGGL(fp4_gemm_kernel<T>, dim3(grid), dim3(T::THREADS), 0, s, a.A, a.B, a.a_scale,
                      a.b_scale, a.m_indices, a.alpha, a.C, a.M, a.N, a.K, a.G, num_windows,
-                     num_ntiles, (int)total, group_w);
+                     num_ntiles, (int)total, group_w, split);
   return hipGetLastError();
 }
 
@@ -411,12 +421,12 @@ using namespace fp4_detail;
 int fp4_num_tiles() { return (int)(sizeof(kFp4Tiles) / sizeof(kFp4Tiles[0])); }
 const TileCfg& fp4_tile(int id) { return kFp4Tiles[id]; }
 
-hipError_t launch_fp4(const Fp4Args& a, int tile_id, int max_wg, int num_cus, hipStream_t s) {
+hipError_t launch_fp4(const Fp4Args& a, int tile_id, const LaunchOpts& o, hipStream_t s) {
   switch (tile_id) {
-    case 0: return launch_cfg<Cfg0>(a, max_wg, num_cus, s);
-    case 1: return launch_cfg<Cfg1>(a, max_wg, num_cus, s);
-    case 2: return launch_cfg<Cfg2>(a, max_wg, num_cus, s);
-    case 3: return launch_cfg<Cfg3>(a, max_wg, num_cus, s);
+    case 0: return launch_cfg<Cfg0>(a, o, s);
+    case 1: return launch_cfg<Cfg1>(a, o, s);
+    case 2: return launch_cfg<Cfg2>(a, o, s);
+    case 3: return launch_cfg<Cfg3>(a, o, s);
     default: return hipErrorInvalidValue;
   }
 }

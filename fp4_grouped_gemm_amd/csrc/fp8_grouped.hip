@@ -275,7 +275,7 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
     const float* __restrict__ a_scale, const float* __restrict__ b_scale,
     const int32_t* __restrict__ m_indices, uint16_t* __restrict__ C, int M, int N, int K, int G,
-    int num_windows, int num_ntiles, int total_tiles, int group_w) {
+    int num_windows, int num_ntiles, int total_tiles, int group_w, int split) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[T::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[T::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[T::STAGES > 2 ? T::STAGE : 16];
@@ -304,10 +304,16 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
     ps.lane_off = (uint32_t)(wave * 8 + r8) * (uint32_t)K + (uint32_t)(chunk << 4);
   }
 
-  build_plan<T::BM, T::THREADS>(plan_bits, &plan_heavy, m_indices, M, G, num_windows);
+  // With split > 1 every pass of a tile is its own work item (the tile
+  // order then needs no plan: no item costs more than one pass).
+  build_plan<T::BM, T::THREADS>(plan_bits, &plan_heavy, split > 1 ? nullptr : m_indices, M, G,
+                                num_windows);
   const int heavy = plan_heavy;
+  const int items = total_tiles * split;
 
-  for (int tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int tile = split > 1 ? item / split : item;
+    const int run_sel = split > 1 ? item % split : 0;  // which pass this item runs
     int window, ntile;
     plan_tile(plan_bits, heavy, tile, num_windows, num_ntiles, group_w, window, ntile);
     const int row0 = window * T::BM;
@@ -330,7 +336,7 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
       const int r = c / (T::BN / 8);
       const int cc = c % (T::BN / 8);
       const int col = col0 + cc * 8;
-      if (ids[r] == -1 && col < N)
+      if (ids[r] == -1 && col < N && run_sel == 0)
         *reinterpret_cast<uint4*>(C + (size_t)(row0 + r) * N + col) = make_uint4(0, 0, 0, 0);
     }
 
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
 
     // One pass per distinct expert present in the window, in increasing id.
     int cur = -1;
-    while (true) {
+    for (int pass = 0;; ++pass) {
       int e = INT_MAX;
       for (int r = lane; r < T::BM; r += 64) {
         const int v = ids[r];
@@ -354,6 +360,10 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
       e = __builtin_amdgcn_readfirstlane(wave_min(e));
       if (e == INT_MAX) break;
       cur = e;
+      if (split > 1 && pass != run_sel) {
+        if (pass > run_sel) break;
+        continue;
+      }
 
       // Which rows this pass needs: A loads of 8-row groups without a row of
       // expert e are skipped, and a wave whose 64 rows hold none computes
@@ -447,21 +457,21 @@ const TileCfg kFp8Tiles[] = {
 };
 
 template <class T>
-hipError_t launch_cfg(const Fp8Args& a, int max_wg, int num_cus, hipStream_t s) {
+hipError_t launch_cfg(const Fp8Args& a, const LaunchOpts& o, hipStream_t s) {
   const int num_windows = (a.M + T::BM - 1) / T::BM;
   const int num_ntiles = (a.N + T::BN - 1) / T::BN;
   const long long total = (long long)num_windows * num_ntiles;
   if (total <= 0) return hipSuccess;
   if (total > INT_MAX) return hipErrorInvalidValue;
-  int grid = (int)total;
-  if (max_wg > 0 && max_wg < grid) grid = max_wg;
+  const int split = split_items(o.run_split, a.m_indices != nullptr, a.G, T::BM, total, o.num_cus);
+  int grid = (int)(total * split);
+  if (o.max_wg > 0 && o.max_wg < grid) grid = o.max_wg;
   // Row windows per tile group (all column tiles of a group run in one XCD,
   // window fastest): 8 windows measured best on MI355X for the MoE shapes.
-  (void)num_cus;
   const int group_w = 8;
   hipLaunchKernelGGL(fp8_grouped_kernel<T>, dim3(grid), dim3(T::THREADS), 0, s, a.A, a.B,
                      a.a_scale, a.b_scale, a.m_indices, a.C, a.M, a.N, a.K, a.G, num_windows,
-                     num_ntiles, (int)total, group_w);
+                     num_ntiles, (int)total, group_w, split);
   return hipGetLastError();
 }
 
@@ -472,12 +482,12 @@ using namespace fp8_detail;
 int fp8_num_tiles() { return (int)(sizeof(kFp8Tiles) / sizeof(kFp8Tiles[0])); }
 const TileCfg& fp8_tile(int id) { return kFp8Tiles[id]; }
 
-hipError_t launch_fp8(const Fp8Args& a, int tile_id, int max_wg, int num_cus, hipStream_t s) {
+hipError_t launch_fp8(const Fp8Args& a, int tile_id, const LaunchOpts& o, hipStream_t s) {
   switch (tile_id) {
-    case 0: return launch_cfg<Cfg0>(a, max_wg, num_cus, s);
-    case 1: return launch_cfg<Cfg1>(a, max_wg, num_cus, s);
-    case 2: return launch_cfg<Cfg2>(a, max_wg, num_cus, s);
-    case 3: return launch_cfg<Cfg3>(a, max_wg, num_cus, s);
+    case 0: return launch_cfg<Cfg0>(a, o, s);
+    case 1: return launch_cfg<Cfg1>(a, o, s);
+    case 2: return launch_cfg<Cfg2>(a, o, s);
+    case 3: return launch_cfg<Cfg3>(a, o, s);
     default: return hipErrorInvalidValue;
   }
 }

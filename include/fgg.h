@@ -179,6 +179,13 @@ int fgg_rank_tiles(int kind, int M, int N, int K, int G, int num_cus, fgg_tile* 
 typedef struct {
   int tile_id;         /* -1: use the ranker's top choice                    */
   int max_workgroups;  /* > 0: cap the persistent grid (testing / tuning)    */
+  int run_split;       /* grouped calls: 0 automatic, < 0 never, > 0 always.
+                        * Split mode runs each expert pass of a row window as
+                        * its own workgroup (min(G, tile rows) items per
+                        * tile) instead of one after the other; automatic
+                        * mode uses it when every item runs at once on the
+                        * device (small M: latency).  Results are identical
+                        * either way.                                         */
 } fgg_options;
 
 fgg_status grouped_fp8_gemm_ex(const void* A, const void* B, const float* a_scale,

@@ -94,6 +94,23 @@ def test_grouped_single_expert_equals_dense_bitwise():
     assert np.array_equal(c_bits(Cg), c_bits(Cd))
 
 
+@pytest.mark.parametrize("case", ["grouped_runs", "grouped_unsorted", "grouped_out_of_range",
+                                  "grouped_run_of_one", "grouped_all_padding", "grouped_k896"])
+def test_run_split_modes_agree_bitwise(case):
+    """Split mode (each expert pass of a window its own workgroup) against
+    one workgroup per window: same bits, and within the oracle's tolerance."""
+    p = CASES[case]()
+    d = to_dev(p)
+    for tile in FP4_TILES:
+        log(f"fp4 run split {case} tile {tile}")
+        split = c_bits(run(p, d, tile_id=tile, run_split=1)).copy()
+        C = run(p, d, tile_id=tile, run_split=-1)
+        assert np.array_equal(split, c_bits(C)), (case, tile)
+        assert_parity(p, C, what=f"split {case}/tile{tile}")
+    log(f"fp4 run split {case} capped grid")
+    assert_parity(p, run(p, d, run_split=1, max_workgroups=3), what=f"split {case} capped")
+
+
 @pytest.mark.parametrize("max_wg", [1, 5])
 def test_persistent_loop(max_wg):
     p = _grouped(runs_to_indices([100, 300, 11, 200]), N=384, K=256)

@@ -63,6 +63,36 @@ def test_edge_cases(case, tile):
     assert_parity(p, C, what=f"{case}/tile{tile}")
 
 
+SPLIT_CASES = ["run_of_one", "run_across_windows", "empty_experts", "unsorted_rows",
+               "out_of_range_ids", "many_experts_one_window", "all_padding", "N_not_tile_multiple"]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES + ["p2_m777_g8", "c1_tiny_fp8"])
+def test_run_split_modes_agree_bitwise(case):
+    """Each expert pass of a window as its own workgroup (run_split=1) or
+    all passes in one workgroup (-1): the same arithmetic in the same order,
+    so the same bits, and both within the oracle's tolerance."""
+    p = EDGE[case]() if case in EDGE else make(case)
+    d = to_dev(p)
+    for tile in FP8_TILES:
+        log(f"run split {case} tile {tile}")
+        split = c_bits(run(p, d, tile_id=tile, run_split=1)).copy()
+        C = run(p, d, tile_id=tile, run_split=-1)
+        assert np.array_equal(split, c_bits(C)), (case, tile)
+        assert_parity(p, C, what=f"split {case}/tile{tile}")
+
+
+@pytest.mark.parametrize("max_wg", [1, 5])
+def test_run_split_with_capped_grid(max_wg):
+    """Split items on a capped persistent grid: a workgroup runs passes of
+    many tiles back to back."""
+    p = EDGE["many_experts_one_window"]()
+    for tile in FP8_TILES:
+        log(f"run split capped grid max_wg={max_wg} tile {tile}")
+        C = run(p, tile_id=tile, run_split=1, max_workgroups=max_wg)
+        assert_parity(p, C, what=f"split max_wg={max_wg}/tile{tile}")
+
+
 @pytest.mark.parametrize("max_wg", [1, 3, 7])
 def test_persistent_loop_reinitialises_state(max_wg):
     """A capped grid makes each workgroup run many tiles and passes back to
