@@ -283,6 +283,50 @@ def bench_quant(args, torch):
     print(json.dumps(res), flush=True)
 
 
+def tune_report(args, torch):
+    """Heuristic top-1 against the best of the ranker's top-k on every GEMM
+    workload (the measurement the flashinfer#3948 page reports: the top-1
+    pick's loss and the geomean loss of tuning only the top candidates)."""
+    import fp4_grouped_gemm_amd as fgg
+    from tests.gpu_util import to_dev
+    from workloads import make
+
+    if not os.path.exists(fgg.library_path()):
+        from fp4_grouped_gemm_amd.build import build
+        build()
+    rows, ratios = [], []
+    for name, w in WORKLOADS.items():
+        if w["kind"] not in ("fp8", "fp4"):
+            continue
+        print(f"[bench] tune {name}", file=sys.stderr, flush=True)
+        p = make(name)
+        d = to_dev(p)
+        big = p["M"] * p["N"] * p["K"] > 1 << 34
+        kw = dict(top_k=args.top_k, reps=10 if big else 100)
+        fgg.tune_clear()
+        if p["kind"] == "fp8":
+            _, rep = fgg.grouped_fp8_gemm_tune(d["A"], d["B"], d["a_scale"], d["b_scale"],
+                                               d["m_indices"], **kw)
+        elif p.get("m_indices") is None:
+            _, rep = fgg.fp4_gemm_tune(d["A"], d["B"], d["a_scale"], d["b_scale"], p["alpha"], **kw)
+        else:
+            _, rep = fgg.grouped_fp4_gemm_tune(d["A"], d["B"], d["a_scale"], d["b_scale"],
+                                               d["m_indices"], p["alpha"], **kw)
+        heur, best = rep["ms"][0], rep["ms"][rep["best"]]
+        ratios.append(heur / best)
+        rows.append(dict(workload=name, candidates=rep["tile_id"],
+                         us=[round(1e3 * t, 2) for t in rep["ms"]], heuristic=rep["tile_id"][0],
+                         best=rep["chosen"], heuristic_loss=round(heur / best - 1.0, 4)))
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        del d, p
+        torch.cuda.empty_cache()
+    geo = float(np.exp(np.mean(np.log(ratios))))
+    print(json.dumps({"metric": "bounded autotune: heuristic top-1 time / best-of-top-k time",
+                      "top_k": args.top_k, "workloads": rows,
+                      "geomean_heuristic_over_best": round(geo, 4),
+                      "geomean_loss": round(geo - 1.0, 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +338,11 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="capture the K timed launches in one HIP graph and time its replay "
                          "(launch-bound small shapes: GPU time without host launch overhead)")
+    ap.add_argument("--tune-report", action="store_true",
+                    help="bounded autotune of every GEMM workload: time the ranker's top-k tile "
+                         "configs (the library's *_tune calls), report heuristic top-1 against "
+                         "the best of the k, and the geomean loss; one JSON line")
+    ap.add_argument("--top-k", type=int, default=4)
     ap.add_argument("--run-split", type=int, default=0,
                     help="fgg_options.run_split (0 automatic, -1 never, 1 always)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -332,6 +381,10 @@ def main():
         ms = (time.perf_counter() - t0) * 1e3 / args.steps
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 4),
                           "gbps": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+        return
+
+    if args.tune_report:
+        tune_report(args, torch)
         return
 
     if WORKLOADS[args.workload]["kind"].startswith("quant"):

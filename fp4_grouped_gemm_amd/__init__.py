@@ -18,7 +18,8 @@ import os
 
 __all__ = [
     "grouped_fp8_gemm", "fp4_gemm", "grouped_fp4_gemm", "quantize_fp8_1x128",
-    "quantize_nvfp4", "rank_tiles", "num_tiles",
+    "quantize_nvfp4", "grouped_fp8_gemm_tune", "fp4_gemm_tune", "grouped_fp4_gemm_tune",
+    "tuned_tile", "tune_clear", "rank_tiles", "num_tiles",
     "device_info", "library_path", "load_library", "FP8", "FP4",
 ]
 
@@ -34,6 +35,14 @@ def library_path() -> str:
 class _Tile(ctypes.Structure):
     _fields_ = [("id", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
                 ("waves", ctypes.c_int), ("wg_per_cu", ctypes.c_int), ("score", ctypes.c_float)]
+
+
+TUNE_MAX = 8  # FGG_TUNE_MAX
+
+
+class _TuneReport(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int), ("tile_id", ctypes.c_int * TUNE_MAX),
+                ("ms", ctypes.c_float * TUNE_MAX), ("best", ctypes.c_int)]
 
 
 class _Options(ctypes.Structure):
@@ -52,6 +61,7 @@ def load_library():
     lib = ctypes.CDLL(path)
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     OPT = ctypes.POINTER(_Options)
+    REP = ctypes.POINTER(_TuneReport)
     lib.fgg_last_error.restype = ctypes.c_char_p
     lib.fgg_last_error.argtypes = []
     for name, args in (
@@ -63,10 +73,16 @@ def load_library():
         ("grouped_fp4_gemm_ex", [P, P, P, P, P, F, P, I, I, I, I, OPT, P]),
         ("quantize_fp8_1x128", [P, P, P, I, I, P]),
         ("quantize_nvfp4", [P, P, P, P, I, I, P]),
+        ("grouped_fp8_gemm_tune", [P, P, P, P, P, P, I, I, I, I, I, I, REP, P]),
+        ("fp4_gemm_tune", [P, P, P, P, F, P, I, I, I, I, I, REP, P]),
+        ("grouped_fp4_gemm_tune", [P, P, P, P, P, F, P, I, I, I, I, I, I, REP, P]),
+        ("fgg_tuned_tile", [I, I, I, I, I]),
     ):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = args
+    lib.fgg_tune_clear.restype = None
+    lib.fgg_tune_clear.argtypes = []
     lib.fgg_num_tiles.restype = I
     lib.fgg_num_tiles.argtypes = [I]
     lib.fgg_rank_tiles.restype = I
@@ -131,17 +147,8 @@ def _out(out, M, N, device):
     return _dev(out, "out", device)
 
 
-def grouped_fp8_gemm(A, B, a_scale, b_scale, m_indices, out=None, *, tile_id=None,
-                     max_workgroups=0, run_split=0, stream=None):
-    """C[M, N] (bfloat16) of the grouped block-scaled FP8 GEMM.
-
-    A [M, K] and B [G, N, K] hold E4M3FN codes; a_scale [M, K/128] and
-    b_scale [G, N/128, K/128] are float32; m_indices [M] is int32 (expert id or
-    -1).  See include/fgg.h for the exact definition.  tile_id,
-    max_workgroups and run_split are the fields of fgg_options (run_split: 0
-    automatic, -1 never, 1 always run each expert pass of a row window as its
-    own workgroup).
-    """
+def _fp8_call(A, B, a_scale, b_scale, m_indices, out):
+    """Checks and marshals the arguments of grouped_fp8_gemm (and _tune)."""
     torch = _torch()
     A, B = _bytes(A, "A"), _bytes(B, "B")
     dev = A.device
@@ -161,13 +168,47 @@ def grouped_fp8_gemm(A, B, a_scale, b_scale, m_indices, out=None, *, tile_id=Non
                  (m_indices, "m_indices")):
         _dev(t, n, dev)
     C = _out(out, M, N, dev)
-    lib = load_library()
+    args = (A.data_ptr(), B.data_ptr(), a_scale.data_ptr(), b_scale.data_ptr(),
+            m_indices.data_ptr(), C.data_ptr(), M, N, K, G)
+    return C, dev, args
+
+
+def grouped_fp8_gemm(A, B, a_scale, b_scale, m_indices, out=None, *, tile_id=None,
+                     max_workgroups=0, run_split=0, stream=None):
+    """C[M, N] (bfloat16) of the grouped block-scaled FP8 GEMM.
+
+    A [M, K] and B [G, N, K] hold E4M3FN codes; a_scale [M, K/128] and
+    b_scale [G, N/128, K/128] are float32; m_indices [M] is int32 (expert id or
+    -1).  See include/fgg.h for the exact definition.  tile_id,
+    max_workgroups and run_split are the fields of fgg_options (run_split: 0
+    automatic, -1 never, 1 always run each expert pass of a row window as its
+    own workgroup).
+    """
+    torch = _torch()
+    C, dev, args = _fp8_call(A, B, a_scale, b_scale, m_indices, out)
     with torch.cuda.device(dev):
-        _check(lib.grouped_fp8_gemm_ex(A.data_ptr(), B.data_ptr(), a_scale.data_ptr(),
-                                       b_scale.data_ptr(), m_indices.data_ptr(), C.data_ptr(),
-                                       M, N, K, G, _opts(tile_id, max_workgroups, run_split),
-                                       _stream_ptr(stream, dev)))
+        _check(load_library().grouped_fp8_gemm_ex(*args, _opts(tile_id, max_workgroups, run_split),
+                                                  _stream_ptr(stream, dev)))
     return C
+
+
+def _report(r):
+    return dict(tile_id=list(r.tile_id[:r.n]), ms=list(r.ms[:r.n]), best=r.best,
+                chosen=r.tile_id[r.best] if r.n else -1)
+
+
+def grouped_fp8_gemm_tune(A, B, a_scale, b_scale, m_indices, out=None, *, top_k=4, reps=5,
+                          stream=None):
+    """Time the ranker's top_k tile configs on these inputs and record the
+    fastest for this shape (C ABI grouped_fp8_gemm_tune; synchronises).
+    Returns (C, report) with report = {tile_id, ms, best, chosen}."""
+    torch = _torch()
+    C, dev, args = _fp8_call(A, B, a_scale, b_scale, m_indices, out)
+    rep = _TuneReport()
+    with torch.cuda.device(dev):
+        _check(load_library().grouped_fp8_gemm_tune(*args, int(top_k), int(reps),
+                                                    ctypes.byref(rep), _stream_ptr(stream, dev)))
+    return C, _report(rep)
 
 
 def _fp4_shapes(A, a_scale, b_scale):
@@ -180,31 +221,50 @@ def _fp4_shapes(A, a_scale, b_scale):
     return M, 2 * K2
 
 
+def _fp4_call(A, B, a_scale, b_scale, m_indices, alpha, out):
+    """Checks and marshals the arguments of fp4_gemm (m_indices None) or
+    grouped_fp4_gemm (and their _tune variants)."""
+    torch = _torch()
+    A, B = _bytes(A, "A"), _bytes(B, "B")
+    dev = A.device
+    grouped = m_indices is not None
+    if A.dim() != 2 or B.dim() != (3 if grouped else 2):
+        raise ValueError("A must be [M, K/2] and B " + ("[G, N, K/2]" if grouped else "[N, K/2]"))
+    M, K = _fp4_shapes(A, a_scale, b_scale)
+    G, N, K2 = B.shape if grouped else (1, *B.shape)
+    if K2 * 2 != K:
+        raise ValueError("A and B disagree on K")
+    sa, sb = _bytes(a_scale, "a_scale"), _bytes(b_scale, "b_scale")
+    want_sb = (G, N, K // 16) if grouped else (N, K // 16)
+    if tuple(sa.shape) != (M, K // 16) or tuple(sb.shape) != want_sb:
+        raise ValueError(f"scale shapes must be ({M}, {K // 16}) and {want_sb}")
+    tensors = [(A, "A"), (B, "B"), (sa, "a_scale"), (sb, "b_scale")]
+    if grouped:
+        if m_indices.dtype != torch.int32 or tuple(m_indices.shape) != (M,):
+            raise ValueError(f"m_indices must be int32 of shape ({M},)")
+        tensors.append((m_indices, "m_indices"))
+    for t, n in tensors:
+        _dev(t, n, dev)
+    C = _out(out, M, N, dev)
+    if grouped:
+        args = (A.data_ptr(), B.data_ptr(), sa.data_ptr(), sb.data_ptr(), m_indices.data_ptr(),
+                float(alpha), C.data_ptr(), M, N, K, G)
+    else:
+        args = (A.data_ptr(), B.data_ptr(), sa.data_ptr(), sb.data_ptr(), float(alpha),
+                C.data_ptr(), M, N, K)
+    return C, dev, args
+
+
 def fp4_gemm(A, B, a_scale, b_scale, alpha, out=None, *, tile_id=None, max_workgroups=0,
              stream=None):
     """C[M, N] (bfloat16) of the dense NVFP4 GEMM: A [M, K/2] and B [N, K/2]
     packed E2M1, a_scale [M, K/16] and b_scale [N, K/16] E4M3 bytes, alpha =
     product of the two global scales."""
     torch = _torch()
-    A, B = _bytes(A, "A"), _bytes(B, "B")
-    dev = A.device
-    if A.dim() != 2 or B.dim() != 2:
-        raise ValueError("A must be [M, K/2] and B [N, K/2]")
-    M, K = _fp4_shapes(A, a_scale, b_scale)
-    N = B.shape[0]
-    if B.shape[1] * 2 != K:
-        raise ValueError("A and B disagree on K")
-    sa, sb = _bytes(a_scale, "a_scale"), _bytes(b_scale, "b_scale")
-    if tuple(sa.shape) != (M, K // 16) or tuple(sb.shape) != (N, K // 16):
-        raise ValueError(f"scale shapes must be ({M}, {K // 16}) and ({N}, {K // 16})")
-    for t, n in ((A, "A"), (B, "B"), (sa, "a_scale"), (sb, "b_scale")):
-        _dev(t, n, dev)
-    C = _out(out, M, N, dev)
-    lib = load_library()
+    C, dev, args = _fp4_call(A, B, a_scale, b_scale, None, alpha, out)
     with torch.cuda.device(dev):
-        _check(lib.fp4_gemm_ex(A.data_ptr(), B.data_ptr(), sa.data_ptr(), sb.data_ptr(),
-                               float(alpha), C.data_ptr(), M, N, K,
-                               _opts(tile_id, max_workgroups), _stream_ptr(stream, dev)))
+        _check(load_library().fp4_gemm_ex(*args, _opts(tile_id, max_workgroups),
+                                          _stream_ptr(stream, dev)))
     return C
 
 
@@ -213,29 +273,45 @@ def grouped_fp4_gemm(A, B, a_scale, b_scale, m_indices, alpha, out=None, *, tile
     """C[M, N] (bfloat16) of the grouped NVFP4 GEMM: B [G, N, K/2], b_scale
     [G, N, K/16]; m_indices int32 [M] routes rows (-1 = padding)."""
     torch = _torch()
-    A, B = _bytes(A, "A"), _bytes(B, "B")
-    dev = A.device
-    if A.dim() != 2 or B.dim() != 3:
-        raise ValueError("A must be [M, K/2] and B [G, N, K/2]")
-    M, K = _fp4_shapes(A, a_scale, b_scale)
-    G, N, K2 = B.shape
-    if K2 * 2 != K:
-        raise ValueError("A and B disagree on K")
-    sa, sb = _bytes(a_scale, "a_scale"), _bytes(b_scale, "b_scale")
-    if tuple(sa.shape) != (M, K // 16) or tuple(sb.shape) != (G, N, K // 16):
-        raise ValueError(f"scale shapes must be ({M}, {K // 16}) and ({G}, {N}, {K // 16})")
-    if m_indices.dtype != torch.int32 or tuple(m_indices.shape) != (M,):
-        raise ValueError(f"m_indices must be int32 of shape ({M},)")
-    for t, n in ((A, "A"), (B, "B"), (sa, "a_scale"), (sb, "b_scale"), (m_indices, "m_indices")):
-        _dev(t, n, dev)
-    C = _out(out, M, N, dev)
-    lib = load_library()
+    C, dev, args = _fp4_call(A, B, a_scale, b_scale, m_indices, alpha, out)
     with torch.cuda.device(dev):
-        _check(lib.grouped_fp4_gemm_ex(A.data_ptr(), B.data_ptr(), sa.data_ptr(), sb.data_ptr(),
-                                       m_indices.data_ptr(), float(alpha), C.data_ptr(), M, N, K,
-                                       G, _opts(tile_id, max_workgroups, run_split),
-                                       _stream_ptr(stream, dev)))
+        _check(load_library().grouped_fp4_gemm_ex(*args, _opts(tile_id, max_workgroups, run_split),
+                                                  _stream_ptr(stream, dev)))
     return C
+
+
+def fp4_gemm_tune(A, B, a_scale, b_scale, alpha, out=None, *, top_k=4, reps=5, stream=None):
+    """Bounded autotune of fp4_gemm for this shape (as grouped_fp8_gemm_tune)."""
+    torch = _torch()
+    C, dev, args = _fp4_call(A, B, a_scale, b_scale, None, alpha, out)
+    rep = _TuneReport()
+    with torch.cuda.device(dev):
+        _check(load_library().fp4_gemm_tune(*args, int(top_k), int(reps), ctypes.byref(rep),
+                                            _stream_ptr(stream, dev)))
+    return C, _report(rep)
+
+
+def grouped_fp4_gemm_tune(A, B, a_scale, b_scale, m_indices, alpha, out=None, *, top_k=4, reps=5,
+                          stream=None):
+    """Bounded autotune of grouped_fp4_gemm for this shape (as
+    grouped_fp8_gemm_tune)."""
+    torch = _torch()
+    C, dev, args = _fp4_call(A, B, a_scale, b_scale, m_indices, alpha, out)
+    rep = _TuneReport()
+    with torch.cuda.device(dev):
+        _check(load_library().grouped_fp4_gemm_tune(*args, int(top_k), int(reps),
+                                                    ctypes.byref(rep), _stream_ptr(stream, dev)))
+    return C, _report(rep)
+
+
+def tuned_tile(kind: int, M: int, N: int, K: int, G: int = 1) -> int:
+    """The tile config recorded by a *_tune call for this shape, or -1."""
+    return load_library().fgg_tuned_tile(kind, M, N, K, G)
+
+
+def tune_clear() -> None:
+    """Forget every recorded tuning choice (C ABI fgg_tune_clear)."""
+    load_library().fgg_tune_clear()
 
 
 def num_tiles(kind: int) -> int:

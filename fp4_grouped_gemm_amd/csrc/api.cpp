@@ -15,7 +15,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <limits>
+#include <map>
 #include <mutex>
+#include <tuple>
 #include <string>
 #include <vector>
 
@@ -146,7 +149,31 @@ int rank(int kind, int M, int N, int G, int num_cus, fgg_tile* out, int max_out)
   return k;
 }
 
-fgg_status pick_tile(const char* fn, int kind, int M, int N, int G, int num_cus,
+// ------------------------------------------------------------ autotuning
+// Configs chosen by the *_tune entry points, per (kind, device, shape).
+struct TuneKey {
+  int kind, dev, M, N, K, G;
+  bool operator<(const TuneKey& o) const {
+    return std::tie(kind, dev, M, N, K, G) < std::tie(o.kind, o.dev, o.M, o.N, o.K, o.G);
+  }
+};
+std::mutex g_tune_mu;
+std::map<TuneKey, int> g_tuned;
+
+int current_dev() {
+  int dev = -1;
+  return hipGetDevice(&dev) == hipSuccess ? dev : -1;
+}
+
+int tuned_tile(int kind, int M, int N, int K, int G) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  auto it = g_tuned.find(TuneKey{kind, current_dev(), M, N, K, G});
+  return it == g_tuned.end() ? -1 : it->second;
+}
+
+// Tile for a call: the explicit option, else the recorded tuning result for
+// this shape, else the ranker's top choice.
+fgg_status pick_tile(const char* fn, int kind, int M, int N, int K, int G, int num_cus,
                      const fgg_options* opt, int* tile_id) {
   const int n = kind == FGG_KIND_FP8 ? fgg::fp8_num_tiles() : fgg::fp4_num_tiles();
   if (opt && opt->tile_id >= 0) {
@@ -154,9 +181,58 @@ fgg_status pick_tile(const char* fn, int kind, int M, int N, int G, int num_cus,
     *tile_id = opt->tile_id;
     return FGG_OK;
   }
+  const int t = tuned_tile(kind, M, N, K, G);
+  if (t >= 0) {
+    *tile_id = t;
+    return FGG_OK;
+  }
   fgg_tile best;
   rank(kind, M, N, G, num_cus, &best, 1);
   *tile_id = best.id;
+  return FGG_OK;
+}
+
+// Time the ranker's top candidates with `launch(tile_id)` (returns the
+// launch's hipError_t) and record the fastest.  Bounded: at most
+// FGG_TUNE_MAX configs x (reps + 1) launches.
+template <class Launch>
+fgg_status run_tune(const char* fn, int kind, int M, int N, int K, int G, int num_cus, int top_k,
+                    int reps, fgg_tune_report* report, hipStream_t s, Launch launch) {
+  if (top_k < 1) return fail(FGG_EINVAL, fn, "top_k must be >= 1, got %d", top_k);
+  if (reps < 1 || reps > 100000) return fail(FGG_EINVAL, fn, "reps must be in [1, 100000], got %d", reps);
+  fgg_tile cand[FGG_TUNE_MAX];
+  const int n = rank(kind, M, N, G, num_cus, cand, std::min(top_k, FGG_TUNE_MAX));
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  fgg_tune_report r;
+  std::memset(&r, 0, sizeof(r));
+  r.n = n;
+  float best_ms = std::numeric_limits<float>::infinity();
+  for (int i = 0; i < n && e == hipSuccess; ++i) {
+    r.tile_id[i] = cand[i].id;
+    e = launch(cand[i].id);  // untimed: first use of this config's code
+    if (e == hipSuccess) e = hipEventRecord(e0, s);
+    for (int k = 0; k < reps && e == hipSuccess; ++k) e = launch(cand[i].id);
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+    r.ms[i] = ms / (float)reps;
+    if (e == hipSuccess && r.ms[i] < best_ms) {
+      best_ms = r.ms[i];
+      r.best = i;
+    }
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return fail(FGG_EHIP, fn, "tuning failed: %s", hipGetErrorString(e));
+  {
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    g_tuned[TuneKey{kind, current_dev(), M, N, K, G}] = r.tile_id[r.best];
+  }
+  if (report) *report = r;
+  g_err.clear();
   return FGG_OK;
 }
 
@@ -209,19 +285,44 @@ fgg_status fgg_device_info(int* num_cus, int* lds_per_block, int* clock_khz, cha
   return FGG_OK;
 }
 
+// Checks and device facts of a grouped FP8 call; fills the kernel arguments.
+static fgg_status fp8_prepare(const char* fn, const void* A, const void* B, const float* a_scale,
+                              const float* b_scale, const int32_t* m_indices, void* C, int M,
+                              int N, int K, int G, fgg::Fp8Args* a, const DeviceFacts** d) {
+  fgg_status st = check_common(fn, A, B, a_scale, b_scale, C, M, N, K, G, true, m_indices, 4);
+  if (st != FGG_OK) return st;
+  if (!(*d = current_device(fn, &st))) return st;
+  *a = fgg::Fp8Args{static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), a_scale,
+                    b_scale, m_indices, static_cast<uint16_t*>(C), M, N, K, G};
+  return FGG_OK;
+}
+
 fgg_status grouped_fp8_gemm_ex(const void* A, const void* B, const float* a_scale,
                                const float* b_scale, const int32_t* m_indices, void* C, int M,
                                int N, int K, int G, const fgg_options* opt, void* stream) {
   const char* fn = "grouped_fp8_gemm";
-  fgg_status st = check_common(fn, A, B, a_scale, b_scale, C, M, N, K, G, true, m_indices, 4);
+  fgg::Fp8Args a;
+  const DeviceFacts* d = nullptr;
+  fgg_status st = fp8_prepare(fn, A, B, a_scale, b_scale, m_indices, C, M, N, K, G, &a, &d);
   if (st != FGG_OK) return st;
-  const DeviceFacts* d = current_device(fn, &st);
-  if (!d) return st;
   int tile;
-  if ((st = pick_tile(fn, FGG_KIND_FP8, M, N, G, d->num_cus, opt, &tile)) != FGG_OK) return st;
-  fgg::Fp8Args a{static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), a_scale, b_scale,
-                 m_indices, static_cast<uint16_t*>(C), M, N, K, G};
+  if ((st = pick_tile(fn, FGG_KIND_FP8, M, N, K, G, d->num_cus, opt, &tile)) != FGG_OK) return st;
   return launched(fn, fgg::launch_fp8(a, tile, launch_opts(opt, d), static_cast<hipStream_t>(stream)));
+}
+
+fgg_status grouped_fp8_gemm_tune(const void* A, const void* B, const float* a_scale,
+                                 const float* b_scale, const int32_t* m_indices, void* C, int M,
+                                 int N, int K, int G, int top_k, int reps,
+                                 fgg_tune_report* report, void* stream) {
+  const char* fn = "grouped_fp8_gemm_tune";
+  fgg::Fp8Args a;
+  const DeviceFacts* d = nullptr;
+  fgg_status st = fp8_prepare(fn, A, B, a_scale, b_scale, m_indices, C, M, N, K, G, &a, &d);
+  if (st != FGG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const fgg::LaunchOpts o = launch_opts(nullptr, d);
+  return run_tune(fn, FGG_KIND_FP8, M, N, K, G, d->num_cus, top_k, reps, report, s,
+                  [&](int tile) { return fgg::launch_fp8(a, tile, o, s); });
 }
 
 fgg_status grouped_fp8_gemm(const void* A, const void* B, const float* a_scale,
@@ -230,21 +331,48 @@ fgg_status grouped_fp8_gemm(const void* A, const void* B, const float* a_scale,
   return grouped_fp8_gemm_ex(A, B, a_scale, b_scale, m_indices, C, M, N, K, G, nullptr, stream);
 }
 
+// Checks and device facts of an NVFP4 call; fills the kernel arguments.
+static fgg_status fp4_prepare(const char* fn, const void* A, const void* B, const void* a_scale,
+                              const void* b_scale, const int32_t* m_indices, float alpha, void* C,
+                              int M, int N, int K, int G, bool grouped, fgg::Fp4Args* a,
+                              const DeviceFacts** d) {
+  fgg_status st = check_common(fn, A, B, a_scale, b_scale, C, M, N, K, G, grouped, m_indices, 16);
+  if (st != FGG_OK) return st;
+  if (!std::isfinite(alpha)) return fail(FGG_EINVAL, fn, "alpha must be finite");
+  if (!(*d = current_device(fn, &st))) return st;
+  *a = fgg::Fp4Args{static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B),
+                    static_cast<const uint8_t*>(a_scale), static_cast<const uint8_t*>(b_scale),
+                    grouped ? m_indices : nullptr, alpha, static_cast<uint16_t*>(C), M, N, K, G};
+  return FGG_OK;
+}
+
 static fgg_status fp4_common(const char* fn, const void* A, const void* B, const void* a_scale,
                              const void* b_scale, const int32_t* m_indices, float alpha, void* C,
                              int M, int N, int K, int G, bool grouped, const fgg_options* opt,
                              void* stream) {
-  fgg_status st = check_common(fn, A, B, a_scale, b_scale, C, M, N, K, G, grouped, m_indices, 16);
+  fgg::Fp4Args a;
+  const DeviceFacts* d = nullptr;
+  fgg_status st = fp4_prepare(fn, A, B, a_scale, b_scale, m_indices, alpha, C, M, N, K, G, grouped,
+                              &a, &d);
   if (st != FGG_OK) return st;
-  if (!std::isfinite(alpha)) return fail(FGG_EINVAL, fn, "alpha must be finite");
-  const DeviceFacts* d = current_device(fn, &st);
-  if (!d) return st;
   int tile;
-  if ((st = pick_tile(fn, FGG_KIND_FP4, M, N, G, d->num_cus, opt, &tile)) != FGG_OK) return st;
-  fgg::Fp4Args a{static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B),
-                 static_cast<const uint8_t*>(a_scale), static_cast<const uint8_t*>(b_scale),
-                 grouped ? m_indices : nullptr, alpha, static_cast<uint16_t*>(C), M, N, K, G};
+  if ((st = pick_tile(fn, FGG_KIND_FP4, M, N, K, G, d->num_cus, opt, &tile)) != FGG_OK) return st;
   return launched(fn, fgg::launch_fp4(a, tile, launch_opts(opt, d), static_cast<hipStream_t>(stream)));
+}
+
+static fgg_status fp4_tune(const char* fn, const void* A, const void* B, const void* a_scale,
+                           const void* b_scale, const int32_t* m_indices, float alpha, void* C,
+                           int M, int N, int K, int G, bool grouped, int top_k, int reps,
+                           fgg_tune_report* report, void* stream) {
+  fgg::Fp4Args a;
+  const DeviceFacts* d = nullptr;
+  fgg_status st = fp4_prepare(fn, A, B, a_scale, b_scale, m_indices, alpha, C, M, N, K, G, grouped,
+                              &a, &d);
+  if (st != FGG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const fgg::LaunchOpts o = launch_opts(nullptr, d);
+  return run_tune(fn, FGG_KIND_FP4, M, N, K, G, d->num_cus, top_k, reps, report, s,
+                  [&](int tile) { return fgg::launch_fp4(a, tile, o, s); });
 }
 
 fgg_status fp4_gemm_ex(const void* A, const void* B, const void* a_scale, const void* b_scale,
@@ -271,6 +399,28 @@ fgg_status grouped_fp4_gemm(const void* A, const void* B, const void* a_scale,
                             int M, int N, int K, int G, void* stream) {
   return grouped_fp4_gemm_ex(A, B, a_scale, b_scale, m_indices, alpha, C, M, N, K, G, nullptr,
                              stream);
+}
+
+fgg_status fp4_gemm_tune(const void* A, const void* B, const void* a_scale, const void* b_scale,
+                         float alpha, void* C, int M, int N, int K, int top_k, int reps,
+                         fgg_tune_report* report, void* stream) {
+  return fp4_tune("fp4_gemm_tune", A, B, a_scale, b_scale, nullptr, alpha, C, M, N, K, 1, false,
+                  top_k, reps, report, stream);
+}
+
+fgg_status grouped_fp4_gemm_tune(const void* A, const void* B, const void* a_scale,
+                                 const void* b_scale, const int32_t* m_indices, float alpha,
+                                 void* C, int M, int N, int K, int G, int top_k, int reps,
+                                 fgg_tune_report* report, void* stream) {
+  return fp4_tune("grouped_fp4_gemm_tune", A, B, a_scale, b_scale, m_indices, alpha, C, M, N, K, G,
+                  true, top_k, reps, report, stream);
+}
+
+int fgg_tuned_tile(int kind, int M, int N, int K, int G) { return tuned_tile(kind, M, N, K, G); }
+
+void fgg_tune_clear(void) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  g_tuned.clear();
 }
 
 // Activation quantisers (the step before the GEMM).

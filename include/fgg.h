@@ -167,11 +167,12 @@ typedef struct {
 /* Number of compiled tile configs for `kind`, or -1 for a bad kind. */
 int fgg_num_tiles(int kind);
 
-/* Rank every tile config of `kind` for a problem.  `rows_hint` is the
- * expected number of row tiles' worth of work (pass M when the routing is
- * unknown); `num_cus` the compute units (256 on MI355X; <= 0 means query the
- * current device).  Writes up to `max_out` entries, best first, and returns
- * how many were written, or -1 with fgg_last_error() set. */
+/* Rank every tile config of `kind` for a problem of M rows (G experts; the
+ * routing is unknown on the host, so every expert boundary is assumed to fall
+ * inside a row window), N columns and K; `num_cus` the compute units (256 on
+ * MI355X; <= 0 means query the current device).  Writes up to `max_out`
+ * entries, best first, and returns how many were written, or -1 with
+ * fgg_last_error() set. */
 int fgg_rank_tiles(int kind, int M, int N, int K, int G, int num_cus, fgg_tile* out,
                    int max_out);
 
@@ -199,6 +200,51 @@ fgg_status grouped_fp4_gemm_ex(const void* A, const void* B, const void* a_scale
                                const void* b_scale, const int32_t* m_indices, float alpha,
                                void* C, int M, int N, int K, int G, const fgg_options* opt,
                                void* stream);
+
+/* ------------------------------------------------------------------------
+ * Bounded autotuning of the ranker's top choices (the flashinfer#3948 page,
+ * "Code analysis 1": rank the candidate configs with the heuristic and
+ * profile only the top few instead of all of them).
+ *
+ * Each *_tune call takes the arguments of its GEMM (same checks, same
+ * errors), times the ranker's best min(top_k, FGG_TUNE_MAX) tile configs on
+ * those inputs -- one untimed launch, then `reps` launches between two HIP
+ * events on `stream`, per config -- and records the fastest for (kind, M, N,
+ * K, G) on the current device.  Later calls of that GEMM on that shape with
+ * no explicit tile_id launch the recorded config instead of the ranker's
+ * top one.  C is overwritten (with the GEMM's result).  The call
+ * synchronises `stream` and is not graph-capturable; it allocates no device
+ * memory.  `report` (may be NULL) receives the candidates in ranker order
+ * with their mean milliseconds per launch.  Recorded choices are process-wide
+ * and thread-safe; fgg_tune_clear() forgets them all.
+ * ------------------------------------------------------------------------ */
+#define FGG_TUNE_MAX 8
+
+typedef struct {
+  int n;                      /* candidates timed                              */
+  int tile_id[FGG_TUNE_MAX];  /* ranker order: tile_id[0] is the heuristic's   */
+  float ms[FGG_TUNE_MAX];     /* mean time per launch                          */
+  int best;                   /* index (into tile_id / ms) of the fastest      */
+} fgg_tune_report;
+
+fgg_status grouped_fp8_gemm_tune(const void* A, const void* B, const float* a_scale,
+                                 const float* b_scale, const int32_t* m_indices, void* C, int M,
+                                 int N, int K, int G, int top_k, int reps,
+                                 fgg_tune_report* report, void* stream);
+fgg_status fp4_gemm_tune(const void* A, const void* B, const void* a_scale, const void* b_scale,
+                         float alpha, void* C, int M, int N, int K, int top_k, int reps,
+                         fgg_tune_report* report, void* stream);
+fgg_status grouped_fp4_gemm_tune(const void* A, const void* B, const void* a_scale,
+                                 const void* b_scale, const int32_t* m_indices, float alpha,
+                                 void* C, int M, int N, int K, int G, int top_k, int reps,
+                                 fgg_tune_report* report, void* stream);
+
+/* The recorded config for a shape on the current device (kind as
+ * fgg_rank_tiles; G = 1 for fp4_gemm), or -1 when none is recorded. */
+int fgg_tuned_tile(int kind, int M, int N, int K, int G);
+
+/* Forget every recorded choice. */
+void fgg_tune_clear(void);
 
 /* Device facts cached once per device (gfx950 check, CU count, LDS bytes per
  * workgroup).  Returns FGG_EDEVICE when no usable device is present. */

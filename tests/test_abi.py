@@ -87,6 +87,24 @@ def test_quantizer_validation():
     assert lib.quantize_nvfp4(P, P + 8, P, P, 8, 256, None) == 2
 
 
+def test_tune_validation_and_cache_without_gpu():
+    """The *_tune entry points check their GEMM's arguments first (same
+    messages, named after the tune call); with no tuning recorded the cache
+    answers -1, and clearing it is always allowed."""
+    lib = fgg.load_library()
+    rep = fgg._TuneReport()
+    st = lib.grouped_fp8_gemm_tune(P, P, P, P, P, P, 256, 256, 200, 2, 4, 5, ctypes.byref(rep), None)
+    msg = lib.fgg_last_error().decode()
+    assert st == 1 and msg.startswith("grouped_fp8_gemm_tune:") and "K % 128" in msg
+    st = lib.fp4_gemm_tune(P, P, P, P, float("nan"), P, 100, 256, 128, 4, 5, None, None)
+    assert st == 1 and "alpha" in lib.fgg_last_error().decode()
+    st = lib.grouped_fp4_gemm_tune(P, P, P, P, 0, 1.0, P, 100, 256, 128, 2, 4, 5, None, None)
+    assert st == 1 and lib.fgg_last_error().decode().startswith("grouped_fp4_gemm_tune:")
+    assert lib.fgg_tuned_tile(fgg.FP8, 256, 256, 512, 2) == -1
+    lib.fgg_tune_clear()
+    assert fgg.tuned_tile(fgg.FP4, 2048, 36864, 4608) == -1
+
+
 def test_python_binding_raises_value_error():
     torch = pytest.importorskip("torch")
     A = torch.zeros((4, 128), dtype=torch.uint8)
