@@ -42,6 +42,7 @@ from .gemm import (  # noqa: F401
     grouped_fp8_gemm,
     fp4_gemm,
     grouped_fp4_gemm,
+    fp4_gemm_problems,
     rms_nonpadding,
     check_tolerance,
 )

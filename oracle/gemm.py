@@ -116,7 +116,12 @@ def fp4_gemm(A, B, a_scale, b_scale, alpha, rows=None) -> np.ndarray:
 def grouped_fp4_gemm(A, B, a_scale, b_scale, m_indices, alpha, rows=None) -> np.ndarray:
     """C (float64, [len(rows), N]) of the grouped NVFP4 GEMM: row i uses
     B[g], b_scale[g] with g = m_indices[i]; rows with g = -1 are zero.
-    Parity: pinned (G = 1 equals the dense form; brute force; invariants)."""
+    ``alpha`` is one float (one global scale for every expert's B) or a
+    sequence of G floats, alpha[g] = gA * gB[g] (a global scale per expert:
+    the per-group scaling of the cutlass#3124 page's grouped block-scaled
+    GEMM); either way expert g's rows are multiplied by its alpha.
+    Parity: pinned (G = 1 equals the dense form; brute force with distinct
+    per-expert alphas; invariants)."""
     A = np.asarray(A, np.uint8)
     B = np.asarray(B, np.uint8)
     m_indices = np.asarray(m_indices, np.int32)
@@ -124,6 +129,7 @@ def grouped_fp4_gemm(A, B, a_scale, b_scale, m_indices, alpha, rows=None) -> np.
     G, N, K2b = B.shape
     assert K2 == K2b and m_indices.shape == (M,)
     assert np.all((m_indices >= -1) & (m_indices < G)), "expert ids must lie in [-1, G)"
+    alphas = np.broadcast_to(np.asarray(alpha, np.float32), (G,))
     rows = _rows_arg(rows, M)
     ids = m_indices[rows]
     C = np.zeros((rows.size, N), dtype=np.float64)
@@ -132,8 +138,19 @@ def grouped_fp4_gemm(A, B, a_scale, b_scale, m_indices, alpha, rows=None) -> np.
         if sel.size == 0:
             continue
         r = rows[sel]
-        C[sel] = fp4_gemm(A[r], B[g], np.asarray(a_scale)[r], np.asarray(b_scale)[g], alpha)
+        C[sel] = fp4_gemm(A[r], B[g], np.asarray(a_scale)[r], np.asarray(b_scale)[g], alphas[g])
     return C
+
+
+def fp4_gemm_problems(problems) -> list:
+    """A batch of independent dense NVFP4 GEMMs of different shapes in one
+    call (cutlass#3124 page, "Intro": one launch runs several GEMMs whose M,
+    N and K differ).  ``problems`` is a sequence of dicts with A [M, K/2], B
+    [N, K/2], a_scale [M, K/16], b_scale [N, K/16] and alpha; the result is
+    the list of their C (float64 [M, N]), each exactly fp4_gemm of its
+    problem.  Parity: pinned (row and column slices of one problem tile that
+    problem's result; exact brute force)."""
+    return [fp4_gemm(q["A"], q["B"], q["a_scale"], q["b_scale"], q["alpha"]) for q in problems]
 
 
 def rms_nonpadding(ref, ids=None) -> float:

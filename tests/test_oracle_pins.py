@@ -127,6 +127,60 @@ def test_nvfp4_oracle_equals_exact_integer(grouped):
             assert abs(C[i, n] - float(exact)) <= 2.0 ** -45 * (abs(float(exact)) + 1e-30) + 1e-300
 
 
+def test_nvfp4_per_expert_alpha_equals_exact_integer():
+    """Distinct per-expert alphas (not powers of two) against the exact
+    integer brute force, expert by expert."""
+    rng = np.random.default_rng(17)
+    ids = np.array([2, 0, -1, 1, 2, 0, 0, 1], np.int32)
+    p = nvfp4_problem(ids, 8, 128, 256, 3, rng)
+    alphas = np.array([0.3, 1.75e-3, 37.0], np.float32)
+    C = oracle.grouped_fp4_gemm(p["A"], p["B"], p["a_scale"], p["b_scale"], ids, alphas)
+    tot = brute_nvfp4(p["A"], p["B"], p["a_scale"], p["b_scale"], ids, None)
+    for i in range(8):
+        if ids[i] < 0:
+            assert np.all(C[i] == 0.0)
+            continue
+        a = Fraction(float(alphas[ids[i]]))
+        for n in range(128):
+            exact = a * int(tot[i, n]) / (1 << 20)
+            assert abs(C[i, n] - float(exact)) <= 2.0 ** -45 * (abs(float(exact)) + 1e-30) + 1e-300
+
+
+def test_nvfp4_per_expert_alpha_invariants():
+    rng = np.random.default_rng(18)
+    ids = runs_to_indices([5, 0, 7, 4])
+    p = nvfp4_problem(ids, ids.size, 128, 128, 4, rng)
+    args = (p["A"], p["B"], p["a_scale"], p["b_scale"], ids)
+    one = oracle.grouped_fp4_gemm(*args, np.float32(0.625))
+    same = oracle.grouped_fp4_gemm(*args, np.full(4, 0.625, np.float32))
+    assert np.array_equal(one, same)
+    # scaling one expert's alpha by 2^k scales exactly that expert's rows
+    base = oracle.grouped_fp4_gemm(*args, np.ones(4, np.float32))
+    scaled = oracle.grouped_fp4_gemm(*args, np.array([1, 1, 8, 1], np.float32))
+    assert np.array_equal(scaled[ids == 2], 8 * base[ids == 2])
+    assert np.array_equal(scaled[ids != 2], base[ids != 2])
+
+
+def test_nvfp4_problem_batch_slices_tile_one_problem():
+    """Row slices and column slices of one dense problem, given as separate
+    problems, tile that problem's result; problems of different K are each
+    exact."""
+    rng = np.random.default_rng(19)
+    p = nvfp4_problem(None, 40, 384, 256, 1, rng)
+    full = oracle.fp4_gemm(p["A"], p["B"], p["a_scale"], p["b_scale"], p["alpha"])
+    parts = [dict(A=p["A"][r], B=p["B"][c], a_scale=p["a_scale"][r], b_scale=p["b_scale"][c],
+                  alpha=p["alpha"]) for r in (slice(0, 17), slice(17, 40))
+             for c in (slice(0, 128), slice(128, 384))]
+    out = oracle.fp4_gemm_problems(parts)
+    assert np.array_equal(np.block([[out[0], out[1]], [out[2], out[3]]]), full)
+    q = nvfp4_problem(None, 5, 128, 512, 1, np.random.default_rng(20))
+    (c1, c2) = oracle.fp4_gemm_problems([p, q])
+    tot = brute_nvfp4(q["A"], q["B"], q["a_scale"], q["b_scale"], None, None)
+    exact = np.array([[float(Fraction(float(q["alpha"])) * int(t) / (1 << 20)) for t in row]
+                      for row in tot])
+    assert np.allclose(c2, exact, rtol=2.0 ** -45, atol=0) and c1.shape == (40, 384)
+
+
 # -------------------------------------------------------------- worked examples
 @pytest.mark.parametrize("ex", load_examples(), ids=lambda e: e["name"])
 def test_worked_examples(ex):
