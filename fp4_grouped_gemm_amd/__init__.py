@@ -19,7 +19,7 @@ import os
 __all__ = [
     "grouped_fp8_gemm", "fp4_gemm", "grouped_fp4_gemm", "quantize_fp8_1x128",
     "quantize_nvfp4", "grouped_fp8_gemm_tune", "fp4_gemm_tune", "grouped_fp4_gemm_tune",
-    "tuned_tile", "tune_clear", "rank_tiles", "num_tiles",
+    "tuned_tile", "tune_clear", "fp4_gemm_problems", "rank_tiles", "num_tiles",
     "device_info", "library_path", "load_library", "FP8", "FP4",
 ]
 
@@ -43,6 +43,15 @@ TUNE_MAX = 8  # FGG_TUNE_MAX
 class _TuneReport(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int), ("tile_id", ctypes.c_int * TUNE_MAX),
                 ("ms", ctypes.c_float * TUNE_MAX), ("best", ctypes.c_int)]
+
+
+MAX_PROBLEMS = 32  # FGG_MAX_PROBLEMS
+
+
+class _Fp4Problem(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("a_scale", ctypes.c_void_p),
+                ("b_scale", ctypes.c_void_p), ("C", ctypes.c_void_p), ("M", ctypes.c_int),
+                ("N", ctypes.c_int), ("K", ctypes.c_int), ("alpha", ctypes.c_float)]
 
 
 class _Options(ctypes.Structure):
@@ -73,6 +82,10 @@ def load_library():
         ("grouped_fp4_gemm_ex", [P, P, P, P, P, F, P, I, I, I, I, OPT, P]),
         ("quantize_fp8_1x128", [P, P, P, I, I, P]),
         ("quantize_nvfp4", [P, P, P, P, I, I, P]),
+        ("grouped_fp4_gemm_alpha", [P, P, P, P, P, P, P, I, I, I, I, P]),
+        ("grouped_fp4_gemm_alpha_ex", [P, P, P, P, P, P, P, I, I, I, I, OPT, P]),
+        ("fp4_gemm_problems", [ctypes.POINTER(_Fp4Problem), I, P]),
+        ("fp4_gemm_problems_ex", [ctypes.POINTER(_Fp4Problem), I, OPT, P]),
         ("grouped_fp8_gemm_tune", [P, P, P, P, P, P, I, I, I, I, I, I, REP, P]),
         ("fp4_gemm_tune", [P, P, P, P, F, P, I, I, I, I, I, REP, P]),
         ("grouped_fp4_gemm_tune", [P, P, P, P, P, F, P, I, I, I, I, I, I, REP, P]),
@@ -271,13 +284,53 @@ def fp4_gemm(A, B, a_scale, b_scale, alpha, out=None, *, tile_id=None, max_workg
 def grouped_fp4_gemm(A, B, a_scale, b_scale, m_indices, alpha, out=None, *, tile_id=None,
                      max_workgroups=0, run_split=0, stream=None):
     """C[M, N] (bfloat16) of the grouped NVFP4 GEMM: B [G, N, K/2], b_scale
-    [G, N, K/16]; m_indices int32 [M] routes rows (-1 = padding)."""
+    [G, N, K/16]; m_indices int32 [M] routes rows (-1 = padding).  alpha is
+    a float (one global scale for every expert) or a float32 device tensor
+    [G] of per-expert factors (C ABI grouped_fp4_gemm_alpha)."""
     torch = _torch()
-    C, dev, args = _fp4_call(A, B, a_scale, b_scale, m_indices, alpha, out)
+    per_expert = isinstance(alpha, torch.Tensor)
+    C, dev, args = _fp4_call(A, B, a_scale, b_scale, m_indices, 1.0 if per_expert else alpha, out)
+    lib = load_library()
     with torch.cuda.device(dev):
-        _check(load_library().grouped_fp4_gemm_ex(*args, _opts(tile_id, max_workgroups, run_split),
-                                                  _stream_ptr(stream, dev)))
+        if per_expert:
+            G = B.shape[0]
+            if alpha.dtype != torch.float32 or tuple(alpha.shape) != (G,):
+                raise ValueError(f"per-expert alpha must be a float32 tensor of shape ({G},)")
+            _dev(alpha, "alpha", dev)
+            a = list(args)
+            a[5] = alpha.data_ptr()
+            _check(lib.grouped_fp4_gemm_alpha_ex(*a, _opts(tile_id, max_workgroups, run_split),
+                                                 _stream_ptr(stream, dev)))
+        else:
+            _check(lib.grouped_fp4_gemm_ex(*args, _opts(tile_id, max_workgroups, run_split),
+                                           _stream_ptr(stream, dev)))
     return C
+
+
+def fp4_gemm_problems(problems, outs=None, *, tile_id=None, max_workgroups=0, stream=None):
+    """A batch of dense NVFP4 GEMMs of different shapes in one launch (C ABI
+    fp4_gemm_problems).  ``problems``: sequence of (A, B, a_scale, b_scale,
+    alpha) as for fp4_gemm; returns the list of C tensors."""
+    torch = _torch()
+    if not 1 <= len(problems) <= MAX_PROBLEMS:
+        raise ValueError(f"need 1 to {MAX_PROBLEMS} problems, got {len(problems)}")
+    arr = (_Fp4Problem * len(problems))()
+    Cs, dev = [], None
+    for g, (A, B, a_scale, b_scale, alpha) in enumerate(problems):
+        C, d, args = _fp4_call(A, B, a_scale, b_scale, None, alpha,
+                               None if outs is None else outs[g])
+        if dev is None:
+            dev = d
+        elif d != dev:
+            raise ValueError("all problems must be on one device")
+        a_ptr, b_ptr, sa_ptr, sb_ptr, al, c_ptr, M, N, K = args
+        arr[g] = _Fp4Problem(a_ptr, b_ptr, sa_ptr, sb_ptr, c_ptr, M, N, K, al)
+        Cs.append(C)
+    with torch.cuda.device(dev):
+        _check(load_library().fp4_gemm_problems_ex(arr, len(problems),
+                                                   _opts(tile_id, max_workgroups),
+                                                   _stream_ptr(stream, dev)))
+    return Cs
 
 
 def fp4_gemm_tune(A, B, a_scale, b_scale, alpha, out=None, *, top_k=4, reps=5, stream=None):

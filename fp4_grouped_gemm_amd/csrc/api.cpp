@@ -173,6 +173,34 @@ int tuned_tile(int kind, int M, int N, int K, int G) {
 
 // Tile for a call: the explicit option, else the recorded tuning result for
 // this shape, else the ranker's top choice.
+// Tile config for a problem batch: the ranker's terms summed over the
+// problems (useful over computed elements, busy fraction of the last wave of
+// tiles, per-CU efficiency of the shape).
+int rank_problems(const fgg::Fp4ProblemSet& set, int num_cus) {
+  int best = 0;
+  double best_score = -1.0;
+  for (int i = 0; i < fgg::fp4_num_tiles(); ++i) {
+    const fgg::TileCfg& t = fgg::fp4_tile(i);
+    double useful = 0.0, computed = 0.0;
+    long long tiles = 0;
+    for (int g = 0; g < set.count; ++g) {
+      const long long tg = (long long)((set.p[g].M + t.block_m - 1) / t.block_m) *
+                           ((set.p[g].N + t.block_n - 1) / t.block_n);
+      tiles += tg;
+      useful += (double)set.p[g].M * set.p[g].N * set.p[g].K;
+      computed += (double)tg * t.block_m * t.block_n * set.p[g].K;
+    }
+    const long long slots = (long long)std::max(1, num_cus) * t.wg_per_cu;
+    const long long waves = (tiles + slots - 1) / slots;
+    const double score = useful / computed * ((double)tiles / (double)(waves * slots)) * t.tput;
+    if (score > best_score) {
+      best_score = score;
+      best = i;
+    }
+  }
+  return best;
+}
+
 fgg_status pick_tile(const char* fn, int kind, int M, int N, int K, int G, int num_cus,
                      const fgg_options* opt, int* tile_id) {
   const int n = kind == FGG_KIND_FP8 ? fgg::fp8_num_tiles() : fgg::fp4_num_tiles();
@@ -335,14 +363,15 @@ fgg_status grouped_fp8_gemm(const void* A, const void* B, const float* a_scale,
 static fgg_status fp4_prepare(const char* fn, const void* A, const void* B, const void* a_scale,
                               const void* b_scale, const int32_t* m_indices, float alpha, void* C,
                               int M, int N, int K, int G, bool grouped, fgg::Fp4Args* a,
-                              const DeviceFacts** d) {
+                              const DeviceFacts** d, const float* alphas = nullptr) {
   fgg_status st = check_common(fn, A, B, a_scale, b_scale, C, M, N, K, G, grouped, m_indices, 16);
   if (st != FGG_OK) return st;
   if (!std::isfinite(alpha)) return fail(FGG_EINVAL, fn, "alpha must be finite");
   if (!(*d = current_device(fn, &st))) return st;
   *a = fgg::Fp4Args{static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B),
                     static_cast<const uint8_t*>(a_scale), static_cast<const uint8_t*>(b_scale),
-                    grouped ? m_indices : nullptr, alpha, static_cast<uint16_t*>(C), M, N, K, G};
+                    grouped ? m_indices : nullptr, alpha, alphas, static_cast<uint16_t*>(C), M, N,
+                    K, G};
   return FGG_OK;
 }
 
@@ -414,6 +443,71 @@ fgg_status grouped_fp4_gemm_tune(const void* A, const void* B, const void* a_sca
                                  fgg_tune_report* report, void* stream) {
   return fp4_tune("grouped_fp4_gemm_tune", A, B, a_scale, b_scale, m_indices, alpha, C, M, N, K, G,
                   true, top_k, reps, report, stream);
+}
+
+fgg_status grouped_fp4_gemm_alpha_ex(const void* A, const void* B, const void* a_scale,
+                                     const void* b_scale, const int32_t* m_indices,
+                                     const float* alpha, void* C, int M, int N, int K, int G,
+                                     const fgg_options* opt, void* stream) {
+  const char* fn = "grouped_fp4_gemm_alpha";
+  if (!alpha) return fail(FGG_EINVAL, fn, "alpha is null");
+  if (!aligned(alpha, 4)) return fail(FGG_EALIGN, fn, "alpha must be 4-byte aligned");
+  fgg::Fp4Args a;
+  const DeviceFacts* d = nullptr;
+  fgg_status st = fp4_prepare(fn, A, B, a_scale, b_scale, m_indices, 1.0f, C, M, N, K, G, true,
+                              &a, &d, alpha);
+  if (st != FGG_OK) return st;
+  int tile;
+  if ((st = pick_tile(fn, FGG_KIND_FP4, M, N, K, G, d->num_cus, opt, &tile)) != FGG_OK) return st;
+  return launched(fn, fgg::launch_fp4(a, tile, launch_opts(opt, d), static_cast<hipStream_t>(stream)));
+}
+
+fgg_status grouped_fp4_gemm_alpha(const void* A, const void* B, const void* a_scale,
+                                  const void* b_scale, const int32_t* m_indices, const float* alpha,
+                                  void* C, int M, int N, int K, int G, void* stream) {
+  return grouped_fp4_gemm_alpha_ex(A, B, a_scale, b_scale, m_indices, alpha, C, M, N, K, G, nullptr,
+                                   stream);
+}
+
+fgg_status fp4_gemm_problems_ex(const fgg_fp4_problem* problems, int count,
+                                const fgg_options* opt, void* stream) {
+  const char* fn = "fp4_gemm_problems";
+  if (!problems) return fail(FGG_EINVAL, fn, "problems is null");
+  if (count < 1 || count > FGG_MAX_PROBLEMS)
+    return fail(FGG_EINVAL, fn, "requires 1 <= count <= %d, got %d", FGG_MAX_PROBLEMS, count);
+  fgg::Fp4ProblemSet set;
+  std::memset(&set, 0, sizeof(set));
+  set.count = count;
+  for (int g = 0; g < count; ++g) {
+    const fgg_fp4_problem& q = problems[g];
+    char where[64];
+    std::snprintf(where, sizeof(where), "%s (problem %d)", fn, g);
+    fgg_status st = check_common(where, q.A, q.B, q.a_scale, q.b_scale, q.C, q.M, q.N, q.K, 1,
+                                 false, nullptr, 16);
+    if (st != FGG_OK) return st;
+    if (!std::isfinite(q.alpha)) return fail(FGG_EINVAL, where, "alpha must be finite");
+    set.p[g] = fgg::Fp4Problem{static_cast<const uint8_t*>(q.A), static_cast<const uint8_t*>(q.B),
+                               static_cast<const uint8_t*>(q.a_scale),
+                               static_cast<const uint8_t*>(q.b_scale), static_cast<uint16_t*>(q.C),
+                               q.M, q.N, q.K, q.alpha};
+  }
+  fgg_status st;
+  const DeviceFacts* d = current_device(fn, &st);
+  if (!d) return st;
+  int tile = -1;
+  if (opt && opt->tile_id >= 0) {
+    if (opt->tile_id >= fgg::fp4_num_tiles())
+      return fail(FGG_EINVAL, fn, "tile_id %d out of range [0, %d)", opt->tile_id, fgg::fp4_num_tiles());
+    tile = opt->tile_id;
+  } else {
+    tile = rank_problems(set, d->num_cus);
+  }
+  return launched(fn, fgg::launch_fp4_problems(set, tile, launch_opts(opt, d),
+                                               static_cast<hipStream_t>(stream)));
+}
+
+fgg_status fp4_gemm_problems(const fgg_fp4_problem* problems, int count, void* stream) {
+  return fp4_gemm_problems_ex(problems, count, nullptr, stream);
 }
 
 int fgg_tuned_tile(int kind, int M, int N, int K, int G) { return tuned_tile(kind, M, N, K, G); }

@@ -33,8 +33,27 @@ struct Fp4Args {
   const uint8_t* b_scale;  // [G, N, K/16] E4M3
   const int32_t* m_indices;  // nullptr = dense
   float alpha;
+  const float* alphas;       // device [G] per-expert alpha, or nullptr (use alpha)
   uint16_t* C;
   int M, N, K, G;
+};
+
+// A batch of dense NVFP4 problems, passed to the kernel by value (kernel
+// arguments: no device allocation, capturable in a graph).
+constexpr int kMaxProblems = 32;
+struct Fp4Problem {
+  const uint8_t* A;        // [M, K/2]
+  const uint8_t* B;        // [N, K/2]
+  const uint8_t* a_scale;  // [M, K/16]
+  const uint8_t* b_scale;  // [N, K/16]
+  uint16_t* C;             // [M, N]
+  int M, N, K;
+  float alpha;
+};
+struct Fp4ProblemSet {
+  Fp4Problem p[kMaxProblems];
+  int tile_start[kMaxProblems + 1];  // filled by the launcher
+  int count;
 };
 
 // Number of compiled configs and their descriptions.
@@ -71,6 +90,8 @@ inline int split_items(int mode, bool grouped, int G, int BM, long long tiles, i
 // Launchers: enqueue on `stream`, return hipSuccess or the launch error.
 hipError_t launch_fp8(const Fp8Args& a, int tile_id, const LaunchOpts& o, hipStream_t s);
 hipError_t launch_fp4(const Fp4Args& a, int tile_id, const LaunchOpts& o, hipStream_t s);
+hipError_t launch_fp4_problems(const Fp4ProblemSet& set, int tile_id, const LaunchOpts& o,
+                               hipStream_t s);
 hipError_t launch_quant_fp8(const uint16_t* X, uint8_t* Q, float* scale, int M, int K,
                             int num_cus, hipStream_t s);
 hipError_t launch_quant_nvfp4(const uint16_t* X, uint8_t* Q, uint8_t* S, float* g, int M, int K,

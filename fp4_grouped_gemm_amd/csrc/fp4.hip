@@ -248,12 +248,50 @@ __device__ __forceinline__ void ksteps8(Pass<T>& ps, uint8_t* lds0, uint8_t* lds
   (kstep<T, Q>(ps, lds0, lds1, ks, nks, tid, lane, wm, wn) && ...);
 }
 
+// Per-thread staging offsets for rows of Kp packed bytes and Ks scale bytes.
+template <class T>
+__device__ __forceinline__ void init_offsets(Pass<T>& ps, int tid, uint32_t Kp, uint32_t Ks) {
+#pragma unroll
+  for (int u = 0; u < T::A_UNITS; ++u) {
+    const int g = tid + u * T::THREADS;
+    ps.a_off[u] = (uint32_t)(g >> 1) * Kp + (uint32_t)(g & 1) * 16u;
+    ps.as_off[u] = (uint32_t)(g >> 1) * Ks;
+  }
+#pragma unroll
+  for (int u = 0; u < T::B_UNITS; ++u) {
+    const int g = tid + u * T::THREADS;
+    ps.b_off[u] = (uint32_t)(g >> 1) * Kp + (uint32_t)(g & 1) * 16u;
+    ps.bs_off[u] = (uint32_t)(g >> 1) * Ks;
+  }
+}
+
+// The K loop of one pass (buffer resources and offsets set, accumulators
+// zeroed): prologue staging of step 0, then eight steps per iteration
+// (register set, LDS stage and scale group positions known at compile
+// time).  The last step also stages (a reload, into the stage nobody reads
+// any more).
+template <class T>
+__device__ __forceinline__ void k_loop(Pass<T>& ps, uint8_t* lds0, uint8_t* lds1, int nks, int tid,
+                                       int lane, int wm, int wn) {
+  ps.load(0, 0);
+  ps.load(1, min(1, nks - 1));
+  ps.load_scales(0, 0);
+  ps.stage_all(0, 0, 0, lds0, tid);
+  lds_barrier();
+  for (int ks = 0; ks < nks; ks += 8)
+    ksteps8<T>(ps, lds0, lds1, ks, nks, tid, lane, wm, wn, std::make_integer_sequence<int, 8>{});
+}
+
+// `alphas` (may be null): one factor per expert, alpha[g] = gA * gB[g],
+// replacing the single `alpha` (a global scale per expert's B, the
+// per-group scaling of the cutlass#3124 page's grouped block-scaled GEMM).
 template <class T>
 __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ a_scale, const uint8_t* __restrict__ b_scale,
-    const int32_t* __restrict__ m_indices, float alpha, uint16_t* __restrict__ C, int M, int N,
-    int K, int G, int num_windows, int num_ntiles, int total_tiles, int group_w, int split) {
+    const int32_t* __restrict__ m_indices, float alpha, const float* __restrict__ alphas,
+    uint16_t* __restrict__ C, int M, int N, int K, int G, int num_windows, int num_ntiles,
+    int total_tiles, int group_w, int split) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[T::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[T::STAGE];
   __shared__ int ids[T::BM];
@@ -270,18 +308,7 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
   const uint32_t Ks = (uint32_t)K >> 4;  // scale bytes per row
 
   Pass<T> ps;
-#pragma unroll
-  for (int u = 0; u < T::A_UNITS; ++u) {
-    const int g = tid + u * T::THREADS;
-    ps.a_off[u] = (uint32_t)(g >> 1) * Kp + (uint32_t)(g & 1) * 16u;
-    ps.as_off[u] = (uint32_t)(g >> 1) * Ks;
-  }
-#pragma unroll
-  for (int u = 0; u < T::B_UNITS; ++u) {
-    const int g = tid + u * T::THREADS;
-    ps.b_off[u] = (uint32_t)(g >> 1) * Kp + (uint32_t)(g & 1) * 16u;
-    ps.bs_off[u] = (uint32_t)(g >> 1) * Ks;
-  }
+  init_offsets(ps, tid, Kp, Ks);
 
   // With split > 1 every pass of a tile is its own work item (the tile
   // order then needs no plan: no item costs more than one pass).
@@ -354,18 +381,9 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) ps.acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-      ps.load(0, 0);
-      ps.load(1, min(1, nks - 1));
-      ps.load_scales(0, 0);
-      ps.stage_all(0, 0, 0, lds0, tid);
-      lds_barrier();
-      // Eight steps per iteration (register set, LDS stage and scale group
-      // positions known at compile time).  The last step also stages (a
-      // reload, into the stage nobody reads any more).
-      for (int ks = 0; ks < nks; ks += 8)
-        ksteps8<T>(ps, lds0, lds1, ks, nks, tid, lane, wm, wn,
-                   std::make_integer_sequence<int, 8>{});
+      k_loop(ps, lds0, lds1, nks, tid, lane, wm, wn);
 
+      const float al = alphas ? alphas[e] : alpha;
 #pragma unroll
       for (int i = 0; i < T::TM; ++i) {
         const int rl = wm * T::WM + i * 16 + (lane & 15);
@@ -377,9 +395,84 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
           const int n = wcol0 + j * 16 + 4 * (lane >> 4);
           if (n < N)
             *reinterpret_cast<uint2*>(crow + n) =
-                pack_bf16x4(alpha * ps.acc[i][j][0], alpha * ps.acc[i][j][1],
-                            alpha * ps.acc[i][j][2], alpha * ps.acc[i][j][3]);
+                pack_bf16x4(al * ps.acc[i][j][0], al * ps.acc[i][j][1], al * ps.acc[i][j][2],
+                            al * ps.acc[i][j][3]);
         }
+      }
+    }
+  }
+}
+
+// A batch of independent dense NVFP4 GEMMs of different shapes in one launch
+// (the cutlass#3124 page's grouped block-scaled GEMM, "Intro": problems with
+// their own M, N and K).  Work item t belongs to the problem whose range
+// [tile_start[g], tile_start[g + 1]) holds it; inside a problem, tiles follow
+// the XCD-aware map_tile order.  Every tile is one pass (no routing) with the
+// problem's own K loop, offsets and alpha; rows and columns past the
+// problem's M and N read zeros and are not stored.
+template <class T>
+__global__ __launch_bounds__(T::THREADS) void fp4_problems_kernel(const Fp4ProblemSet set,
+                                                                  int group_w) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[T::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WAVES_N;
+  const int wn = wave % T::WAVES_N;
+  const int total = set.tile_start[set.count];
+  Pass<T> ps;
+
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    int g = 0;
+    while (g + 1 < set.count && set.tile_start[g + 1] <= tile) ++g;
+    const Fp4Problem& p = set.p[g];
+    const int M = p.M, N = p.N, K = p.K;
+    const int nks = K / T::BK;
+    const uint32_t Kp = (uint32_t)K >> 1, Ks = (uint32_t)K >> 4;
+    const int num_windows = (M + T::BM - 1) / T::BM;
+    const int num_ntiles = (N + T::BN - 1) / T::BN;
+    const int tiles_g = set.tile_start[g + 1] - set.tile_start[g];
+    int window, ntile;
+    map_tile(tile - set.tile_start[g], tiles_g, num_windows, num_ntiles, group_w, window, ntile);
+    const int row0 = window * T::BM;
+    const int col0 = ntile * T::BN;
+    const uint32_t rows_a = (uint32_t)min(T::BM, M - row0);
+    const uint32_t rows_b = (uint32_t)min(T::BN, N - col0);
+
+    __syncthreads();  // the previous tile is done with the stages
+    init_offsets(ps, tid, Kp, Ks);
+#pragma unroll
+    for (int u = 0; u < T::A_UNITS; ++u) {
+      ps.pa_off[u] = ps.a_off[u];
+      ps.pas_off[u] = ps.as_off[u];
+    }
+    ps.ra = rsrc(p.A + (size_t)row0 * Kp, rows_a * Kp);
+    ps.rsa = rsrc(p.a_scale + (size_t)row0 * Ks, rows_a * Ks);
+    ps.rb = rsrc(p.B + (size_t)col0 * Kp, rows_b * Kp);
+    ps.rsb = rsrc(p.b_scale + (size_t)col0 * Ks, rows_b * Ks);
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) ps.acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    k_loop(ps, lds0, lds1, nks, tid, lane, wm, wn);
+
+    const float al = p.alpha;
+    const int wcol0 = col0 + wn * T::WN;
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) {
+      const int gr = row0 + wm * T::WM + i * 16 + (lane & 15);
+      if (gr >= M) continue;
+      uint16_t* crow = p.C + (size_t)gr * N;
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) {
+        const int n = wcol0 + j * 16 + 4 * (lane >> 4);
+        if (n < N)
+          *reinterpret_cast<uint2*>(crow + n) =
+              pack_bf16x4(al * ps.acc[i][j][0], al * ps.acc[i][j][1], al * ps.acc[i][j][2],
+                          al * ps.acc[i][j][3]);
       }
     }
   }
@@ -409,8 +502,31 @@ hipError_t launch_cfg(const Fp4Args& a, const LaunchOpts& o, hipStream_t s) {
   if (o.max_wg > 0 && o.max_wg < grid) grid = o.max_wg;
   const int group_w = 8;  // row windows per XCD tile group
   hipLaunchKernelGGL(fp4_gemm_kernel<T>, dim3(grid), dim3(T::THREADS), 0, s, a.A, a.B, a.a_scale,
-                     a.b_scale, a.m_indices, a.alpha, a.C, a.M, a.N, a.K, a.G, num_windows,
-                     num_ntiles, (int)total, group_w, split);
+                     a.b_scale, a.m_indices, a.alpha, a.alphas, a.C, a.M, a.N, a.K, a.G,
+                     num_windows, num_ntiles, (int)total, group_w, split);
+  return hipGetLastError();
+}
+
+// Tile ranges of a problem batch for tile shape BM x BN.
+inline long long problem_tiles(Fp4ProblemSet& set, int BM, int BN) {
+  long long total = 0;
+  for (int g = 0; g < set.count; ++g) {
+    set.tile_start[g] = (int)total;
+    total += (long long)((set.p[g].M + BM - 1) / BM) * ((set.p[g].N + BN - 1) / BN);
+    if (total > INT_MAX) return -1;
+  }
+  set.tile_start[set.count] = (int)total;
+  return total;
+}
+
+template <class T>
+hipError_t launch_problems_cfg(Fp4ProblemSet set, const LaunchOpts& o, hipStream_t s) {
+  const long long total = problem_tiles(set, T::BM, T::BN);
+  if (total < 0) return hipErrorInvalidValue;
+  if (total == 0) return hipSuccess;
+  int grid = (int)total;
+  if (o.max_wg > 0 && o.max_wg < grid) grid = o.max_wg;
+  hipLaunchKernelGGL(fp4_problems_kernel<T>, dim3(grid), dim3(T::THREADS), 0, s, set, 8);
   return hipGetLastError();
 }
 
@@ -420,6 +536,18 @@ using namespace fp4_detail;
 
 int fp4_num_tiles() { return (int)(sizeof(kFp4Tiles) / sizeof(kFp4Tiles[0])); }
 const TileCfg& fp4_tile(int id) { return kFp4Tiles[id]; }
+
+hipError_t launch_fp4_problems(const Fp4ProblemSet& set, int tile_id, const LaunchOpts& o,
+                               hipStream_t s) {
+  if (set.count < 1 || set.count > kMaxProblems) return hipErrorInvalidValue;
+  switch (tile_id) {
+    case 0: return launch_problems_cfg<Cfg0>(set, o, s);
+    case 1: return launch_problems_cfg<Cfg1>(set, o, s);
+    case 2: return launch_problems_cfg<Cfg2>(set, o, s);
+    case 3: return launch_problems_cfg<Cfg3>(set, o, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_fp4(const Fp4Args& a, int tile_id, const LaunchOpts& o, hipStream_t s) {
   switch (tile_id) {

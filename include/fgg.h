@@ -114,6 +114,45 @@ fgg_status grouped_fp4_gemm(const void* A, const void* B, const void* a_scale,
                             const void* b_scale, const int32_t* m_indices, float alpha,
                             void* C, int M, int N, int K, int G, void* stream);
 
+/*
+ * grouped_fp4_gemm_alpha -- grouped_fp4_gemm with one global scale per
+ * expert: row i of expert g is multiplied by alpha[g] (= gA * gB[g]) instead
+ * of one alpha for all experts (the per-group scaling of the cutlass#3124
+ * page's grouped block-scaled GEMM).  `alpha` is a device array of G finite
+ * floats, 4-byte aligned, read on the device at every launch (graph replay
+ * sees new values); everything else as grouped_fp4_gemm.
+ */
+fgg_status grouped_fp4_gemm_alpha(const void* A, const void* B, const void* a_scale,
+                                  const void* b_scale, const int32_t* m_indices,
+                                  const float* alpha, void* C, int M, int N, int K, int G,
+                                  void* stream);
+
+/*
+ * fp4_gemm_problems -- a batch of independent dense NVFP4 GEMMs whose M, N
+ * and K may all differ, in one launch (the cutlass#3124 page's grouped
+ * block-scaled GEMM, "Intro").  Problem g computes its own
+ *   C_g[i, n] = alpha_g * sum_k (qA sA)(qB sB)
+ * exactly as fp4_gemm does on its operands.  `problems` is a host array of
+ * `count` descriptors (1 <= count <= FGG_MAX_PROBLEMS), read during the call
+ * and passed to the kernel by value: no device allocation, no host
+ * synchronisation, capturable in a HIP graph (the descriptors are captured
+ * with it).  Every problem must meet fp4_gemm's requirements; an error names
+ * the problem's index.  Problems must not write overlapping C.
+ */
+#define FGG_MAX_PROBLEMS 32
+
+typedef struct {
+  const void* A;        /* [M, K/2] packed E2M1                               */
+  const void* B;        /* [N, K/2] packed E2M1                               */
+  const void* a_scale;  /* [M, K/16] E4M3FN                                   */
+  const void* b_scale;  /* [N, K/16] E4M3FN                                   */
+  void* C;              /* [M, N] BF16, written in full                       */
+  int M, N, K;
+  float alpha;          /* product of the two global scales                   */
+} fgg_fp4_problem;
+
+fgg_status fp4_gemm_problems(const fgg_fp4_problem* problems, int count, void* stream);
+
 /* ------------------------------------------------------------------------
  * Activation quantisers: the step before the GEMM, producing its A operand.
  *
@@ -200,6 +239,13 @@ fgg_status grouped_fp4_gemm_ex(const void* A, const void* B, const void* a_scale
                                const void* b_scale, const int32_t* m_indices, float alpha,
                                void* C, int M, int N, int K, int G, const fgg_options* opt,
                                void* stream);
+fgg_status grouped_fp4_gemm_alpha_ex(const void* A, const void* B, const void* a_scale,
+                                     const void* b_scale, const int32_t* m_indices,
+                                     const float* alpha, void* C, int M, int N, int K, int G,
+                                     const fgg_options* opt, void* stream);
+/* run_split is ignored (a batch has no routing). */
+fgg_status fp4_gemm_problems_ex(const fgg_fp4_problem* problems, int count,
+                                const fgg_options* opt, void* stream);
 
 /* ------------------------------------------------------------------------
  * Bounded autotuning of the ranker's top choices (the flashinfer#3948 page,

@@ -105,6 +105,32 @@ def test_tune_validation_and_cache_without_gpu():
     assert fgg.tuned_tile(fgg.FP4, 2048, 36864, 4608) == -1
 
 
+def test_problem_batch_and_expert_alpha_validation():
+    lib = fgg.load_library()
+    arr = (fgg._Fp4Problem * 3)()
+    for g in range(3):
+        arr[g] = fgg._Fp4Problem(P, P, P, P, P, 100, 256, 512, 1.0)
+    assert lib.fp4_gemm_problems(arr, 0, None) == 1
+    assert "count" in lib.fgg_last_error().decode()
+    assert lib.fp4_gemm_problems(arr, fgg.MAX_PROBLEMS + 1, None) == 1
+    arr[1].K = 200
+    st = lib.fp4_gemm_problems(arr, 3, None)
+    msg = lib.fgg_last_error().decode()
+    assert st == 1 and "problem 1" in msg and "K % 128" in msg
+    arr[1].K = 512
+    arr[2].alpha = float("inf")
+    st = lib.fp4_gemm_problems(arr, 3, None)
+    assert st == 1 and "problem 2" in lib.fgg_last_error().decode()
+    arr[2].alpha = 1.0
+    arr[0].C = P + 4
+    assert lib.fp4_gemm_problems(arr, 3, None) == 2
+    st = lib.grouped_fp4_gemm_alpha(P, P, P, P, P, 0, P, 100, 256, 128, 2, None)
+    assert st == 1 and "alpha" in lib.fgg_last_error().decode()
+    assert lib.grouped_fp4_gemm_alpha(P, P, P, P, P, P + 2, P, 100, 256, 128, 2, None) == 2
+    st = lib.grouped_fp4_gemm_alpha(P, P, P, P, P, P, P, 100, 256, 100, 2, None)
+    assert st == 1 and lib.fgg_last_error().decode().startswith("grouped_fp4_gemm_alpha:")
+
+
 def test_python_binding_raises_value_error():
     torch = pytest.importorskip("torch")
     A = torch.zeros((4, 128), dtype=torch.uint8)
