@@ -44,6 +44,10 @@ WORKLOADS = {
     "c5_moe_nvfp4": dict(kind="fp4", desc="grouped NVFP4 W4A4 MoE prefill, G=8x8192 rows, "
                          "N=8192, K=8192"),
     "c1_tiny_fp8": dict(kind="fp8", desc="tiny grouped FP8, G=2, M=256, N=256, K=512"),
+    "p4_problems_nvfp4": dict(kind="fp4_problems",
+                              desc="8 NVFP4 problems of different shapes in one launch: "
+                                   "multinomial(16384) rows, (N, K) alternately (4096, 7168) and "
+                                   "(7168, 2048)"),
     # Latency shapes of the flashinfer#7877 page's timing table: launch-bound,
     # the interesting figure is ms_per_step.
     "p2_unaligned": dict(kind="fp8", desc="small grouped FP8, G=2, M=65, N=128, K=128"),
@@ -283,6 +287,77 @@ def bench_quant(args, torch):
     print(json.dumps(res), flush=True)
 
 
+def bench_problems(args, torch):
+    """A batch of dense NVFP4 problems of different shapes, one
+    fp4_gemm_problems launch per step."""
+    import fp4_grouped_gemm_amd as fgg
+    import oracle
+    from tests.gpu_util import c_to_f64, to_dev
+    from workloads import make
+
+    if not os.path.exists(fgg.library_path()):
+        from fp4_grouped_gemm_amd.build import build
+        build()
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    p = make(args.workload)
+    probs = p["problems"]
+    ds = [to_dev(q) for q in probs]
+    outs = [torch.empty((q["M"], q["N"]), dtype=torch.bfloat16, device="cuda") for q in probs]
+    batch = [(d["A"], d["B"], d["a_scale"], d["b_scale"], q["alpha"]) for d, q in zip(ds, probs)]
+    kw = {} if args.tile is None else {"tile_id": args.tile}
+    for _ in range(args.warmup):
+        fgg.fp4_gemm_problems(batch, outs, **kw)
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        fgg.fp4_gemm_problems(batch, outs, **kw)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    flops = sum(2.0 * q["M"] * q["N"] * q["K"] for q in probs)
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "nvfp4_e2m1",
+        "data": "synthetic (seeded NumPy; quantised on the host, resident in HBM)",
+        "config": {"workload": args.workload, "desc": WORKLOADS[args.workload]["desc"],
+                   "problems": [[q["M"], q["N"], q["K"]] for q in probs],
+                   "tile": args.tile, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK["fp16"],
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK["fp16"], 4), "traffic": None,
+                     "mfma_dtype": "fp16", "frac_of_fp4_peak": round(tflops / PEAK["fp4"], 4)},
+        "kernel_source_sha": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on the first rows of every problem, in turn, until the budget
+        print("[bench] cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
+        from threadpoolctl import threadpool_info
+        t0, fl, ok, nrows = time.perf_counter(), 0.0, True, 0
+        for c0 in range(0, max(q["M"] for q in probs), 128):
+            for q, C in zip(probs, outs):
+                rows = np.arange(c0, min(c0 + 128, q["M"]))
+                if rows.size == 0:
+                    continue
+                r = oracle.fp4_gemm(q["A"], q["B"], q["a_scale"], q["b_scale"], q["alpha"],
+                                    rows=rows)
+                ok &= oracle.check_tolerance(c_to_f64(C)[rows], r)["ok"]
+                fl += 2.0 * rows.size * q["N"] * q["K"]
+                nrows += rows.size
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        out["cpu_baseline"] = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOPS",
+                               "cores": int(threads), "kind": "oracle",
+                               "sample": f"first {nrows} rows over the 8 problems x all columns, "
+                                         f"float64 NumPy/BLAS, {dt:.1f} s"}
+        out["parity_sample"] = {"rows": nrows, "ok": bool(ok)}
+    print(json.dumps(out), flush=True)
+
+
 def tune_report(args, torch):
     """Heuristic top-1 against the best of the ranker's top-k on every GEMM
     workload (the measurement the flashinfer#3948 page reports: the top-1
@@ -297,7 +372,7 @@ def tune_report(args, torch):
     rows, ratios = [], []
     for name, w in WORKLOADS.items():
         if w["kind"] not in ("fp8", "fp4"):
-            continue
+            continue  # the quantisers and the problem batch have no tile choice to tune
         print(f"[bench] tune {name}", file=sys.stderr, flush=True)
         p = make(name)
         d = to_dev(p)
@@ -385,6 +460,10 @@ def main():
 
     if args.tune_report:
         tune_report(args, torch)
+        return
+
+    if WORKLOADS[args.workload]["kind"] == "fp4_problems":
+        bench_problems(args, torch)
         return
 
     if WORKLOADS[args.workload]["kind"].startswith("quant"):

@@ -24,6 +24,7 @@
 // stored as eight 16-byte chunks XOR-swizzled by row.
 #include "common.h"
 
+#include <algorithm>
 #include <climits>
 #include <utility>
 
@@ -537,9 +538,14 @@ using namespace fp4_detail;
 int fp4_num_tiles() { return (int)(sizeof(kFp4Tiles) / sizeof(kFp4Tiles[0])); }
 const TileCfg& fp4_tile(int id) { return kFp4Tiles[id]; }
 
-hipError_t launch_fp4_problems(const Fp4ProblemSet& set, int tile_id, const LaunchOpts& o,
+hipError_t launch_fp4_problems(const Fp4ProblemSet& in, int tile_id, const LaunchOpts& o,
                                hipStream_t s) {
-  if (set.count < 1 || set.count > kMaxProblems) return hipErrorInvalidValue;
+  if (in.count < 1 || in.count > kMaxProblems) return hipErrorInvalidValue;
+  // Longest K loops first (the order of the problems does not change any
+  // result): workgroups that draw the short tiles last even out the finish.
+  Fp4ProblemSet set = in;
+  std::stable_sort(set.p, set.p + set.count,
+                   [](const Fp4Problem& a, const Fp4Problem& b) { return a.K > b.K; });
   switch (tile_id) {
     case 0: return launch_problems_cfg<Cfg0>(set, o, s);
     case 1: return launch_problems_cfg<Cfg1>(set, o, s);

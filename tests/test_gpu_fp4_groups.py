@@ -121,3 +121,18 @@ def test_problem_in_a_batch_equals_fp4_gemm_bitwise():
         for d, q, C in zip(ds, probs, Cs):
             Cd = fgg.fp4_gemm(d["A"], d["B"], d["a_scale"], d["b_scale"], q["alpha"], tile_id=tile)
             assert np.array_equal(c_bits(C), c_bits(Cd)), tile
+
+
+@pytest.mark.slow
+def test_full_size_problem_batch_sampled():
+    """The 8-problem workload the benchmark times: every problem checked on
+    its first, last and a seeded sample of rows."""
+    from workloads import make
+    p = make("p4_problems_nvfp4")
+    probs = p["problems"]
+    log("full-size problem batch")
+    _, Cs = _run_batch(probs)
+    rng = np.random.default_rng(5)
+    for i, (q, C) in enumerate(zip(probs, Cs)):
+        rows = np.unique(np.concatenate([[0, q["M"] - 1], rng.choice(q["M"], 24, replace=False)]))
+        assert_parity(q, C, rows=rows, what=f"problem {i}")

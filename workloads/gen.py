@@ -18,6 +18,11 @@ are the MoE-shaped problems the kernels are measured and checked on:
                        page's "correctness_unaligned_transition" shape)
   p2_m777_g8           FP8, M=777, N=256, K=512, G=8 (that page's
                        "random_s9_m777_g8_n256_k512" shape; seed 9)
+  p4_problems_nvfp4    a batch of 8 dense NVFP4 problems of different
+                       shapes for one launch (the cutlass#3124 page's
+                       grouped GEMM over different M, N, K): expert g has
+                       multinomial(16384, uniform) rows and alternately
+                       (N, K) = (4096, 7168) and (7168, 2048), seed 0
 
 Padding rows (m_indices = -1) hold ordinary random data so that a kernel which
 wrongly computes them is caught.
@@ -141,10 +146,20 @@ def make(name: str, seed: int | None = None) -> dict:
         rng = np.random.default_rng(9 if seed is None else seed)
         counts = rng.multinomial(777, [1 / 8] * 8)
         return fp8_problem(runs_to_indices(counts), 256, 512, 8, rng)
+    if name == "p4_problems_nvfp4":
+        rng = np.random.default_rng(0 if seed is None else seed)
+        counts = rng.multinomial(16384, [1 / 8] * 8)
+        probs = []
+        for g, m in enumerate(counts):
+            N, K = (4096, 7168) if g % 2 == 0 else (7168, 2048)
+            probs.append(nvfp4_problem(None, int(m), N, K, 1, rng))
+        return dict(kind="fp4_problems", problems=probs, G=len(probs))
     raise KeyError(name)
 
 
 def real_rows(problem: dict) -> int:
+    if problem["kind"] == "fp4_problems":
+        return sum(q["M"] for q in problem["problems"])
     idx = problem.get("m_indices")
     if idx is None:
         return problem["M"]
