@@ -43,6 +43,7 @@ from .gemm import (  # noqa: F401
     fp4_gemm,
     grouped_fp4_gemm,
     fp4_gemm_problems,
+    grouped_w4a16_gemm,
     rms_nonpadding,
     check_tolerance,
 )

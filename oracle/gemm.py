@@ -142,6 +142,38 @@ def grouped_fp4_gemm(A, B, a_scale, b_scale, m_indices, alpha, rows=None) -> np.
     return C
 
 
+def grouped_w4a16_gemm(A, B, b_scale, m_indices, b_global, rows=None) -> np.ndarray:
+    """C (float64, [len(rows), N]) of the grouped W4A16 GEMM: 16-bit
+    activations times NVFP4 weights (the onnxruntime#29824 page, "Code
+    analysis 1": FP4 weights with 16-bit activations, dequantised, on the
+    decode / small-M path).  A [M, K] holds BF16 values (as float32 or
+    float64), B [G, N, K/2] packed E2M1 with E4M3 block scales b_scale [G, N,
+    K/16] and one FP32 global scale b_global for all experts:
+      C[i, n] = b_global * sum_k A[i, k] * qB[g, n, k] * sB[g, n, k/16],
+    g = m_indices[i]; rows with g = -1 are zero.  B is dequantised exactly
+    (at most 6 significant bits) and multiplied in float64.
+    Parity: pinned (inputs that are exactly NVFP4 reproduce the W4A4 form;
+    exact rational brute force; padding rows)."""
+    A = np.asarray(A, np.float64)
+    B = np.asarray(B, np.uint8)
+    m_indices = np.asarray(m_indices, np.int32)
+    M, K = A.shape
+    G, N, K2 = B.shape
+    assert 2 * K2 == K and m_indices.shape == (M,)
+    assert np.all((m_indices >= -1) & (m_indices < G)), "expert ids must lie in [-1, G)"
+    rows = _rows_arg(rows, M)
+    ids = m_indices[rows]
+    gb = float(np.float32(b_global))
+    C = np.zeros((rows.size, N), dtype=np.float64)
+    for g in range(G):
+        sel = np.nonzero(ids == g)[0]
+        if sel.size == 0:
+            continue
+        Bd = _nvfp4_dequant(B[g], np.asarray(b_scale)[g])
+        C[sel] = gb * (A[rows[sel]] @ Bd.T)
+    return C
+
+
 def fp4_gemm_problems(problems) -> list:
     """A batch of independent dense NVFP4 GEMMs of different shapes in one
     call (cutlass#3124 page, "Intro": one launch runs several GEMMs whose M,

@@ -181,6 +181,55 @@ def test_nvfp4_problem_batch_slices_tile_one_problem():
     assert np.allclose(c2, exact, rtol=2.0 ** -45, atol=0) and c1.shape == (40, 384)
 
 
+def test_w4a16_reproduces_w4a4_on_nvfp4_representable_activations():
+    """Activations that are exactly NVFP4 values (qA sA gA) through the
+    W4A16 form equal the W4A4 oracle with alpha = gA gB."""
+    rng = np.random.default_rng(24)
+    ids = np.array([1, -1, 0, 2, 2, 0, 1, 1, -1, 2], np.int32)
+    p = nvfp4_problem(ids, 10, 256, 384, 3, rng)
+    qa = _e2m1_values(p["A"])
+    sa = oracle.decode_e4m3fn(p["a_scale"])
+    ga = np.float32(0.375)
+    A16 = (qa.reshape(10, 384 // 16, 16) * sa[:, :, None]).reshape(10, 384) * float(ga)
+    gb = np.float32(p["alpha"])
+    w4a16 = oracle.grouped_w4a16_gemm(A16, p["B"], p["b_scale"], ids, gb)
+    w4a4 = oracle.grouped_fp4_gemm(p["A"], p["B"], p["a_scale"], p["b_scale"], ids,
+                                   np.float32(ga * gb))
+    assert np.allclose(w4a16, w4a4, rtol=1e-12, atol=0)
+    assert np.all(w4a16[ids == -1] == 0.0)
+
+
+def _e2m1_values(packed):
+    q = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), np.uint8)
+    q[..., 0::2], q[..., 1::2] = packed & 0xF, packed >> 4
+    return oracle.decode_e2m1(q)
+
+
+def test_w4a16_equals_exact_rational():
+    """BF16 activations (arbitrary 8-bit significands) against exact
+    Fraction arithmetic, with a non-power-of-two global scale."""
+    rng = np.random.default_rng(25)
+    ids = np.array([0, 1, 1, -1, 0], np.int32)
+    p = nvfp4_problem(ids, 5, 128, 128, 2, rng)
+    A = rng.standard_normal((5, 128)).astype(np.float32)
+    A = (A.view(np.uint32) & 0xFFFF0000).view(np.float32)  # BF16 values
+    gb = np.float32(0.7)
+    C = oracle.grouped_w4a16_gemm(A, p["B"], p["b_scale"], ids, gb)
+    qb = _e2m1_values(p["B"])
+    sb = oracle.decode_e4m3fn(p["b_scale"])
+    for i in range(5):
+        g = int(ids[i])
+        for n in range(0, 128, 7):
+            if g < 0:
+                assert C[i, n] == 0.0
+                continue
+            terms = [Fraction(float(A[i, k])) * Fraction(float(qb[g, n, k]))
+                     * Fraction(float(sb[g, n, k // 16])) * Fraction(float(gb))
+                     for k in range(128)]
+            exact, mag = sum(terms), float(sum(abs(t) for t in terms))
+            assert abs(C[i, n] - float(exact)) <= 2.0 ** -45 * mag + 1e-300
+
+
 # -------------------------------------------------------------- worked examples
 @pytest.mark.parametrize("ex", load_examples(), ids=lambda e: e["name"])
 def test_worked_examples(ex):
