@@ -44,6 +44,9 @@ WORKLOADS = {
     "c5_moe_nvfp4": dict(kind="fp4", desc="grouped NVFP4 W4A4 MoE prefill, G=8x8192 rows, "
                          "N=8192, K=8192"),
     "c1_tiny_fp8": dict(kind="fp8", desc="tiny grouped FP8, G=2, M=256, N=256, K=512"),
+    "d5_decode_w4a16": dict(kind="w4a16",
+                            desc="W4A16 decode on c5's experts: 64 tokens x top-2 of G=8 (128 "
+                                 "rows), BF16 activations x NVFP4 B [8, 8192, 8192]"),
     "p4_problems_nvfp4": dict(kind="fp4_problems",
                               desc="8 NVFP4 problems of different shapes in one launch: "
                                    "multinomial(16384) rows, (N, K) alternately (4096, 7168) and "
@@ -287,6 +290,91 @@ def bench_quant(args, torch):
     print(json.dumps(res), flush=True)
 
 
+def w4a16_bytes(p: dict) -> int:
+    """Bytes a W4A16 launch must move at least once: the weights and scales
+    of every expert that has a row, the activations, the routing, C."""
+    M, N, K = p["M"], p["N"], p["K"]
+    ids = p["m_indices"]
+    used = int(np.unique(ids[(ids >= 0) & (ids < p["G"])]).size)
+    return used * N * (K // 2 + K // 16) + M * K * 2 + M * 4 + M * N * 2
+
+
+def bench_w4a16(args, torch):
+    """Grouped W4A16 decode: HBM-bound on the weights; GB/s and µs."""
+    import fp4_grouped_gemm_amd as fgg
+    import oracle
+    from tests.gpu_util import c_to_f64
+    from workloads import make
+
+    if not os.path.exists(fgg.library_path()):
+        from fp4_grouped_gemm_amd.build import build
+        build()
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    p = make(args.workload)
+    A = torch.from_numpy(p["A_bits"].view(np.int16)).cuda().view(torch.bfloat16)
+    B, sb = torch.from_numpy(p["B"]).cuda(), torch.from_numpy(p["b_scale"]).cuda()
+    ids = torch.from_numpy(p["m_indices"]).cuda()
+    C = torch.empty((p["M"], p["N"]), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        fgg.grouped_w4a16_gemm(A, B, sb, ids, p["b_global"], out=C)
+
+    for _ in range(args.warmup):
+        call()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                call()
+        graph.replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+    else:
+        start.record(stream)
+        for _ in range(args.steps):
+            call()
+        end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    nbytes = w4a16_bytes(p)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "GB/s (algorithmic bytes / time) and % of HBM peak, grouped W4A16 decode",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 x nvfp4_e2m1",
+        "data": "synthetic (seeded NumPy; weights quantised on the host, resident in HBM)",
+        "config": {"workload": args.workload, "desc": WORKLOADS[args.workload]["desc"],
+                   "M": p["M"], "N": p["N"], "K": p["K"], "G": p["G"],
+                   "timing": "hip graph of K launches" if args.graph else "K stream launches",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK, 4), "traffic": None,
+                     "algorithmic_bytes": nbytes, "us_per_call": round(ms * 1e3, 2)},
+        "kernel_source_sha": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+        print("[bench] cpu baseline (oracle, every row)", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        ref = oracle.grouped_w4a16_gemm(p["A"], p["B"], p["b_scale"], p["m_indices"],
+                                        p["b_global"])
+        dt = time.perf_counter() - t0
+        ok = oracle.check_tolerance(c_to_f64(C), ref, p["m_indices"])["ok"]
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        res["cpu_baseline"] = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s",
+                               "cores": int(threads), "kind": "oracle",
+                               "sample": f"the whole workload ({p['M']} rows), float64 "
+                                         f"NumPy/BLAS, {dt:.1f} s"}
+        res["parity_sample"] = {"rows": p["M"], "ok": bool(ok)}
+    print(json.dumps(res), flush=True)
+
+
 def bench_problems(args, torch):
     """A batch of dense NVFP4 problems of different shapes, one
     fp4_gemm_problems launch per step."""
@@ -372,7 +460,7 @@ def tune_report(args, torch):
     rows, ratios = [], []
     for name, w in WORKLOADS.items():
         if w["kind"] not in ("fp8", "fp4"):
-            continue  # the quantisers and the problem batch have no tile choice to tune
+            continue  # the quantisers, W4A16 and the problem batch have no tile choice to tune
         print(f"[bench] tune {name}", file=sys.stderr, flush=True)
         p = make(name)
         d = to_dev(p)
@@ -460,6 +548,10 @@ def main():
 
     if args.tune_report:
         tune_report(args, torch)
+        return
+
+    if WORKLOADS[args.workload]["kind"] == "w4a16":
+        bench_w4a16(args, torch)
         return
 
     if WORKLOADS[args.workload]["kind"] == "fp4_problems":

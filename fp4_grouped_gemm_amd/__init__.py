@@ -19,7 +19,8 @@ import os
 __all__ = [
     "grouped_fp8_gemm", "fp4_gemm", "grouped_fp4_gemm", "quantize_fp8_1x128",
     "quantize_nvfp4", "grouped_fp8_gemm_tune", "fp4_gemm_tune", "grouped_fp4_gemm_tune",
-    "tuned_tile", "tune_clear", "fp4_gemm_problems", "rank_tiles", "num_tiles",
+    "tuned_tile", "tune_clear", "fp4_gemm_problems", "grouped_w4a16_gemm", "rank_tiles",
+    "num_tiles",
     "device_info", "library_path", "load_library", "FP8", "FP4",
 ]
 
@@ -86,6 +87,7 @@ def load_library():
         ("grouped_fp4_gemm_alpha_ex", [P, P, P, P, P, P, P, I, I, I, I, OPT, P]),
         ("fp4_gemm_problems", [ctypes.POINTER(_Fp4Problem), I, P]),
         ("fp4_gemm_problems_ex", [ctypes.POINTER(_Fp4Problem), I, OPT, P]),
+        ("grouped_w4a16_gemm", [P, P, P, P, F, P, I, I, I, I, P]),
         ("grouped_fp8_gemm_tune", [P, P, P, P, P, P, I, I, I, I, I, I, REP, P]),
         ("fp4_gemm_tune", [P, P, P, P, F, P, I, I, I, I, I, REP, P]),
         ("grouped_fp4_gemm_tune", [P, P, P, P, P, F, P, I, I, I, I, I, I, REP, P]),
@@ -304,6 +306,34 @@ def grouped_fp4_gemm(A, B, a_scale, b_scale, m_indices, alpha, out=None, *, tile
         else:
             _check(lib.grouped_fp4_gemm_ex(*args, _opts(tile_id, max_workgroups, run_split),
                                            _stream_ptr(stream, dev)))
+    return C
+
+
+def grouped_w4a16_gemm(A, B, b_scale, m_indices, b_global, out=None, *, stream=None):
+    """C[M, N] (bfloat16) of the grouped W4A16 GEMM (decode path): A [M, K]
+    bfloat16 activations, B [G, N, K/2] packed E2M1, b_scale [G, N, K/16] E4M3
+    bytes, m_indices int32 [M], b_global the FP32 global scale of B."""
+    torch = _torch()
+    if not isinstance(A, torch.Tensor) or A.dtype != torch.bfloat16 or A.dim() != 2:
+        raise ValueError("A must be a 2-D torch.bfloat16 tensor [M, K]")
+    dev = A.device
+    B, sb = _bytes(B, "B"), _bytes(b_scale, "b_scale")
+    M, K = A.shape
+    if B.dim() != 3 or B.shape[2] * 2 != K:
+        raise ValueError(f"B must be [G, N, {K // 2}]")
+    G, N, _ = B.shape
+    if tuple(sb.shape) != (G, N, K // 16):
+        raise ValueError(f"b_scale must be ({G}, {N}, {K // 16})")
+    if m_indices.dtype != torch.int32 or tuple(m_indices.shape) != (M,):
+        raise ValueError(f"m_indices must be int32 of shape ({M},)")
+    for t, n in ((A, "A"), (B, "B"), (sb, "b_scale"), (m_indices, "m_indices")):
+        _dev(t, n, dev)
+    C = _out(out, M, N, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().grouped_w4a16_gemm(A.data_ptr(), B.data_ptr(), sb.data_ptr(),
+                                                 m_indices.data_ptr(), float(b_global),
+                                                 C.data_ptr(), M, N, K, G,
+                                                 _stream_ptr(stream, dev)))
     return C
 
 

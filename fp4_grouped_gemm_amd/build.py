@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfgg.so")
 
-SOURCES = ["api.cpp", "fp8_grouped.hip", "fp4.hip", "quant.hip"]
+SOURCES = ["api.cpp", "fp8_grouped.hip", "fp4.hip", "quant.hip", "w4a16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

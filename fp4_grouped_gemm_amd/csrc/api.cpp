@@ -510,6 +510,22 @@ fgg_status fp4_gemm_problems(const fgg_fp4_problem* problems, int count, void* s
   return fp4_gemm_problems_ex(problems, count, nullptr, stream);
 }
 
+fgg_status grouped_w4a16_gemm(const void* A, const void* B, const void* b_scale,
+                              const int32_t* m_indices, float b_global, void* C, int M, int N,
+                              int K, int G, void* stream) {
+  const char* fn = "grouped_w4a16_gemm";
+  // A stands in for a_scale in the shared checks (16-byte aligned, non-null).
+  fgg_status st = check_common(fn, A, B, A, b_scale, C, M, N, K, G, true, m_indices, 16);
+  if (st != FGG_OK) return st;
+  if (!std::isfinite(b_global)) return fail(FGG_EINVAL, fn, "b_global must be finite");
+  const DeviceFacts* d = current_device(fn, &st);
+  if (!d) return st;
+  const fgg::W4A16Args a{static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(B),
+                         static_cast<const uint8_t*>(b_scale), m_indices, b_global,
+                         static_cast<uint16_t*>(C), M, N, K, G};
+  return launched(fn, fgg::launch_w4a16(a, static_cast<hipStream_t>(stream)));
+}
+
 int fgg_tuned_tile(int kind, int M, int N, int K, int G) { return tuned_tile(kind, M, N, K, G); }
 
 void fgg_tune_clear(void) {

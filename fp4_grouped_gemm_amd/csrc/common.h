@@ -62,6 +62,16 @@ const TileCfg& fp8_tile(int id);
 int fp4_num_tiles();
 const TileCfg& fp4_tile(int id);
 
+struct W4A16Args {
+  const uint16_t* A;         // [M, K] BF16
+  const uint8_t* B;          // [G, N, K/2] packed E2M1
+  const uint8_t* b_scale;    // [G, N, K/16] E4M3
+  const int32_t* m_indices;  // [M]
+  float b_global;            // global scale of B
+  uint16_t* C;               // [M, N] BF16
+  int M, N, K, G;
+};
+
 // Launch choices made on the host.
 struct LaunchOpts {
   int max_wg;     // > 0: cap on the persistent grid
@@ -92,6 +102,7 @@ hipError_t launch_fp8(const Fp8Args& a, int tile_id, const LaunchOpts& o, hipStr
 hipError_t launch_fp4(const Fp4Args& a, int tile_id, const LaunchOpts& o, hipStream_t s);
 hipError_t launch_fp4_problems(const Fp4ProblemSet& set, int tile_id, const LaunchOpts& o,
                                hipStream_t s);
+hipError_t launch_w4a16(const W4A16Args& a, hipStream_t s);
 hipError_t launch_quant_fp8(const uint16_t* X, uint8_t* Q, float* scale, int M, int K,
                             int num_cus, hipStream_t s);
 hipError_t launch_quant_nvfp4(const uint16_t* X, uint8_t* Q, uint8_t* S, float* g, int M, int K,

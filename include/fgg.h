@@ -153,6 +153,29 @@ typedef struct {
 
 fgg_status fp4_gemm_problems(const fgg_fp4_problem* problems, int count, void* stream);
 
+/*
+ * grouped_w4a16_gemm -- grouped GEMM of BF16 activations with NVFP4 weights
+ * (W4A16), BF16 out: the decode / small-M path of the onnxruntime#29824 page
+ * ("Code analysis 1": FP4 weights with 16-bit activations, dequantised).
+ *
+ *   A        [M, K]        BF16 activations (row i routed by m_indices[i])
+ *   B        [G, N, K/2]   packed E2M1;   b_scale [G, N, K/16] E4M3FN bytes
+ *   m_indices[M]           int32 expert id or -1 (as for grouped_fp8_gemm)
+ *   b_global               FP32 global scale of B (one for all experts)
+ *   C        [M, N]        BF16, written in full; -1 rows are zero
+ *
+ *   C[i, n] = b_global * sum_k A[i, k] * qB[g, n, k] * sB[g, n, k / 16]
+ *
+ * Weights are dequantised exactly (E2M1 x E4M3 has at most 6 significant
+ * bits) and multiplied with FP32 accumulation.  Built for few rows per expert
+ * (decode): each expert's weights are read once per 16 of its rows, and an
+ * expert with no rows costs no weight traffic.  Requirements as
+ * grouped_fp4_gemm (A 16-byte aligned); b_global finite.
+ */
+fgg_status grouped_w4a16_gemm(const void* A, const void* B, const void* b_scale,
+                              const int32_t* m_indices, float b_global, void* C, int M, int N,
+                              int K, int G, void* stream);
+
 /* ------------------------------------------------------------------------
  * Activation quantisers: the step before the GEMM, producing its A operand.
  *

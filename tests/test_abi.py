@@ -131,6 +131,17 @@ def test_problem_batch_and_expert_alpha_validation():
     assert st == 1 and lib.fgg_last_error().decode().startswith("grouped_fp4_gemm_alpha:")
 
 
+def test_w4a16_validation():
+    lib = fgg.load_library()
+    st = lib.grouped_w4a16_gemm(P, P, P, P, 1.0, P, 16, 256, 200, 2, None)
+    msg = lib.fgg_last_error().decode()
+    assert st == 1 and msg.startswith("grouped_w4a16_gemm:") and "K % 128" in msg
+    assert lib.grouped_w4a16_gemm(P, P, P, 0, 1.0, P, 16, 256, 256, 2, None) == 1
+    assert lib.grouped_w4a16_gemm(P + 8, P, P, P, 1.0, P, 16, 256, 256, 2, None) == 2
+    st = lib.grouped_w4a16_gemm(P, P, P, P, float("nan"), P, 16, 256, 256, 2, None)
+    assert st == 1 and "b_global" in lib.fgg_last_error().decode()
+
+
 def test_python_binding_raises_value_error():
     torch = pytest.importorskip("torch")
     A = torch.zeros((4, 128), dtype=torch.uint8)

@@ -20,5 +20,7 @@ from .gen import (  # noqa: F401
     make,
     fp8_problem,
     nvfp4_problem,
+    w4a16_problem,
+    decode_routing,
     runs_to_indices,
 )

@@ -18,6 +18,9 @@ are the MoE-shaped problems the kernels are measured and checked on:
                        page's "correctness_unaligned_transition" shape)
   p2_m777_g8           FP8, M=777, N=256, K=512, G=8 (that page's
                        "random_s9_m777_g8_n256_k512" shape; seed 9)
+  d5_decode_w4a16      W4A16 decode on c5's experts: 64 tokens x top-2 of
+                       G=8 (128 rows, unsorted), BF16 activations, NVFP4
+                       B [8, 8192, 8192], seed 0
   p4_problems_nvfp4    a batch of 8 dense NVFP4 problems of different
                        shapes for one launch (the cutlass#3124 page's
                        grouped GEMM over different M, N, K): expert g has
@@ -104,6 +107,34 @@ def nvfp4_problem(m_indices, M: int, N: int, K: int, G: int, rng) -> dict:
     return d
 
 
+def w4a16_problem(m_indices, N: int, K: int, G: int, rng) -> dict:
+    """BF16 activations (N(0,1) rounded to nearest even) routed by
+    m_indices, and NVFP4 weights B [G, N, K/2] with one global scale."""
+    m_indices = np.ascontiguousarray(m_indices, dtype=np.int32)
+    M = m_indices.size
+    X = _draw(rng, "normal", (M, K))
+    u = X.view(np.uint32)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)  # RNE to BF16
+    A = (bits.astype(np.uint32) << 16).view(np.float32)
+    Bf = np.empty((G, N, K), np.float32)
+    for g in range(G):
+        Bf[g] = _draw(rng, "normal", (N, K))
+    gB = nvfp4_global_scale(float(np.abs(Bf).max()))
+    B, b_sc, _ = quantize_nvfp4(Bf.reshape(G * N, K), gB)
+    del Bf
+    return dict(kind="w4a16", A=A, A_bits=bits, B=B.reshape(G, N, K // 2),
+                b_scale=b_sc.reshape(G, N, K // 16), b_global=np.float32(gB),
+                m_indices=m_indices, M=M, N=N, K=K, G=G)
+
+
+def decode_routing(tokens: int, top_k: int, G: int, rng) -> np.ndarray:
+    """MoE decode routing: each token picks top_k distinct experts uniformly;
+    row t * top_k + j of the expanded batch goes to token t's j-th expert
+    (unsorted, as the router emits them)."""
+    return np.stack([rng.choice(G, top_k, replace=False) for _ in range(tokens)]).reshape(-1) \
+        .astype(np.int32)
+
+
 def _zipf_counts(rng, G=32, total_rows=16384, start_T=14336, s=1.2, pad_to=128):
     p = (np.arange(1, G + 1, dtype=np.float64)) ** (-s)
     p /= p.sum()
@@ -146,6 +177,10 @@ def make(name: str, seed: int | None = None) -> dict:
         rng = np.random.default_rng(9 if seed is None else seed)
         counts = rng.multinomial(777, [1 / 8] * 8)
         return fp8_problem(runs_to_indices(counts), 256, 512, 8, rng)
+    if name == "d5_decode_w4a16":
+        rng = np.random.default_rng(0 if seed is None else seed)
+        idx = decode_routing(64, 2, 8, rng)
+        return w4a16_problem(idx, 8192, 8192, 8, rng)
     if name == "p4_problems_nvfp4":
         rng = np.random.default_rng(0 if seed is None else seed)
         counts = rng.multinomial(16384, [1 / 8] * 8)
