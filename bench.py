@@ -506,6 +506,8 @@ def main():
                          "configs (the library's *_tune calls), report heuristic top-1 against "
                          "the best of the k, and the geomean loss; one JSON line")
     ap.add_argument("--top-k", type=int, default=4)
+    ap.add_argument("--max-workgroups", type=int, default=0,
+                    help="fgg_options.max_workgroups (0: one workgroup per tile)")
     ap.add_argument("--run-split", type=int, default=0,
                     help="fgg_options.run_split (0 automatic, -1 never, 1 always)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -582,6 +584,8 @@ def main():
     kw = {} if args.tile is None else {"tile_id": args.tile}
     if args.run_split and p.get("m_indices") is not None:
         kw["run_split"] = args.run_split
+    if args.max_workgroups:
+        kw["max_workgroups"] = args.max_workgroups
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         run(p, d, out=C, **kw)
@@ -622,7 +626,8 @@ def main():
         "config": {"workload": args.workload, "desc": WORKLOADS[args.workload]["desc"],
                    "M": M, "N": N, "K": K, "G": G, "real_rows": rr,
                    "tile": args.tile if args.tile is not None else tiles[0]["id"],
-                   "run_split": args.run_split, "timing": "hip graph of K launches" if args.graph
+                   "run_split": args.run_split, "max_workgroups": args.max_workgroups,
+                   "timing": "hip graph of K launches" if args.graph
                    else "K stream launches", "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK[mma],
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK[mma], 4),

@@ -518,6 +518,8 @@ fgg_status grouped_w4a16_gemm(const void* A, const void* B, const void* b_scale,
   fgg_status st = check_common(fn, A, B, A, b_scale, C, M, N, K, G, true, m_indices, 16);
   if (st != FGG_OK) return st;
   if (!std::isfinite(b_global)) return fail(FGG_EINVAL, fn, "b_global must be finite");
+  if ((long long)M * K * 2 > 0x7FFFFFFFLL)
+    return fail(FGG_EINVAL, fn, "requires M * K * 2 < 2^31 bytes of activations (decode path), got M=%d K=%d", M, K);
   const DeviceFacts* d = current_device(fn, &st);
   if (!d) return st;
   const fgg::W4A16Args a{static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(B),

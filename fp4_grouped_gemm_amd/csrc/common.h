@@ -225,6 +225,62 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
   return r;
 }
 
+// ------------------------------------------------- direct-to-LDS staging
+// Shared by the kernels that stage tiles with buffer loads straight into
+// LDS and order them with explicit waits and barriers.
+namespace lds_dma {
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Wait until at most N of this wave's vector-memory operations (including
+// the loads into LDS) are outstanding; they complete in issue order, so a
+// following barrier publishes the data of every earlier load.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier after this wave's LDS reads have completed.  Unlike
+// __syncthreads() it does not also wait for every global load in flight
+// (the look-ahead stages must stay in flight across it).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// A buffer offset past every buffer's end (buffers are below 2^31 bytes):
+// a load there returns zeros without touching memory.
+constexpr uint32_t kSkip = 0x80000000u;
+
+// Raw buffer resource over [base, base + bytes), as its four descriptor
+// words (base address, stride 0, size, raw-access flags): loads at offsets
+// past the end return zeros, the out-of-range fill the tail tiles rely on.
+__device__ __forceinline__ i32x4 rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return (i32x4){(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr)(const_cast<void*>(p));
+}
+
+// Direct global->LDS loads of 16 (or 4) bytes per lane at buffer offset
+// voff + soff; lane l's bytes land at LDS address lds + 16 l (or 4 l).
+// Inline assembly, so that the compiler does not track these LDS writes and
+// add waits of its own for them: the pipeline orders them with its explicit
+// vmcnt waits and barriers.
+__device__ __forceinline__ void dma16(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds),
+               "v"(voff), "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(lds), "v"(voff),
+               "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
+
+}  // namespace lds_dma
+
 // Wave-wide minimum (64 lanes).
 __device__ __forceinline__ int wave_min(int v) {
 #pragma unroll

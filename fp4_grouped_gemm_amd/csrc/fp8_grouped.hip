@@ -72,8 +72,6 @@ struct Fp8Cfg {
   static_assert(WM == 64 && BM <= 512, "one row per lane in the pass masks");
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
 // LDS byte offset of 16-byte chunk `c` (0..7) of tile row `r`.  The chunk
 // is XOR-swizzled with bits 1..3 of the row, so the 16 rows that one
 // fragment read touches (128-byte rows, two per 256-byte bank line) land on
@@ -92,52 +90,7 @@ __device__ __forceinline__ i32x8 read_frag(const uint8_t* tile, int row0, int la
   return (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Wait until at most N of this wave's vector-memory operations (including
-// the loads into LDS) are outstanding; they complete in issue order, so a
-// following barrier publishes the data of every earlier load.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Workgroup barrier after this wave's LDS reads have completed.  Unlike
-// __syncthreads() it does not also wait for every global load in flight
-// (the look-ahead stages must stay in flight across it).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// A buffer offset past every buffer's end (buffers are below 2^31 bytes):
-// a load there returns zeros without touching memory.
-constexpr uint32_t kSkip = 0x80000000u;
-
-// Raw buffer resource over [base, base + bytes), as its four descriptor
-// words (base address, stride 0, size, raw-access flags): loads at offsets
-// past the end return zeros, the out-of-range fill the tail tiles rely on.
-__device__ __forceinline__ i32x4 rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)base;
-  return (i32x4){(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(lds_ptr)(const_cast<void*>(p));
-}
-
-// Direct global->LDS loads of 16 (or 4) bytes per lane at buffer offset
-// voff + soff; lane l's bytes land at LDS address lds + 16 l (or 4 l).
-// Inline assembly, so that the compiler does not track these LDS writes and
-// add waits of its own for them: the pipeline orders them with its explicit
-// vmcnt waits and barriers.
-__device__ __forceinline__ void dma16(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds),
-               "v"(voff), "s"(rs), "s"(soff)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(lds), "v"(voff),
-               "s"(rs), "s"(soff)
-               : "memory", "m0");
-}
+using namespace lds_dma;
 
 // Per-pass state: buffer resources, offsets, next scales, accumulators.
 //  * A/B staging: a tile row is K bytes for both operands; lane l of a

@@ -8,73 +8,74 @@
 //
 // Design: with a few rows per expert the weights dominate the traffic (each
 // weight byte is used by those few rows only), so the kernel streams B once
-// from HBM at full width and keeps everything else on the side.
-//  * One workgroup per (expert, 128-column block).  A workgroup first compacts the rows
-//    routed to its expert into LDS (one wave, ballot + popcount, in row
-//    order); a workgroup whose expert has no rows ends there and never reads
-//    that expert's weights.  Rows are processed 32 at a time (two MFMA row
-//    blocks sharing each dequantised weight fragment), each chunk streaming
-//    the 64 columns' weights again.
-//  * The four waves split K (128-wide groups, round robin).  Per group a lane
-//    loads, for each of the 8 column blocks, 16 packed bytes (32 weights of
-//    one column) and their two E4M3 scale codes, and 64 bytes of each of its
-//    two activation rows (from L2: every workgroup of the expert reads the same
-//    rows).  The next group's loads are in flight during this group's
-//    dequantisation and MFMAs.
+// from HBM with many loads in flight and keeps the dequantisation VALU work
+// of one wave overlapped with the load waits of the others.
+//  * One workgroup (4 waves) per (expert, 128-column block); wave w owns
+//    columns 32 w .. 32 w + 31 (two MFMA column blocks) over all of K, so
+//    no partial sums cross waves.  Wave 0 first compacts the rows routed to
+//    the expert into LDS (ballot + popcount, in row order; expert 0's
+//    workgroups also zero the padding rows found); a workgroup whose expert
+//    has no rows stops there and never reads that expert's weights.
+//  * Rows run 32 at a time (two MFMA row blocks sharing each dequantised
+//    weight fragment).  Their activations, 32 rows x 128 K per group, go
+//    through a 4-stage LDS ring with direct-to-LDS loads (no registers),
+//    shared by the four waves; 16-byte chunks are XOR-swizzled by row so a
+//    fragment read hits 16 distinct chunk positions.
+//  * Weights stream through a 4-slot register ring, 3 groups ahead: per
+//    group a lane loads 16 packed bytes (32 weights of one column) and their
+//    two E4M3 scale codes per column block.  Every group issues the same
+//    loads (past the last group they reload it and add exact zeros through
+//    a zero scale), so one explicit count waits for the oldest group.
 //  * Weights are dequantised exactly to BF16 in registers (q * s has at most
 //    6 significant bits and lies in [2^-10, 2688]): the E2M1 pair convert with
 //    scale 1.0, an FP32 multiply by the block scale, a pack to BF16.  Then
 //    v_mfma_f32_16x16x32_bf16 with FP32 accumulation: lane (r, q) of the
 //    activation operand and lane (c, q) of the weight operand hold the same
 //    eight k, so every k pairs with itself.
-//  * The four waves' partial sums meet in LDS and are added in wave order
-//    (deterministic), times gB, rounded to BF16 and stored for the chunk's
-//    rows.  The workgroups of expert 0 also write the zero rows (found in
-//    the same scan).
 #include "common.h"
 
 #include <climits>
+#include <utility>
 
 namespace fgg {
 namespace w4a16_detail {
 
+using namespace lds_dma;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kCols = 128;      // columns per workgroup: 8 MFMA column blocks
-constexpr int kBlocks = kCols / 16;
+constexpr int kCB = 2;                 // MFMA column blocks per wave
+constexpr int kCols = 16 * kCB * kWaves;  // columns per workgroup
+constexpr int kRB = 2;                 // MFMA row blocks per chunk
+constexpr int kRows = 16 * kRB;        // rows per chunk
+constexpr int kGroup = 128;            // K per group: 4 MFMAs of K = 32
+constexpr int kScan = 1024;            // m_indices entries compacted per scan
+constexpr int kAStages = 4;            // LDS ring of activation groups
+constexpr int kBSlots = 4;             // register ring of weight groups
+constexpr int kAhead = kBSlots - 1;    // weight groups issued ahead
+constexpr int kAStage = kRows * kGroup * 2;         // bytes per activation stage
+constexpr int kADma = kAStage / 16 / kThreads;      // 16-byte loads per thread
 static_assert(kCols == 2 * 64, "a zero row is one 4-byte store per lane");
-constexpr int kRB = 2;          // MFMA row blocks per chunk
-constexpr int kRows = 16 * kRB; // rows per chunk
-constexpr int kGroup = 128;     // K per group: 4 MFMAs of K = 32
-constexpr int kScan = 1024;     // m_indices entries compacted per scan
+static_assert(kBSlots % kAStages == 0, "an unrolled block of kBSlots groups starts at stage 0");
+static_assert(kADma * 16 * kThreads == kAStage, "activation staging split");
+// Loads per group per wave: activation DMAs, then per column block the
+// weight bytes and the scale codes.
+constexpr int kLoadsPerGroup = kADma + 2 * kCB;
+// Step i issues the activations of group i + kAStages - 1, then the weights
+// of group i + kAhead.  So group i's weights go out kLead steps before its
+// activations (or right after them, kLead = 0), and when step i waits, the
+// later of the two is followed by the weights of its own step (kLead > 0)
+// and by the kAStages - 2 steps in between.
+constexpr int kLead = kAhead - kAStages + 1;
+static_assert(kLead >= 0, "weights must not trail their activations");
+constexpr int kWaitAfter = (kLead > 0 ? 2 * kCB : 0) + (kAStages - 2) * kLoadsPerGroup;
 
-// One group's operands in registers.
-struct Group {
-  i32x4 a[kRB][4];           // activation rows of this lane: 32 BF16 at k0 + 32 q
-  i32x4 b[kBlocks];          // packed weights: 32 E2M1 of column c at k0 + 32 q
-  uint32_t s[kBlocks];       // two E4M3 scale codes of those 32 weights
+struct Weights {
+  i32x4 b[kCB];      // 32 E2M1 codes of column c at k0 + 32 q
+  uint32_t s[kCB];   // their two E4M3 scale codes
 };
 
-__device__ __forceinline__ void load_group(Group& gr, const uint16_t* const arow[kRB],
-                                           const uint8_t* bcol, const uint8_t* scol, int k0, int q,
-                                           uint32_t Kp, uint32_t Ks) {
-#pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const i32x4* ap = reinterpret_cast<const i32x4*>(arow[rb] + k0 + 32 * q);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) gr.a[rb][u] = ap[u];
-  }
-#pragma unroll
-  for (int b = 0; b < kBlocks; ++b) {
-    gr.b[b] = *reinterpret_cast<const i32x4*>(bcol + (size_t)b * 16 * Kp + (k0 + 32 * q) / 2);
-    gr.s[b] = *reinterpret_cast<const uint16_t*>(scol + (size_t)b * 16 * Ks + (k0 + 32 * q) / 16);
-  }
-}
-
-// Eight E2M1 codes (one 32-bit word, low nibble first) times the block
-// scale s -> eight BF16 values.  Exact: at most 6 significant bits.
 template <int H>
 __device__ __forceinline__ void dequant2(uint32_t word, float s, bf16x8& r) {
   const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, H);  // byte H
@@ -83,6 +84,8 @@ __device__ __forceinline__ void dequant2(uint32_t word, float s, bf16x8& r) {
   r[2 * H + 1] = p[1];
 }
 
+// Eight E2M1 codes (one 32-bit word, low nibble first) times the block
+// scale s -> eight BF16 values.  Exact: at most 6 significant bits.
 __device__ __forceinline__ bf16x8 dequant8(uint32_t word, float s) {
   bf16x8 r;
   dequant2<0>(word, s, r);
@@ -92,38 +95,106 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t word, float s) {
   return r;
 }
 
-__device__ __forceinline__ float e4m3_value(uint32_t code) {
-  return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+// LDS byte offset of 16-byte chunk c (0..15) of activation row r (0..31).
+__device__ __forceinline__ int a_swz(int r, int c) { return r * (kGroup * 2) + ((c ^ (r & 15)) << 4); }
+
+struct Ctx {
+  const uint8_t* bcol[kCB];   // weight row of this lane's column, per column block
+  const uint8_t* scol[kCB];   // its scale codes
+  i32x4 ra;                   // activation buffer resource (whole A)
+  uint32_t a_off[kADma];      // this lane's activation chunks: row offset + chunk
+  uint32_t lds_a[kADma];      // their LDS destinations (stage 0)
+  int ngroups;
+  int q;
+};
+
+// Issue group g's activation chunks into LDS stage g % kAStages (group index
+// clamped to the last one past the end).
+__device__ __forceinline__ void load_a(const Ctx& c, uint8_t* ring, int g) {
+  const int gc = min(g, c.ngroups - 1);
+  const uint32_t st = (uint32_t)((g % kAStages) * kAStage);
+#pragma unroll
+  for (int u = 0; u < kADma; ++u) dma16(c.ra, c.lds_a[u] + st, c.a_off[u], gc * kGroup * 2);
+  (void)ring;
 }
 
-__device__ __forceinline__ void mma_group(const Group& gr, f32x4 acc[kRB][kBlocks], bool valid) {
-  // MFMA j takes k0 + 32 q + 8 j .. + 8: 16-byte chunk j of the lane's 64
-  // activation bytes and 32-bit word j of its 16 weight bytes; each
-  // dequantised weight fragment serves every row block.
+__device__ __forceinline__ void load_b(const Ctx& c, Weights& w, int g) {
+  const int k0 = min(g, c.ngroups - 1) * kGroup;
 #pragma unroll
-  for (int b = 0; b < kBlocks; ++b) {
-    const uint32_t sc = valid ? gr.s[b] : 0u;  // code 0 = scale 0
-    const float s0 = e4m3_value(sc & 0xFFu), s1 = e4m3_value((sc >> 8) & 0xFFu);
+  for (int b = 0; b < kCB; ++b) {
+    w.b[b] = *reinterpret_cast<const i32x4*>(c.bcol[b] + (k0 + 32 * c.q) / 2);
+    w.s[b] = *reinterpret_cast<const uint16_t*>(c.scol[b] + (k0 + 32 * c.q) / 16);
+  }
+}
+
+// MFMAs of one group: activations from LDS stage `a`, weights from `w`;
+// RB row blocks (the second is skipped when the chunk has at most 16 rows).
+// Each activation fragment is read once per k slice and serves both column
+// blocks.
+template <int RB>
+__device__ __forceinline__ void mma_group(const uint8_t* a, const Weights& w, bool valid, int lane,
+                                          f32x4 acc[kRB][kCB]) {
+  const int r = lane & 15, q = lane >> 4;
+  float s0[kCB], s1[kCB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8 bf = dequant8((uint32_t)gr.b[b][j], j < 2 ? s0 : s1);
+  for (int b = 0; b < kCB; ++b) {
+    const uint32_t sc = valid ? w.s[b] : 0u;  // code 0 = scale 0: adds exact zeros
+    s0[b] = __builtin_amdgcn_cvt_f32_fp8((int)(sc & 0xFFu), 0);
+    s1[b] = __builtin_amdgcn_cvt_f32_fp8((int)((sc >> 8) & 0xFFu), 0);
+  }
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb)
-        acc[rb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            bf, __builtin_bit_cast(bf16x8, gr.a[rb][j]), acc[rb][b], 0, 0, 0);
+  for (int j = 0; j < 4; ++j) {
+    // k0 + 32 q + 8 j .. + 8: chunk 4 q + j of the lane's activation rows and
+    // word j of its 16 weight bytes
+    bf16x8 af[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      af[rb] = *reinterpret_cast<const bf16x8*>(a + a_swz(16 * rb + r, 4 * q + j));
+#pragma unroll
+    for (int b = 0; b < kCB; ++b) {
+      const bf16x8 bf = dequant8((uint32_t)w.b[b][j], j < 2 ? s0[b] : s1[b]);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        acc[rb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, af[rb], acc[rb][b], 0, 0, 0);
     }
   }
 }
 
-__global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restrict__ A,
+// One group i = g0 + I of the ring: wait until group i's activations and
+// weights have landed, publish the stage, refill the rings (activations of
+// group i + kAStages - 1 into the stage group i - 1 used, weights of group
+// i + kAhead into the slot group i - 1 used), then compute group i.
+template <int RB, int I>
+__device__ __forceinline__ void group_step(const Ctx& c, uint8_t* ring, Weights (&w)[kBSlots],
+                                           int g0, int lane, f32x4 acc[kRB][kCB]) {
+  const int i = g0 + I;
+  wait_vmem<kWaitAfter>();
+  lds_barrier();
+  load_a(c, ring, i + kAStages - 1);
+  load_b(c, w[(I + kAhead) % kBSlots], i + kAhead);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_group<RB>(ring + (I % kAStages) * kAStage, w[I % kBSlots], i < c.ngroups, lane, acc);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int RB, int... I>
+__device__ __forceinline__ void group_steps(const Ctx& c, uint8_t* ring, Weights (&w)[kBSlots],
+                                            int g0, int lane, f32x4 acc[kRB][kCB],
+                                            std::integer_sequence<int, I...>) {
+  (group_step<RB, I>(c, ring, w, g0, lane, acc), ...);
+}
+
+// Two waves per SIMD at least (one wave's dequantisation overlaps another's
+// load waits): at most 256 registers per lane.
+__global__ __launch_bounds__(kThreads, 2) void w4a16_kernel(const uint16_t* __restrict__ A,
                                                          const uint8_t* __restrict__ B,
                                                          const uint8_t* __restrict__ b_scale,
                                                          const int32_t* __restrict__ m_indices,
                                                          float gb, uint16_t* __restrict__ C,
                                                          int M, int N, int K, int G) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kAStages * kAStage];
   __shared__ int rows[kScan];
   __shared__ int nrows;
-  __shared__ f32x4 red[kWaves][kRB][kBlocks][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -132,17 +203,21 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restr
   const int n0 = (blockIdx.x % nblk) * kCols;
   const int g = blockIdx.x / nblk;
   const uint32_t Kp = (uint32_t)K / 2, Ks = (uint32_t)K / 16;
-  const int r = lane & 15, q = lane >> 4;
 
-  // Weights of this workgroup: column n0 + 16 b + (lane % 16), from byte
-  // (k0 + 32 q) / 2 of its row.
-  const uint8_t* bcol = B + ((size_t)g * N + n0 + r) * Kp;
-  const uint8_t* scol = b_scale + ((size_t)g * N + n0 + r) * Ks;
-  const int ngroups = K / kGroup;
+  Ctx c;
+  c.q = lane >> 4;
+  c.ngroups = K / kGroup;
+  c.ra = rsrc(A, (uint32_t)((size_t)M * K * 2));
+#pragma unroll
+  for (int b = 0; b < kCB; ++b) {
+    const size_t col = (size_t)g * N + n0 + 32 * wave + 16 * b + (lane & 15);
+    c.bcol[b] = B + col * Kp;
+    c.scol[b] = b_scale + col * Ks;
+  }
 
   for (int scan0 = 0; scan0 < M; scan0 += kScan) {
     // Compact the rows of this expert among m_indices[scan0, scan0 + kScan).
-    __syncthreads();  // the previous chunks are done with rows[]
+    __syncthreads();  // the previous chunks are done with rows[] and the ring
     if (wave == 0) {
       int count = 0;
       const int end = min(M, scan0 + kScan);
@@ -168,62 +243,55 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restr
     const int count = nrows;
 
     for (int c0 = 0; c0 < count; c0 += kRows) {
-      // Rows of this lane in the activation operands (row block rb: chunk
-      // row 16 rb + l % 16); rows past the chunk read a valid row and are
-      // never stored.
-      const uint16_t* arow[kRB];
+      // This thread's activation chunks: LDS chunk p = u * 256 + tid of a
+      // stage is row p / 16, physical chunk p % 16, which holds logical
+      // chunk (p % 16) ^ (row % 16); rows past the chunk read a valid row
+      // and are never stored.
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) arow[rb] = A + (size_t)rows[min(c0 + 16 * rb + r, count - 1)] * K;
-      f32x4 acc[kRB][kBlocks];
+      for (int u = 0; u < kADma; ++u) {
+        const int p = u * kThreads + tid;
+        const int row = p >> 4, lc = (p & 15) ^ (row & 15);
+        c.a_off[u] = (uint32_t)rows[min(c0 + row, count - 1)] * (uint32_t)K * 2u + (uint32_t)lc * 16u;
+        c.lds_a[u] = lds_addr(ring) + (uint32_t)(u * kThreads + wave * 64) * 16u;
+      }
+      f32x4 acc[kRB][kCB];
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-        for (int b = 0; b < kBlocks; ++b) acc[rb][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < kCB; ++b) acc[rb][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-      // This wave's groups wave, wave + 4, ...: two register sets used in
-      // turn, the next group's loads issued before this group's MFMAs.
-      // Loads are unconditional (a group index past the end is clamped to
-      // the last group and its data unused), so the waits count a fixed
-      // number of loads; the fences keep each batch of loads ahead of the
-      // MFMAs it overlaps.
-      // Groups are taken in pairs with no early exit (an exit between a
-      // load and its use lets the compiler sink the load past it): the
-      // second group of the last pair may lie past the end, and then its
-      // block scales are taken as 0, so it adds exact zeros (A is finite).
-      Group g0, g1;
-      const int last = ngroups - 1;
-      load_group(g0, arow, bcol, scol, min(wave, last) * kGroup, q, Kp, Ks);
-      for (int kg = wave; kg < ngroups; kg += 2 * kWaves) {
-        load_group(g1, arow, bcol, scol, min(kg + kWaves, last) * kGroup, q, Kp, Ks);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_group(g0, acc, true);
-        load_group(g0, arow, bcol, scol, min(kg + 2 * kWaves, last) * kGroup, q, Kp, Ks);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_group(g1, acc, kg + kWaves < ngroups);
+      // Prologue in the steady-state order: the weights of the first kLead
+      // groups, then (activations j, weights j + kLead).
+      Weights w[kBSlots];
+#pragma unroll
+      for (int j = 0; j < kLead; ++j) load_b(c, w[j], j);
+#pragma unroll
+      for (int j = 0; j < kAStages - 1; ++j) {
+        load_a(c, ring, j);
+        load_b(c, w[j + kLead], j + kLead);
       }
+      if (count - c0 > 16) {
+        for (int g0 = 0; g0 < c.ngroups; g0 += kBSlots)
+          group_steps<2>(c, ring, w, g0, lane, acc, std::make_integer_sequence<int, kBSlots>{});
+      } else {
+        for (int g0 = 0; g0 < c.ngroups; g0 += kBSlots)
+          group_steps<1>(c, ring, w, g0, lane, acc, std::make_integer_sequence<int, kBSlots>{});
+      }
+      wait_vmem<0>();  // no load into the ring may outlive the chunk
+      lds_barrier();
 
-      // Sum the waves' partials in wave order; lane holds C[row c0 + 16 rb
-      // + l % 16][n0 + 16 b + 4 (l / 16) + t].
+      // Lane holds C[row c0 + 16 rb + l % 16][n0 + 32 w + 16 b + 4 (l / 16) + t].
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb)
+      for (int rb = 0; rb < kRB; ++rb) {
+        const int m = c0 + 16 * rb + (lane & 15);
+        if (m >= count) continue;
+        uint16_t* crow = C + (size_t)rows[m] * N + n0 + 32 * wave + 4 * (lane >> 4);
 #pragma unroll
-        for (int b = 0; b < kBlocks; ++b) red[wave][rb][b][lane] = acc[rb][b];
-      __syncthreads();
-      for (int b = wave; b < kBlocks; b += kWaves) {
-#pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) {
-          f32x4 s = red[0][rb][b][lane];
-#pragma unroll
-          for (int w = 1; w < kWaves; ++w) s += red[w][rb][b][lane];
-          const int m = c0 + 16 * rb + (lane & 15);
-          if (m < count) {
-            const int n = n0 + 16 * b + 4 * (lane >> 4);
-            *reinterpret_cast<uint2*>(C + (size_t)rows[m] * N + n) =
-                pack_bf16x4(gb * s[0], gb * s[1], gb * s[2], gb * s[3]);
-          }
-        }
+        for (int b = 0; b < kCB; ++b)
+          *reinterpret_cast<uint2*>(crow + 16 * b) =
+              pack_bf16x4(gb * acc[rb][b][0], gb * acc[rb][b][1], gb * acc[rb][b][2],
+                          gb * acc[rb][b][3]);
       }
-      __syncthreads();  // red[] is reused by the next chunk
     }
   }
 }

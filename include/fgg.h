@@ -170,7 +170,8 @@ fgg_status fp4_gemm_problems(const fgg_fp4_problem* problems, int count, void* s
  * bits) and multiplied with FP32 accumulation.  Built for few rows per expert
  * (decode): each expert's weights are read once per 16 of its rows, and an
  * expert with no rows costs no weight traffic.  Requirements as
- * grouped_fp4_gemm (A 16-byte aligned); b_global finite.
+ * grouped_fp4_gemm (A 16-byte aligned); b_global and A finite; M * K * 2 <
+ * 2^31 (the activations of a decode batch).
  */
 fgg_status grouped_w4a16_gemm(const void* A, const void* B, const void* b_scale,
                               const int32_t* m_indices, float b_global, void* C, int M, int N,
