@@ -136,3 +136,35 @@ def test_full_size_problem_batch_sampled():
     for i, (q, C) in enumerate(zip(probs, Cs)):
         rows = np.unique(np.concatenate([[0, q["M"] - 1], rng.choice(q["M"], 24, replace=False)]))
         assert_parity(q, C, rows=rows, what=f"problem {i}")
+
+
+def test_problem_batch_graph_replay():
+    """The descriptors are kernel arguments, captured with the graph; new
+    operand values written into the captured buffers are used at replay."""
+    import torch
+    shapes = BATCHES["mixed"]
+    probs = [_problem(M, N, K, 60 + i) for i, (M, N, K) in enumerate(shapes)]
+    ds = [to_dev(q) for q in probs]
+    outs = [torch.empty((q["M"], q["N"]), dtype=torch.bfloat16, device="cuda") for q in probs]
+    batch = [(d["A"], d["B"], d["a_scale"], d["b_scale"], q["alpha"]) for d, q in zip(ds, probs)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fgg.fp4_gemm_problems(batch, outs)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    log("problem batch graph capture")
+    with torch.cuda.graph(g):
+        fgg.fp4_gemm_problems(batch, outs)
+    for rep in range(2):
+        new = [_problem(M, N, K, 70 + 10 * rep + i) for i, (M, N, K) in enumerate(shapes)]
+        for d, q in zip(ds, new):
+            for k in ("A", "B", "a_scale", "b_scale"):
+                d[k].copy_(torch.from_numpy(np.ascontiguousarray(q[k])))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (q, C) in enumerate(zip(new, outs)):
+            # alpha is a captured kernel argument: the first batch's
+            assert_parity(dict(q, alpha=probs[i]["alpha"]), C, what=f"replay {rep} problem {i}")

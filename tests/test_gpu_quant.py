@@ -148,3 +148,88 @@ def test_quantised_activations_feed_the_gemm():
     out = C.float().cpu().numpy().astype(np.float64)
     res = oracle.check_tolerance(out, ref, ids)
     assert res["ok"], res
+
+
+EDGE = {
+    "one_block": (1, 128),        # 4 of 64 lanes hold a piece (FP8), 4 blocks (NVFP4)
+    "one_wave_plus_one": (1, 2176),  # 17 FP8 blocks, 136 NVFP4 blocks
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE))
+def test_partial_waves_bitwise(case):
+    M, K = EDGE[case]
+    x, t = _bf16(np.random.default_rng(300 + sorted(EDGE).index(case)), M, K)
+    log(f"quantisers partial wave {case}")
+    Q, S = _gpu_fp8(t)
+    q_ref, s_ref = oq.quantize_fp8_1x128(x)
+    assert np.array_equal(Q, q_ref) and np.array_equal(S, s_ref)
+    Q, S, g = _gpu_nvfp4(t)
+    q_ref, s_ref, g_ref = oq.quantize_nvfp4(x)
+    assert g == g_ref and np.array_equal(Q, q_ref) and np.array_equal(S, s_ref)
+
+
+def test_all_zero_input():
+    import torch
+    t = torch.zeros((4, 256), dtype=torch.bfloat16)
+    log("quantisers all-zero input")
+    Q, S = _gpu_fp8(t)
+    assert not Q.any() and np.all(S == 1.0)
+    Q, S, g = _gpu_nvfp4(t)
+    assert not Q.any() and not S.any() and g == 1.0
+
+
+def test_graph_replay_with_new_inputs():
+    """Both quantisers captured in one HIP graph (the NVFP4 path is four
+    kernels, no memset node) and replayed on new data written into the
+    captured input, each replay bitwise against the oracle."""
+    import torch
+    import fp4_grouped_gemm_amd as fgg
+    M, K = 24, 1152
+    X = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    X.copy_(_bf16(np.random.default_rng(400), M, K)[1])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fgg.quantize_fp8_1x128(X)
+        fgg.quantize_nvfp4(X)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    log("quantisers graph capture")
+    with torch.cuda.graph(g):
+        q8, s8 = fgg.quantize_fp8_1x128(X)
+        q4, s4, g4 = fgg.quantize_nvfp4(X)
+    for rep in range(3):
+        x, t = _bf16(np.random.default_rng(401 + rep), M, K, scale=10.0 ** (rep - 1))
+        X.copy_(t)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        r8 = oq.quantize_fp8_1x128(x)
+        r4 = oq.quantize_nvfp4(x)
+        assert np.array_equal(q8.cpu().numpy(), r8[0]) and np.array_equal(s8.cpu().numpy(), r8[1])
+        assert np.float32(g4.cpu().numpy()[0]) == r4[2], rep
+        assert np.array_equal(q4.cpu().numpy(), r4[0]) and np.array_equal(s4.cpu().numpy(), r4[1])
+
+
+@pytest.mark.slow
+def test_grid_stride_loops_on_sampled_rows():
+    """A tensor large enough that every wave of the capped grids takes
+    several turns of its loop; rows are independent (FP8) or share only the
+    global scale (NVFP4), so sampled rows are checked against the oracle."""
+    import torch
+    M, K = 16384, 8192
+    rng = np.random.default_rng(500)
+    t = torch.from_numpy(rng.standard_normal((M, K), dtype=np.float32)).to(torch.bfloat16)
+    x = t.float().numpy()
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 30, replace=False)]))
+    log("quantisers grid-stride loops")
+    Q, S = _gpu_fp8(t)
+    q_ref, s_ref = oq.quantize_fp8_1x128(x[rows])
+    assert np.array_equal(Q[rows], q_ref) and np.array_equal(S[rows], s_ref)
+    Q, S, g = _gpu_nvfp4(t)
+    g_ref = oq.nvfp4_global_scale(x)
+    assert g == g_ref
+    q_ref, s_ref, _ = oq.quantize_nvfp4(x[rows], g_ref)
+    assert np.array_equal(Q[rows], q_ref) and np.array_equal(S[rows], s_ref)

@@ -78,3 +78,29 @@ def test_full_size_decode():
     p = make("d5_decode_w4a16")
     log("w4a16 full-size decode")
     _check(p, _run(p), "d5_decode_w4a16")
+
+
+def test_graph_replay_rereads_routing():
+    """m_indices is read on the device at every launch: a captured call
+    replayed after the routing changes gives the new routing's result."""
+    import torch
+    p = CASES["decode_top2"]()
+    d = _dev(p)
+    C = torch.empty((p["M"], p["N"]), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fgg.grouped_w4a16_gemm(d["A"], d["B"], d["b_scale"], d["m_indices"], p["b_global"], out=C)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    log("w4a16 graph capture")
+    with torch.cuda.graph(g):
+        fgg.grouped_w4a16_gemm(d["A"], d["B"], d["b_scale"], d["m_indices"], p["b_global"], out=C)
+    base = p["m_indices"]
+    for rep, ids in enumerate([base, np.roll(base, 5), np.where(base % 2 == 0, -1, base)]):
+        d["m_indices"].copy_(torch.from_numpy(ids.astype(np.int32)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _check(dict(p, m_indices=ids.astype(np.int32)), C, f"replay {rep}")
