@@ -65,10 +65,22 @@ WORKLOADS = {
 QUANT_METRIC = "GB/s (algorithmic bytes / time) and % of HBM peak, activation quantiser"
 
 
-def kernel_source_hash() -> str:
+# Source files each workload's kernels are built from: a committed traffic
+# profile stays valid while these are unchanged.
+KERNEL_SOURCES = {
+    "fp8": ("fp8_grouped.hip", "common.h"),
+    "fp4": ("fp4.hip", "common.h"),
+    "fp4_problems": ("fp4.hip", "common.h"),
+    "quant_fp8": ("quant.hip", "common.h"),
+    "quant_nvfp4": ("quant.hip", "common.h"),
+    "w4a16": ("w4a16.hip", "common.h"),
+}
+
+
+def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp4_grouped_gemm_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES[WORKLOADS[workload]["kind"]]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -190,7 +202,7 @@ def rocprof_summary(root: str, workload: str, kernel: str, command: str) -> str:
         f"# rocprofv3 summary: {kernel} on {workload}",
         "",
         f"command: {command}",
-        f"kernel_source_sha={kernel_source_hash()}",
+        f"kernel_source_sha={kernel_source_hash(workload)}",
         f"dispatches traced: {len(durs)}; mean duration {mean(durs):.2f} us; "
         f"min {min(durs) if durs else float('nan'):.2f} us; max {max(durs) if durs else float('nan'):.2f} us",
     ]
@@ -209,7 +221,7 @@ def rocprof_summary(root: str, workload: str, kernel: str, command: str) -> str:
         fh.write(f"# HBM traffic of {kernel} on {workload}, from rocprofv3 FETCH_SIZE/WRITE_SIZE\n")
         fh.write(f"# scaled by a 1 GiB copy calibration (fetch x{f_scale:.4f}, write x{w_scale:.4f})\n")
         fh.write(f"# command: {command}\n")
-        fh.write(f"kernel_source_sha={kernel_source_hash()}\n")
+        fh.write(f"kernel_source_sha={kernel_source_hash(workload)}\n")
         fh.write(f"mean_duration_us={mean(durs):.3f}\n")
         fh.write(f"hbm_bytes_per_launch={hbm:.0f}\n")
     return text
@@ -255,9 +267,10 @@ def bench_quant(args, torch):
         "config": {"workload": args.workload, "desc": w["desc"], "M": M, "K": K,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK, 4), "traffic": None,
+                     "frac": round(gbps / HBM_PEAK, 4),
+                     "traffic": measured_traffic(args.workload, kernel_source_hash(args.workload)),
                      "algorithmic_bytes": nbytes},
-        "kernel_source_sha": kernel_source_hash(),
+        "kernel_source_sha": kernel_source_hash(args.workload),
     }
     if not args.no_cpu_baseline:
         import oracle.quant as oq
@@ -354,9 +367,10 @@ def bench_w4a16(args, torch):
                    "timing": "hip graph of K launches" if args.graph else "K stream launches",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK, 4), "traffic": None,
+                     "frac": round(gbps / HBM_PEAK, 4),
+                     "traffic": measured_traffic(args.workload, kernel_source_hash(args.workload)),
                      "algorithmic_bytes": nbytes, "us_per_call": round(ms * 1e3, 2)},
-        "kernel_source_sha": kernel_source_hash(),
+        "kernel_source_sha": kernel_source_hash(args.workload),
     }
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_info
@@ -415,9 +429,10 @@ def bench_problems(args, torch):
                    "problems": [[q["M"], q["N"], q["K"]] for q in probs],
                    "tile": args.tile, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK["fp16"],
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK["fp16"], 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK["fp16"], 4),
+                     "traffic": measured_traffic(args.workload, kernel_source_hash(args.workload)),
                      "mfma_dtype": "fp16", "frac_of_fp4_peak": round(tflops / PEAK["fp4"], 4)},
-        "kernel_source_sha": kernel_source_hash(),
+        "kernel_source_sha": kernel_source_hash(args.workload),
     }
     if not args.no_cpu_baseline:
         # the oracle on the first rows of every problem, in turn, until the budget
@@ -613,7 +628,7 @@ def main():
     flops = 2.0 * rr * N * K
     tflops = flops / (ms * 1e-3) / 1e12
     mma = "fp8" if kind == "fp8" else "fp16"
-    src = kernel_source_hash()
+    src = kernel_source_hash(args.workload)
     traffic = measured_traffic(args.workload, src)
     tiles = fgg.rank_tiles(fgg.FP8 if kind == "fp8" else fgg.FP4, M, N, K, G,
                            num_cus=fgg.device_info()["num_cus"])
