@@ -17,13 +17,13 @@
 //    workgroups also zero the padding rows found); a workgroup whose expert
 //    has no rows stops there and never reads that expert's weights.
 //  * Rows run 32 at a time (two MFMA row blocks sharing each dequantised
-//    weight fragment).  Their activations, 32 rows x 128 K per group, go
+//    weight fragment).  Their activations, 32 rows x 256 K per group, go
 //    through a 4-stage LDS ring with direct-to-LDS loads (no registers),
 //    shared by the four waves; 16-byte chunks are XOR-swizzled by row so a
 //    fragment read hits 16 distinct chunk positions.
 //  * Weights stream through a 4-slot register ring, 3 groups ahead: per
-//    group a lane loads 16 packed bytes (32 weights of one column) and their
-//    two E4M3 scale codes per column block.  Every group issues the same
+//    group a lane loads 32 packed bytes (64 weights of one column) and their
+//    four E4M3 scale codes per column block.  Every group issues the same
 //    loads (past the last group they reload it and add exact zeros through
 //    a zero scale), so one explicit count waits for the oldest group.
 //  * Weights are dequantised exactly to BF16 in registers (q * s has at most
@@ -49,7 +49,9 @@ constexpr int kCB = 2;                 // MFMA column blocks per wave
 constexpr int kCols = 16 * kCB * kWaves;  // columns per workgroup
 constexpr int kRB = 2;                 // MFMA row blocks per chunk
 constexpr int kRows = 16 * kRB;        // rows per chunk
-constexpr int kGroup = 128;            // K per group: 4 MFMAs of K = 32
+constexpr int kGroup = 256;            // K per group: 8 MFMAs of K = 32
+constexpr int kWords = kGroup / 32;    // 32-bit words of packed weights per lane per group
+constexpr int kChunks = kGroup / 8;    // 16-byte activation chunks per row per group
 constexpr int kScan = 1024;            // m_indices entries compacted per scan
 constexpr int kAStages = 4;            // LDS ring of activation groups
 constexpr int kBSlots = 4;             // register ring of weight groups
@@ -60,8 +62,8 @@ static_assert(kCols == 2 * 64, "a zero row is one 4-byte store per lane");
 static_assert(kBSlots % kAStages == 0, "an unrolled block of kBSlots groups starts at stage 0");
 static_assert(kADma * 16 * kThreads == kAStage, "activation staging split");
 // Loads per group per wave: activation DMAs, then per column block the
-// weight bytes and the scale codes.
-constexpr int kLoadsPerGroup = kADma + 2 * kCB;
+// weight bytes (16 bytes per load) and the scale codes.
+constexpr int kLoadsPerGroup = kADma + kCB * (kWords / 4 + 1);
 // Step i issues the activations of group i + kAStages - 1, then the weights
 // of group i + kAhead.  So group i's weights go out kLead steps before its
 // activations (or right after them, kLead = 0), and when step i waits, the
@@ -69,11 +71,12 @@ constexpr int kLoadsPerGroup = kADma + 2 * kCB;
 // and by the kAStages - 2 steps in between.
 constexpr int kLead = kAhead - kAStages + 1;
 static_assert(kLead >= 0, "weights must not trail their activations");
-constexpr int kWaitAfter = (kLead > 0 ? 2 * kCB : 0) + (kAStages - 2) * kLoadsPerGroup;
+constexpr int kWaitAfter =
+    (kLead > 0 ? kCB * (kWords / 4 + 1) : 0) + (kAStages - 2) * kLoadsPerGroup;
 
 struct Weights {
-  i32x4 b[kCB];      // 32 E2M1 codes of column c at k0 + 32 q
-  uint32_t s[kCB];   // their two E4M3 scale codes
+  i32x4 b[kCB][kWords / 4];  // 64 E2M1 codes of column c at k0 + 64 q
+  uint32_t s[kCB];           // their four E4M3 scale codes
 };
 
 template <int H>
@@ -95,8 +98,9 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t word, float s) {
   return r;
 }
 
-// LDS byte offset of 16-byte chunk c (0..15) of activation row r (0..31).
-__device__ __forceinline__ int a_swz(int r, int c) { return r * (kGroup * 2) + ((c ^ (r & 15)) << 4); }
+// LDS byte offset of 16-byte chunk c (0..31) of activation row r (0..31).
+__device__ __forceinline__ int a_swz(int r, int c) { return r * (kGroup * 2) + ((c ^ r) << 4); }
+static_assert(kChunks == kRows, "the chunk swizzle uses the row's 5 bits");
 
 struct Ctx {
   const uint8_t* bcol[kCB];   // weight row of this lane's column, per column block
@@ -105,6 +109,7 @@ struct Ctx {
   uint32_t a_off[kADma];      // this lane's activation chunks: row offset + chunk
   uint32_t lds_a[kADma];      // their LDS destinations (stage 0)
   int ngroups;
+  int K;
   int q;
 };
 
@@ -118,13 +123,24 @@ __device__ __forceinline__ void load_a(const Ctx& c, uint8_t* ring, int g) {
   (void)ring;
 }
 
+// Group g's weights of this lane: K = k0 + 64 q .. + 63.  When K is an odd
+// multiple of 128 the last group is half full; lanes past K load the
+// group's first valid piece instead (never past the row) and are zeroed by
+// lane_valid.
 __device__ __forceinline__ void load_b(const Ctx& c, Weights& w, int g) {
   const int k0 = min(g, c.ngroups - 1) * kGroup;
+  const int kq = k0 + 64 * c.q < c.K ? k0 + 64 * c.q : k0;
 #pragma unroll
   for (int b = 0; b < kCB; ++b) {
-    w.b[b] = *reinterpret_cast<const i32x4*>(c.bcol[b] + (k0 + 32 * c.q) / 2);
-    w.s[b] = *reinterpret_cast<const uint16_t*>(c.scol[b] + (k0 + 32 * c.q) / 16);
+#pragma unroll
+    for (int h = 0; h < kWords / 4; ++h)
+      w.b[b][h] = *reinterpret_cast<const i32x4*>(c.bcol[b] + kq / 2 + 16 * h);
+    w.s[b] = *reinterpret_cast<const uint32_t*>(c.scol[b] + kq / 16);
   }
+}
+
+__device__ __forceinline__ bool lane_valid(const Ctx& c, int g) {
+  return g < c.ngroups && g * kGroup + 64 * c.q < c.K;
 }
 
 // MFMAs of one group: activations from LDS stage `a`, weights from `w`;
@@ -135,24 +151,21 @@ template <int RB>
 __device__ __forceinline__ void mma_group(const uint8_t* a, const Weights& w, bool valid, int lane,
                                           f32x4 acc[kRB][kCB]) {
   const int r = lane & 15, q = lane >> 4;
-  float s0[kCB], s1[kCB];
+  uint32_t sc[kCB];
 #pragma unroll
-  for (int b = 0; b < kCB; ++b) {
-    const uint32_t sc = valid ? w.s[b] : 0u;  // code 0 = scale 0: adds exact zeros
-    s0[b] = __builtin_amdgcn_cvt_f32_fp8((int)(sc & 0xFFu), 0);
-    s1[b] = __builtin_amdgcn_cvt_f32_fp8((int)((sc >> 8) & 0xFFu), 0);
-  }
+  for (int b = 0; b < kCB; ++b) sc[b] = valid ? w.s[b] : 0u;  // code 0 = scale 0: exact zeros
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // k0 + 32 q + 8 j .. + 8: chunk 4 q + j of the lane's activation rows and
-    // word j of its 16 weight bytes
+  for (int t = 0; t < kWords; ++t) {
+    // k0 + 64 q + 8 t .. + 8: chunk 8 q + t of the lane's activation rows and
+    // word t of its 32 weight bytes (block scale t / 2)
     bf16x8 af[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
-      af[rb] = *reinterpret_cast<const bf16x8*>(a + a_swz(16 * rb + r, 4 * q + j));
+      af[rb] = *reinterpret_cast<const bf16x8*>(a + a_swz(16 * rb + r, 8 * q + t));
 #pragma unroll
     for (int b = 0; b < kCB; ++b) {
-      const bf16x8 bf = dequant8((uint32_t)w.b[b][j], j < 2 ? s0[b] : s1[b]);
+      const float s = __builtin_amdgcn_cvt_f32_fp8((int)((sc[b] >> (8 * (t / 2))) & 0xFFu), 0);
+      const bf16x8 bf = dequant8((uint32_t)w.b[b][t / 4][t % 4], s);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
         acc[rb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, af[rb], acc[rb][b], 0, 0, 0);
@@ -173,7 +186,7 @@ __device__ __forceinline__ void group_step(const Ctx& c, uint8_t* ring, Weights 
   load_a(c, ring, i + kAStages - 1);
   load_b(c, w[(I + kAhead) % kBSlots], i + kAhead);
   __builtin_amdgcn_sched_barrier(0);
-  mma_group<RB>(ring + (I % kAStages) * kAStage, w[I % kBSlots], i < c.ngroups, lane, acc);
+  mma_group<RB>(ring + (I % kAStages) * kAStage, w[I % kBSlots], lane_valid(c, i), lane, acc);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -206,7 +219,8 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_kernel(const uint16_t* __re
 
   Ctx c;
   c.q = lane >> 4;
-  c.ngroups = K / kGroup;
+  c.ngroups = (K + kGroup - 1) / kGroup;
+  c.K = K;
   c.ra = rsrc(A, (uint32_t)((size_t)M * K * 2));
 #pragma unroll
   for (int b = 0; b < kCB; ++b) {
@@ -244,13 +258,13 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_kernel(const uint16_t* __re
 
     for (int c0 = 0; c0 < count; c0 += kRows) {
       // This thread's activation chunks: LDS chunk p = u * 256 + tid of a
-      // stage is row p / 16, physical chunk p % 16, which holds logical
-      // chunk (p % 16) ^ (row % 16); rows past the chunk read a valid row
-      // and are never stored.
+      // stage is row p / kChunks, physical chunk p % kChunks, which holds
+      // logical chunk (p % kChunks) ^ row; rows past the chunk read a valid
+      // row and are never stored.
 #pragma unroll
       for (int u = 0; u < kADma; ++u) {
         const int p = u * kThreads + tid;
-        const int row = p >> 4, lc = (p & 15) ^ (row & 15);
+        const int row = p / kChunks, lc = (p % kChunks) ^ row;
         c.a_off[u] = (uint32_t)rows[min(c0 + row, count - 1)] * (uint32_t)K * 2u + (uint32_t)lc * 16u;
         c.lds_a[u] = lds_addr(ring) + (uint32_t)(u * kThreads + wave * 64) * 16u;
       }
@@ -301,7 +315,7 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_kernel(const uint16_t* __re
 using namespace w4a16_detail;
 
 hipError_t launch_w4a16(const W4A16Args& a, hipStream_t s) {
-  if (a.N % kCols || a.K % kGroup) return hipErrorInvalidValue;
+  if (a.N % kCols || a.K % 128) return hipErrorInvalidValue;
   const long long grid = (long long)(a.N / kCols) * a.G;
   if (grid <= 0 || grid > INT_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(w4a16_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a.A, a.B,
