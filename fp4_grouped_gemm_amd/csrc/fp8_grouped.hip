@@ -105,8 +105,12 @@ struct Pass {
   uint32_t lane_off;              // (8 w + l / 8) K + 16 chunk
   uint32_t K;
   int nkb;
-  const float* bs_row;            // b_scale row of this wave's 128-column block
-  float sb_next;
+  // b_scale row of this wave's 128-column block: lane l holds block
+  // 64 c + l of the current chunk c of 64 K blocks (read with readlane, so
+  // the K loop issues no scalar loads, whose out-of-order return would make
+  // every LDS wait a full drain).
+  const float* bs_row;
+  float bs_vec;
   uint64_t a_groups;              // 8-row groups of A holding a row of this pass
   bool active;                    // this wave's 64 rows hold a row of this pass
   f32x4 acc[T::TM][T::TN];
@@ -143,7 +147,13 @@ struct Pass {
     }
   }
 
-  __device__ __forceinline__ void load_b_scale(int kb) { sb_next = bs_row[kb]; }
+  // Blocks [kb, kb + 64) of the b_scale row into bs_vec (kb a multiple of 64).
+  __device__ __forceinline__ void load_b_scales(int kb, int lane) {
+    bs_vec = kb + lane < nkb ? bs_row[kb + lane] : 0.f;
+  }
+  __device__ __forceinline__ float b_scale_of(int kb) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bs_vec), kb & 63));
+  }
 };
 
 // One K step: start staging step kb + STAGES - 1 into `wr` (if any), then
@@ -158,28 +168,29 @@ __device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* w
                                       int wm, int wn) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   // this step's combined scales; read before any load of this step is issued
+  const float sb = ps.b_scale_of(kb);
   float s[T::TM];
 #pragma unroll
   for (int i = 0; i < T::TM; ++i)
-    s[i] = sa_rd[(wm * T::WM + i * 16 + (lane & 15)) * T::SA_ROW + (unsigned)kb % T::SA_BLK] *
-           ps.sb_next;
+    s[i] = sa_rd[(wm * T::WM + i * 16 + (lane & 15)) * T::SA_ROW + (unsigned)kb % T::SA_BLK] * sb;
   const int kl = kb + T::STAGES - 1;  // the step whose tiles this step loads
   const bool load = kl < ps.nkb;
   // the next a_scale chunk, at the first step of a chunk (implies `load`)
   const bool sload = (unsigned)kb % T::SA_BLK == 0 && kb + T::SA_BLK < ps.nkb;
-  if (kb + 1 < ps.nkb) {  // implied by `load`
-    if (load) {
-      ps.stage_in(wr, kl, wave);
-      if (sload) ps.stage_scales(sa_wr, (unsigned)kb / T::SA_BLK + 1, wave, lane);
-    }
-    ps.load_b_scale(kb + 1);
+  if (load) {
+    ps.stage_in(wr, kl, wave);
+    if (sload) ps.stage_scales(sa_wr, (unsigned)kb / T::SA_BLK + 1, wave, lane);
   }
+  // next chunk of 64 b_scale blocks after the last use of this one (rare:
+  // K above 8192; the compiler's wait for it drains the loads in flight)
+  if ((kb & 63) == 63 && kb + 1 < ps.nkb) ps.load_b_scales(kb + 1, lane);
   if (ps.active) {
+  // B fragment first: the first MFMA then waits for it and A fragment 0 only
+  const uint8_t* rb = rd + T::A_BYTES;
+  i32x8 bf = read_frag(rb, wn * T::WN, lane);
   i32x8 af[T::TM];
 #pragma unroll
   for (int i = 0; i < T::TM; ++i) af[i] = read_frag(rd, wm * T::WM + i * 16, lane);
-  const uint8_t* rb = rd + T::A_BYTES;
-  i32x8 bf = read_frag(rb, wn * T::WN, lane);
   i32x8 bnext = bf;
   // MFMA t = (column subtile j, row subtile i) in j-major order; its partial
   // is promoted LAG MFMAs later, from a small ring, so the FMAs overlap the
@@ -338,9 +349,9 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) ps.acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+      ps.load_b_scales(0, lane);
       ps.stage_in(lds0, 0, wave);
       ps.stage_scales(sa0, 0, wave, lane);
-      ps.load_b_scale(0);
       if constexpr (T::STAGES == 2) {
         wait_vmem<0>();
         __syncthreads();

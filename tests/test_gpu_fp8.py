@@ -105,6 +105,22 @@ def test_persistent_loop_reinitialises_state(max_wg):
         assert_parity(p, C, what=f"max_wg={max_wg}/tile{tile}")
 
 
+@pytest.mark.parametrize("K", [8320, 16640])
+def test_long_k_b_scale_per_block(K):
+    """K above 64 scale blocks: the kernel holds a wave's b_scale row 64
+    blocks at a time and reloads the next 64 in the loop.  b_scale varies by
+    powers of two from block to block, so a block read from the wrong
+    position would be far outside the tolerance."""
+    p = _prob([0] * 70 + [1] * 90, N=256, K=K, G=2, seed=21)
+    rng = np.random.default_rng(22)
+    p["b_scale"] = (p["b_scale"] * np.exp2(rng.integers(-6, 7, p["b_scale"].shape))
+                    ).astype(np.float32)
+    for tile in FP8_TILES:
+        log(f"long K={K} tile {tile}")
+        C = run(p, tile_id=tile)
+        assert_parity(p, C, what=f"K={K}/tile{tile}")
+
+
 def test_small_integer_inputs_bitwise():
     """Codes decoding to small integers and power-of-two scales keep every
     FP32 operation exact, so the BF16 output must equal the oracle's
