@@ -79,10 +79,18 @@ struct Weights {
   uint32_t s[kCB];           // their four E4M3 scale codes
 };
 
+// The two codes of byte H times s, as a BF16 pair.  q * s has at most 6
+// significant bits, so its FP32 value carries no bits below the top 16 and
+// BF16 is that upper half exactly: a byte permute takes the upper halves of
+// the two products (no rounding convert, which issues at a quarter of the
+// multiply rate).  A NaN scale code gives the quiet NaN 0x7FC00000, whose
+// upper half is a BF16 NaN.
 template <int H>
 __device__ __forceinline__ void dequant2(uint32_t word, float s, bf16x8& r) {
   const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, H);  // byte H
-  const bf16x2 p = __builtin_convertvector((f32x2){v[0] * s, v[1] * s}, bf16x2);
+  const uint32_t lo = __builtin_bit_cast(uint32_t, v[0] * s);
+  const uint32_t hi = __builtin_bit_cast(uint32_t, v[1] * s);
+  const bf16x2 p = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(hi, lo, 0x07060302u));
   r[2 * H] = p[0];
   r[2 * H + 1] = p[1];
 }
