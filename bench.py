@@ -13,8 +13,10 @@ Default workload: grouped FP8 MoE prefill, G=8, M=8192 routed rows in sorted
 runs (multinomial counts, unaligned to 128), N=4096, K=7168.
 
 TFLOPS = 2 * (real rows) * N * K / time; padding rows (m_indices = -1) are
-excluded.  `roofline` prices the kernel against MI355X's published dense
-MFMA peak for the arithmetic it uses.  `cpu_baseline` is the float64 CPU
+excluded.  `value` is whole-job throughput (the timed region over K).
+`roofline` prices the kernel against MI355X's published dense MFMA peak for
+the arithmetic it uses, at the same average launch duration
+(`us_per_launch`).  `cpu_baseline` is the float64 CPU
 oracle timed on a bounded row sample of the same workload on this host.
 """
 from __future__ import annotations
@@ -236,6 +238,40 @@ def quant_bytes(kind: str, M: int, K: int) -> int:
     return M * K * 2 + M * K // 2 + M * (K // 16) + 4
 
 
+def time_launches(torch, call, steps: int, graph: bool = False):
+    """Time `steps` calls of `call` (each one kernel launch) on the current
+    stream, with HIP events recorded on that stream around the timed region
+    (or around one graph replay of `steps` captured launches).  Returns
+    (ms_per_step, ms_per_launch), both the region over `steps`: the average
+    launch duration in steady state.  Launches are not bracketed one by one:
+    an event between two launches is a barrier, which for the short kernels
+    adds the launch ramp to every duration and for the grouped GEMMs removes
+    the overlap of one launch's tail with the next launch's head."""
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                call()
+        g.replay()  # untimed first replay
+        torch.cuda.synchronize()
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        return ms, ms
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    return ms, ms
+
+
 def bench_quant(args, torch):
     import fp4_grouped_gemm_amd as fgg
     w = WORKLOADS[args.workload]
@@ -248,17 +284,12 @@ def bench_quant(args, torch):
         (lambda: fgg.quantize_nvfp4(Xd))
     for _ in range(args.warmup):
         out = run()
-    stream = torch.cuda.current_stream()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms, ms_launch = time_launches(torch, run, args.steps)
+    out = run()
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        out = run()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
     nbytes = quant_bytes(kind, M, K)
     gbps = nbytes / (ms * 1e-3) / 1e9
+    gbps_launch = nbytes / (ms_launch * 1e-3) / 1e9
     res = {
         "metric": QUANT_METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -266,10 +297,10 @@ def bench_quant(args, torch):
         "data": "synthetic (seeded NumPy N(0,1), BF16, resident in HBM)",
         "config": {"workload": args.workload, "desc": w["desc"], "M": M, "K": K,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbps_launch, 1), "peak": HBM_PEAK,
+                     "unit": "GB/s", "frac": round(gbps_launch / HBM_PEAK, 4),
                      "traffic": measured_traffic(args.workload, kernel_source_hash(args.workload)),
-                     "algorithmic_bytes": nbytes},
+                     "algorithmic_bytes": nbytes, "us_per_launch": round(ms_launch * 1e3, 2)},
         "kernel_source_sha": kernel_source_hash(args.workload),
     }
     if not args.no_cpu_baseline:
@@ -334,28 +365,10 @@ def bench_w4a16(args, torch):
 
     for _ in range(args.warmup):
         call()
-    stream = torch.cuda.current_stream()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    if args.graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(args.steps):
-                call()
-        graph.replay()
-        torch.cuda.synchronize()
-        start.record(stream)
-        graph.replay()
-        end.record(stream)
-    else:
-        start.record(stream)
-        for _ in range(args.steps):
-            call()
-        end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms, ms_launch = time_launches(torch, call, args.steps, args.graph)
     nbytes = w4a16_bytes(p)
     gbps = nbytes / (ms * 1e-3) / 1e9
+    gbps_launch = nbytes / (ms_launch * 1e-3) / 1e9
     res = {
         "metric": "GB/s (algorithmic bytes / time) and % of HBM peak, grouped W4A16 decode",
         "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -366,10 +379,10 @@ def bench_w4a16(args, torch):
                    "M": p["M"], "N": p["N"], "K": p["K"], "G": p["G"],
                    "timing": "hip graph of K launches" if args.graph else "K stream launches",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbps_launch, 1), "peak": HBM_PEAK,
+                     "unit": "GB/s", "frac": round(gbps_launch / HBM_PEAK, 4),
                      "traffic": measured_traffic(args.workload, kernel_source_hash(args.workload)),
-                     "algorithmic_bytes": nbytes, "us_per_call": round(ms * 1e3, 2)},
+                     "algorithmic_bytes": nbytes, "us_per_launch": round(ms_launch * 1e3, 2)},
         "kernel_source_sha": kernel_source_hash(args.workload),
     }
     if not args.no_cpu_baseline:
@@ -409,17 +422,11 @@ def bench_problems(args, torch):
     kw = {} if args.tile is None else {"tile_id": args.tile}
     for _ in range(args.warmup):
         fgg.fp4_gemm_problems(batch, outs, **kw)
-    stream = torch.cuda.current_stream()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        fgg.fp4_gemm_problems(batch, outs, **kw)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms, ms_launch = time_launches(torch, lambda: fgg.fp4_gemm_problems(batch, outs, **kw),
+                                  args.steps)
     flops = sum(2.0 * q["M"] * q["N"] * q["K"] for q in probs)
     tflops = flops / (ms * 1e-3) / 1e12
+    tflops_launch = flops / (ms_launch * 1e-3) / 1e12
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -428,10 +435,11 @@ def bench_problems(args, torch):
         "config": {"workload": args.workload, "desc": WORKLOADS[args.workload]["desc"],
                    "problems": [[q["M"], q["N"], q["K"]] for q in probs],
                    "tile": args.tile, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK["fp16"],
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK["fp16"], 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops_launch, 2), "peak": PEAK["fp16"],
+                     "unit": "TFLOP/s", "frac": round(tflops_launch / PEAK["fp16"], 4),
                      "traffic": measured_traffic(args.workload, kernel_source_hash(args.workload)),
-                     "mfma_dtype": "fp16", "frac_of_fp4_peak": round(tflops / PEAK["fp4"], 4)},
+                     "mfma_dtype": "fp16", "frac_of_fp4_peak": round(tflops_launch / PEAK["fp4"], 4),
+                     "us_per_launch": round(ms_launch * 1e3, 2)},
         "kernel_source_sha": kernel_source_hash(args.workload),
     }
     if not args.no_cpu_baseline:
@@ -604,29 +612,11 @@ def main():
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         run(p, d, out=C, **kw)
-    stream = torch.cuda.current_stream()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    if args.graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(args.steps):
-                run(p, d, out=C, **kw)
-        graph.replay()  # untimed first replay
-        torch.cuda.synchronize()
-        start.record(stream)
-        graph.replay()
-        end.record(stream)
-    else:
-        start.record(stream)
-        for _ in range(args.steps):
-            run(p, d, out=C, **kw)
-        end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms, ms_launch = time_launches(torch, lambda: run(p, d, out=C, **kw), args.steps, args.graph)
     rr = real_rows(p)
     flops = 2.0 * rr * N * K
     tflops = flops / (ms * 1e-3) / 1e12
+    tflops_launch = flops / (ms_launch * 1e-3) / 1e12
     mma = "fp8" if kind == "fp8" else "fp16"
     src = kernel_source_hash(args.workload)
     traffic = measured_traffic(args.workload, src)
@@ -644,15 +634,16 @@ def main():
                    "run_split": args.run_split, "max_workgroups": args.max_workgroups,
                    "timing": "hip graph of K launches" if args.graph
                    else "K stream launches", "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK[mma],
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK[mma], 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops_launch, 2), "peak": PEAK[mma],
+                     "unit": "TFLOP/s", "frac": round(tflops_launch / PEAK[mma], 4),
                      "traffic": traffic, "mfma_dtype": mma,
                      "algorithmic_bytes": algorithmic_bytes(p),
-                     "hbm_gbps_algorithmic": round(algorithmic_bytes(p) / (ms * 1e-3) / 1e9, 1)},
+                     "hbm_gbps_algorithmic": round(algorithmic_bytes(p) / (ms_launch * 1e-3) / 1e9, 1),
+                     "us_per_launch": round(ms_launch * 1e3, 2)},
         "kernel_source_sha": src,
     }
     if kind == "fp4":
-        out["roofline"]["frac_of_fp4_peak"] = round(tflops / PEAK["fp4"], 4)
+        out["roofline"]["frac_of_fp4_peak"] = round(tflops_launch / PEAK["fp4"], 4)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
         base, parity = cpu_baseline(p, C, args.cpu_seconds)
