@@ -7,7 +7,12 @@ One step = one call of the library entry point for the workload (the whole
 hot path: routing discovery, LDS staging, MFMA, per-block rescale, BF16
 epilogue) on inputs already resident in HBM.  W untimed steps, then exactly
 K timed steps between two synchronisations, timed with HIP events recorded
-on the stream the kernels run on.  Prints one JSON line.
+on the stream the kernels run on.  By default the K steps are captured in
+one HIP graph and the timed region is one replay of it (after an untimed
+replay), the way a captured MoE layer runs them; --stream times K launches
+issued one by one instead.  The line carries the other mode's figure too
+(ms_per_step_stream or ms_per_step_graph), timed second in the same
+process.  Prints one JSON line.
 
 Default workload: grouped FP8 MoE prefill, G=8, M=8192 routed rows in sorted
 runs (multinomial counts, unaligned to 128), N=4096, K=7168.
@@ -37,6 +42,9 @@ METRIC = "TFLOPS and % of MFMA peak, grouped FP8 / NVFP4 block-scaled GEMM"
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
 PEAK = {"fp8": 5000.0, "fp4": 10100.0, "fp16": 2500.0, "bf16": 2500.0}
 HBM_PEAK = 8000.0
+TIMING = {"graph": "one HIP graph replay of K captured launches",
+          "stream": "K launches issued one by one on the stream"}
+OTHER = {"graph": "stream", "stream": "graph"}
 
 WORKLOADS = {
     "c2_moe_fp8": dict(kind="fp8", desc="grouped FP8 MoE prefill, G=8, M=8192, N=4096, K=7168"),
@@ -238,6 +246,14 @@ def quant_bytes(kind: str, M: int, K: int) -> int:
     return M * K * 2 + M * K // 2 + M * (K // 16) + 4
 
 
+def time_modes(torch, call, steps: int, timing: str, single: bool = False):
+    """(ms per step in the `timing` mode, ms per step in the other mode, or
+    None with `single`)."""
+    ms, _ = time_launches(torch, call, steps, timing == "graph")
+    other = None if single else time_launches(torch, call, steps, timing != "graph")[0]
+    return ms, other
+
+
 def time_launches(torch, call, steps: int, graph: bool = False):
     """Time `steps` calls of `call` (each one kernel launch) on the current
     stream, with HIP events recorded on that stream around the timed region
@@ -284,7 +300,8 @@ def bench_quant(args, torch):
         (lambda: fgg.quantize_nvfp4(Xd))
     for _ in range(args.warmup):
         out = run()
-    ms, ms_launch = time_launches(torch, run, args.steps)
+    ms, ms_other = time_modes(torch, run, args.steps, args.timing, args.single_timing)
+    ms_launch = ms
     out = run()
     torch.cuda.synchronize()
     nbytes = quant_bytes(kind, M, K)
@@ -296,13 +313,15 @@ def bench_quant(args, torch):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded NumPy N(0,1), BF16, resident in HBM)",
         "config": {"workload": args.workload, "desc": w["desc"], "M": M, "K": K,
-                   "parallelism": "single GPU"},
+                   "timing": TIMING[args.timing], "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbps_launch, 1), "peak": HBM_PEAK,
                      "unit": "GB/s", "frac": round(gbps_launch / HBM_PEAK, 4),
                      "traffic": measured_traffic(args.workload, kernel_source_hash(args.workload)),
                      "algorithmic_bytes": nbytes, "us_per_launch": round(ms_launch * 1e3, 2)},
         "kernel_source_sha": kernel_source_hash(args.workload),
     }
+    res["ms_per_step_" + OTHER[args.timing]] = (None if ms_other is None
+                                                   else round(ms_other, 5))
     if not args.no_cpu_baseline:
         import oracle.quant as oq
         from threadpoolctl import threadpool_info
@@ -365,7 +384,8 @@ def bench_w4a16(args, torch):
 
     for _ in range(args.warmup):
         call()
-    ms, ms_launch = time_launches(torch, call, args.steps, args.graph)
+    ms, ms_other = time_modes(torch, call, args.steps, args.timing, args.single_timing)
+    ms_launch = ms
     nbytes = w4a16_bytes(p)
     gbps = nbytes / (ms * 1e-3) / 1e9
     gbps_launch = nbytes / (ms_launch * 1e-3) / 1e9
@@ -377,14 +397,15 @@ def bench_w4a16(args, torch):
         "data": "synthetic (seeded NumPy; weights quantised on the host, resident in HBM)",
         "config": {"workload": args.workload, "desc": WORKLOADS[args.workload]["desc"],
                    "M": p["M"], "N": p["N"], "K": p["K"], "G": p["G"],
-                   "timing": "hip graph of K launches" if args.graph else "K stream launches",
-                   "parallelism": "single GPU"},
+                   "timing": TIMING[args.timing], "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbps_launch, 1), "peak": HBM_PEAK,
                      "unit": "GB/s", "frac": round(gbps_launch / HBM_PEAK, 4),
                      "traffic": measured_traffic(args.workload, kernel_source_hash(args.workload)),
                      "algorithmic_bytes": nbytes, "us_per_launch": round(ms_launch * 1e3, 2)},
         "kernel_source_sha": kernel_source_hash(args.workload),
     }
+    res["ms_per_step_" + OTHER[args.timing]] = (None if ms_other is None
+                                                   else round(ms_other, 5))
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_info
         print("[bench] cpu baseline (oracle, every row)", file=sys.stderr, flush=True)
@@ -422,8 +443,9 @@ def bench_problems(args, torch):
     kw = {} if args.tile is None else {"tile_id": args.tile}
     for _ in range(args.warmup):
         fgg.fp4_gemm_problems(batch, outs, **kw)
-    ms, ms_launch = time_launches(torch, lambda: fgg.fp4_gemm_problems(batch, outs, **kw),
-                                  args.steps)
+    ms, ms_other = time_modes(torch, lambda: fgg.fp4_gemm_problems(batch, outs, **kw),
+                              args.steps, args.timing, args.single_timing)
+    ms_launch = ms
     flops = sum(2.0 * q["M"] * q["N"] * q["K"] for q in probs)
     tflops = flops / (ms * 1e-3) / 1e12
     tflops_launch = flops / (ms_launch * 1e-3) / 1e12
@@ -434,7 +456,8 @@ def bench_problems(args, torch):
         "data": "synthetic (seeded NumPy; quantised on the host, resident in HBM)",
         "config": {"workload": args.workload, "desc": WORKLOADS[args.workload]["desc"],
                    "problems": [[q["M"], q["N"], q["K"]] for q in probs],
-                   "tile": args.tile, "parallelism": "single GPU"},
+                   "tile": args.tile, "timing": TIMING[args.timing],
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops_launch, 2), "peak": PEAK["fp16"],
                      "unit": "TFLOP/s", "frac": round(tflops_launch / PEAK["fp16"], 4),
                      "traffic": measured_traffic(args.workload, kernel_source_hash(args.workload)),
@@ -442,6 +465,8 @@ def bench_problems(args, torch):
                      "us_per_launch": round(ms_launch * 1e3, 2)},
         "kernel_source_sha": kernel_source_hash(args.workload),
     }
+    out["ms_per_step_" + OTHER[args.timing]] = (None if ms_other is None
+                                                   else round(ms_other, 5))
     if not args.no_cpu_baseline:
         # the oracle on the first rows of every problem, in turn, until the budget
         print("[bench] cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
@@ -521,9 +546,18 @@ def main():
     ap.add_argument("--workload", default="c2_moe_fp8", choices=sorted(WORKLOADS))
     ap.add_argument("--tile", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true",
-                    help="capture the K timed launches in one HIP graph and time its replay "
-                         "(launch-bound small shapes: GPU time without host launch overhead)")
+    ap.add_argument("--timing", choices=("graph", "stream"), default="graph",
+                    help="graph (default): capture the K timed launches in one HIP graph and "
+                         "time one replay, as a captured MoE layer runs them; stream: time K "
+                         "launches issued one by one on the stream.  The line reports the "
+                         "other mode's ms per step too.")
+    ap.add_argument("--graph", dest="timing", action="store_const", const="graph",
+                    help="same as --timing graph")
+    ap.add_argument("--stream", dest="timing", action="store_const", const="stream",
+                    help="same as --timing stream")
+    ap.add_argument("--single-timing", action="store_true",
+                    help="time only the chosen mode (profiling runs: every traced dispatch "
+                         "then comes from the mode the line reports)")
     ap.add_argument("--tune-report", action="store_true",
                     help="bounded autotune of every GEMM workload: time the ranker's top-k tile "
                          "configs (the library's *_tune calls), report heuristic top-1 against "
@@ -612,7 +646,9 @@ def main():
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         run(p, d, out=C, **kw)
-    ms, ms_launch = time_launches(torch, lambda: run(p, d, out=C, **kw), args.steps, args.graph)
+    ms, ms_other = time_modes(torch, lambda: run(p, d, out=C, **kw), args.steps, args.timing,
+                             args.single_timing)
+    ms_launch = ms
     rr = real_rows(p)
     flops = 2.0 * rr * N * K
     tflops = flops / (ms * 1e-3) / 1e12
@@ -632,8 +668,7 @@ def main():
                    "M": M, "N": N, "K": K, "G": G, "real_rows": rr,
                    "tile": args.tile if args.tile is not None else tiles[0]["id"],
                    "run_split": args.run_split, "max_workgroups": args.max_workgroups,
-                   "timing": "hip graph of K launches" if args.graph
-                   else "K stream launches", "parallelism": "single GPU"},
+                   "timing": TIMING[args.timing], "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops_launch, 2), "peak": PEAK[mma],
                      "unit": "TFLOP/s", "frac": round(tflops_launch / PEAK[mma], 4),
                      "traffic": traffic, "mfma_dtype": mma,
@@ -642,6 +677,8 @@ def main():
                      "us_per_launch": round(ms_launch * 1e3, 2)},
         "kernel_source_sha": src,
     }
+    out["ms_per_step_" + OTHER[args.timing]] = (None if ms_other is None
+                                                   else round(ms_other, 5))
     if kind == "fp4":
         out["roofline"]["frac_of_fp4_peak"] = round(tflops_launch / PEAK["fp4"], 4)
     if not args.no_cpu_baseline:
