@@ -28,7 +28,8 @@
 //    a zero scale), so one explicit count waits for the oldest group.
 //  * Weights are dequantised exactly to BF16 in registers (q * s has at most
 //    6 significant bits and lies in [2^-10, 2688]): the E2M1 pair convert with
-//    scale 1.0, an FP32 multiply by the block scale, a pack to BF16.  Then
+//    scale 1.0, an FP32 multiply by the block scale, and the upper halves of
+//    two exact products packed as a BF16 pair (no rounding needed).  Then
 //    v_mfma_f32_16x16x32_bf16 with FP32 accumulation: lane (r, q) of the
 //    activation operand and lane (c, q) of the weight operand hold the same
 //    eight k, so every k pairs with itself.
