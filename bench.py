@@ -563,6 +563,9 @@ def main():
                          "configs (the library's *_tune calls), report heuristic top-1 against "
                          "the best of the k, and the geomean loss; one JSON line")
     ap.add_argument("--top-k", type=int, default=4)
+    ap.add_argument("--autotune", action="store_true",
+                    help="GEMM workloads: run the library's bounded autotune of the ranker's "
+                         "top-k configs once (untimed) and time the config it records")
     ap.add_argument("--max-workgroups", type=int, default=0,
                     help="fgg_options.max_workgroups (0: one workgroup per tile)")
     ap.add_argument("--run-split", type=int, default=0,
@@ -643,6 +646,22 @@ def main():
         kw["run_split"] = args.run_split
     if args.max_workgroups:
         kw["max_workgroups"] = args.max_workgroups
+    tuned = None
+    if args.autotune and args.tile is None:
+        # the library's bounded autotune, once, untimed: later calls of this
+        # shape launch the config it recorded
+        print("[bench] autotune", file=sys.stderr, flush=True)
+        fgg.tune_clear()
+        tk = dict(top_k=args.top_k, reps=5)
+        if kind == "fp8":
+            _, tuned = fgg.grouped_fp8_gemm_tune(d["A"], d["B"], d["a_scale"], d["b_scale"],
+                                                 d["m_indices"], out=C, **tk)
+        elif p.get("m_indices") is None:
+            _, tuned = fgg.fp4_gemm_tune(d["A"], d["B"], d["a_scale"], d["b_scale"], p["alpha"],
+                                         out=C, **tk)
+        else:
+            _, tuned = fgg.grouped_fp4_gemm_tune(d["A"], d["B"], d["a_scale"], d["b_scale"],
+                                                 d["m_indices"], p["alpha"], out=C, **tk)
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         run(p, d, out=C, **kw)
@@ -666,7 +685,10 @@ def main():
         "data": "synthetic (seeded NumPy; quantised on the host, resident in HBM)",
         "config": {"workload": args.workload, "desc": WORKLOADS[args.workload]["desc"],
                    "M": M, "N": N, "K": K, "G": G, "real_rows": rr,
-                   "tile": args.tile if args.tile is not None else tiles[0]["id"],
+                   "tile": (args.tile if args.tile is not None
+                            else tuned["chosen"] if tuned else tiles[0]["id"]),
+                   "tile_choice": ("given" if args.tile is not None
+                                   else "bounded autotune" if tuned else "ranker"),
                    "run_split": args.run_split, "max_workgroups": args.max_workgroups,
                    "timing": TIMING[args.timing], "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops_launch, 2), "peak": PEAK[mma],

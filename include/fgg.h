@@ -278,14 +278,16 @@ fgg_status fp4_gemm_problems_ex(const fgg_fp4_problem* problems, int count,
  *
  * Each *_tune call takes the arguments of its GEMM (same checks, same
  * errors), times the ranker's best min(top_k, FGG_TUNE_MAX) tile configs on
- * those inputs -- one untimed launch, then `reps` launches between two HIP
- * events on `stream`, per config -- and records the fastest for (kind, M, N,
- * K, G) on the current device.  Later calls of that GEMM on that shape with
+ * those inputs and records the fastest for (kind, M, N, K, G) on the current
+ * device.  Timing: three rounds that visit the configs in turn, each visit
+ * one untimed launch and then `reps` launches between two HIP events on
+ * `stream`; a config's time is its fastest round (so no config pays for the
+ * clock ramp of a GPU coming out of idle, whatever its place in the order).  Later calls of that GEMM on that shape with
  * no explicit tile_id launch the recorded config instead of the ranker's
  * top one.  C is overwritten (with the GEMM's result).  The call
  * synchronises `stream` and is not graph-capturable; it allocates no device
  * memory.  `report` (may be NULL) receives the candidates in ranker order
- * with their mean milliseconds per launch.  Recorded choices are process-wide
+ * with their milliseconds per launch.  Recorded choices are process-wide
  * and thread-safe; fgg_tune_clear() forgets them all.
  * ------------------------------------------------------------------------ */
 #define FGG_TUNE_MAX 8
@@ -293,7 +295,7 @@ fgg_status fp4_gemm_problems_ex(const fgg_fp4_problem* problems, int count,
 typedef struct {
   int n;                      /* candidates timed                              */
   int tile_id[FGG_TUNE_MAX];  /* ranker order: tile_id[0] is the heuristic's   */
-  float ms[FGG_TUNE_MAX];     /* mean time per launch                          */
+  float ms[FGG_TUNE_MAX];     /* time per launch, fastest of the three rounds  */
   int best;                   /* index (into tile_id / ms) of the fastest      */
 } fgg_tune_report;
 
