@@ -92,7 +92,7 @@ __device__ __forceinline__ i32x8 read_frag(const uint8_t* tile, int row0, int la
 
 using namespace lds_dma;
 
-// Per-pass state: buffer resources, offsets, next scales, accumulators.
+// Per-pass state: buffer resources, offsets, the b_scale row, accumulators.
 //  * A/B staging: a tile row is K bytes for both operands; lane l of a
 //    1 KB load writes LDS bytes [16 l, 16 l + 16) = tile row 8 b + l / 8,
 //    physical chunk l % 8, so it fetches logical chunk (l % 8) ^ (row % 8).
