@@ -71,6 +71,9 @@ WORKLOADS = {
                      desc="BF16 -> FP8 1x128 activations of c2, M=8192, K=7168"),
     "q_nvfp4_c5": dict(kind="quant_nvfp4", M=65536, K=8192,
                        desc="BF16 -> NVFP4 activations of c5, M=65536, K=8192"),
+    "q_nvfp4_static_c5": dict(kind="quant_nvfp4_static", M=65536, K=8192,
+                              desc="BF16 -> NVFP4 activations of c5 with a calibrated global "
+                                   "scale (amax of the first 64 rows / 2688), M=65536, K=8192"),
 }
 QUANT_METRIC = "GB/s (algorithmic bytes / time) and % of HBM peak, activation quantiser"
 
@@ -83,6 +86,7 @@ KERNEL_SOURCES = {
     "fp4_problems": ("fp4.hip", "common.h"),
     "quant_fp8": ("quant.hip", "common.h"),
     "quant_nvfp4": ("quant.hip", "common.h"),
+    "quant_nvfp4_static": ("quant.hip", "common.h"),
     "w4a16": ("w4a16.hip", "common.h"),
 }
 
@@ -239,10 +243,13 @@ def rocprof_summary(root: str, workload: str, kernel: str, command: str) -> str:
 
 def quant_bytes(kind: str, M: int, K: int) -> int:
     """Bytes a quantiser launch must move at least once: read X (BF16), write
-    the codes and the scales.  The NVFP4 path reads X twice (the global
-    amax comes before any code); the second read is not counted."""
+    the codes and the scales.  The dynamic NVFP4 path reads X twice (the
+    global amax comes before any code); the second read is not counted.  The
+    static one (a given global scale) reads X once and writes no scale."""
     if kind == "quant_fp8":
         return M * K * 2 + M * K + M * (K // 128) * 4
+    if kind == "quant_nvfp4_static":
+        return M * K * 2 + M * K // 2 + M * (K // 16)
     return M * K * 2 + M * K // 2 + M * (K // 16) + 4
 
 
@@ -296,8 +303,13 @@ def bench_quant(args, torch):
     rng = np.random.default_rng(0)
     X = torch.from_numpy(rng.standard_normal((M, K), dtype=np.float32)).to(torch.bfloat16)
     Xd = X.cuda()
-    run = (lambda: fgg.quantize_fp8_1x128(Xd)) if kind == "quant_fp8" else \
-        (lambda: fgg.quantize_nvfp4(Xd))
+    g_static = float(X[:64].float().abs().max()) / 2688.0  # a calibration on the first rows
+    if kind == "quant_fp8":
+        run = lambda: fgg.quantize_fp8_1x128(Xd)
+    elif kind == "quant_nvfp4_static":
+        run = lambda: fgg.quantize_nvfp4(Xd, global_scale=g_static)
+    else:
+        run = lambda: fgg.quantize_nvfp4(Xd)
     for _ in range(args.warmup):
         out = run()
     ms, ms_other = time_modes(torch, run, args.steps, args.timing, args.single_timing)

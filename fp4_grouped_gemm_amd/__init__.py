@@ -83,6 +83,7 @@ def load_library():
         ("grouped_fp4_gemm_ex", [P, P, P, P, P, F, P, I, I, I, I, OPT, P]),
         ("quantize_fp8_1x128", [P, P, P, I, I, P]),
         ("quantize_nvfp4", [P, P, P, P, I, I, P]),
+        ("quantize_nvfp4_static", [P, P, P, F, I, I, P]),
         ("grouped_fp4_gemm_alpha", [P, P, P, P, P, P, P, I, I, I, I, P]),
         ("grouped_fp4_gemm_alpha_ex", [P, P, P, P, P, P, P, I, I, I, I, OPT, P]),
         ("fp4_gemm_problems", [ctypes.POINTER(_Fp4Problem), I, P]),
@@ -444,19 +445,29 @@ def quantize_fp8_1x128(X, stream=None):
     return Q, S
 
 
-def quantize_nvfp4(X, stream=None):
+def quantize_nvfp4(X, stream=None, global_scale=None):
     """BF16 activations [M, K] -> (packed E2M1 uint8 [M, K/2], E4M3FN scale
     codes uint8 [M, K/16], FP32 global scale as a 1-element device tensor):
     the A operand of fp4_gemm / grouped_fp4_gemm, whose alpha is this global
-    scale times B's (C ABI quantize_nvfp4; no host synchronisation)."""
+    scale times B's (C ABI quantize_nvfp4; no host synchronisation).
+
+    global_scale: None computes g = amax(X) / 2688 on the device; a Python
+    float is a calibrated, static g (C ABI quantize_nvfp4_static: one pass
+    over X, block amaxes above 448 * 6 * g saturate)."""
     torch = _torch()
     lib = load_library()
     X = _bf16_matrix(X)
     M, K = X.shape
     Q = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
     S = torch.empty((M, max(K // 16, 1)), dtype=torch.uint8, device=X.device)
-    g = torch.empty((1,), dtype=torch.float32, device=X.device)
     with torch.cuda.device(X.device):
-        _check(lib.quantize_nvfp4(X.data_ptr(), Q.data_ptr(), S.data_ptr(), g.data_ptr(), M, K,
-                                  _stream_ptr(stream, X.device)))
+        if global_scale is None:
+            g = torch.empty((1,), dtype=torch.float32, device=X.device)
+            _check(lib.quantize_nvfp4(X.data_ptr(), Q.data_ptr(), S.data_ptr(), g.data_ptr(),
+                                      M, K, _stream_ptr(stream, X.device)))
+        else:
+            gs = float(global_scale)
+            _check(lib.quantize_nvfp4_static(X.data_ptr(), Q.data_ptr(), S.data_ptr(), gs, M, K,
+                                             _stream_ptr(stream, X.device)))
+            g = torch.full((1,), gs, dtype=torch.float32, device=X.device)
     return Q, S, g

@@ -581,4 +581,21 @@ fgg_status quantize_nvfp4(const void* X, void* Q, void* scale, float* global_sca
                                               static_cast<hipStream_t>(stream)));
 }
 
+fgg_status quantize_nvfp4_static(const void* X, void* Q, void* scale, float global_scale, int M,
+                                 int K, void* stream) {
+  const char* fn = "quantize_nvfp4_static";
+  fgg_status st = check_quant(fn, X, Q, scale, M, K, 1);
+  if (st != FGG_OK) return st;
+  if (!std::isfinite(global_scale) || !(global_scale >= std::numeric_limits<float>::min()))
+    return fail(FGG_EINVAL, fn, "global_scale must be a finite normal positive float, got %g",
+                (double)global_scale);
+  const DeviceFacts* d = current_device(fn, &st);
+  if (!d) return st;
+  return launched(fn, fgg::launch_quant_nvfp4_static(static_cast<const uint16_t*>(X),
+                                                     static_cast<uint8_t*>(Q),
+                                                     static_cast<uint8_t*>(scale), global_scale, M,
+                                                     K, d->num_cus,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

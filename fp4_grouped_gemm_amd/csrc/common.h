@@ -107,6 +107,8 @@ hipError_t launch_quant_fp8(const uint16_t* X, uint8_t* Q, float* scale, int M, 
                             int num_cus, hipStream_t s);
 hipError_t launch_quant_nvfp4(const uint16_t* X, uint8_t* Q, uint8_t* S, float* g, int M, int K,
                               int num_cus, hipStream_t s);
+hipError_t launch_quant_nvfp4_static(const uint16_t* X, uint8_t* Q, uint8_t* S, float g, int M,
+                                     int K, int num_cus, hipStream_t s);
 
 // --------------------------------------------------------- device helpers
 #ifdef __HIPCC__

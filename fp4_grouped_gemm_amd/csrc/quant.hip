@@ -175,9 +175,10 @@ __global__ __launch_bounds__(kQThreads) void quant_nvfp4_kernel(const uint16_t* 
                                                                 uint8_t* __restrict__ Q,
                                                                 uint8_t* __restrict__ S,
                                                                 const uint32_t* amax_bits,
-                                                                long long nblocks) {
+                                                                float g_given, long long nblocks) {
   const int lane = threadIdx.x & 63;
-  const float g = global_scale(amax_bits[0]);
+  // the global scale: from the amax pass, or given by the caller (static)
+  const float g = amax_bits ? global_scale(amax_bits[0]) : g_given;
   const float g6 = 6.0f * g;
   const long long waves = (long long)gridDim.x * (kQThreads / 64);
   const long long pieces = nblocks / 2;  // nblocks is even (K % 128 == 0)
@@ -247,8 +248,19 @@ hipError_t launch_quant_nvfp4(const uint16_t* X, uint8_t* Q, uint8_t* S, float* 
                      s, X, n8, gb);
   const long long nblocks = n / 16;
   hipLaunchKernelGGL(quant_nvfp4_kernel, dim3(grid_for((nblocks / 2 + 63) / 64, num_cus, 16)),
-                     dim3(kQThreads), 0, s, X, Q, S, (const uint32_t*)gb, nblocks);
+                     dim3(kQThreads), 0, s, X, Q, S, (const uint32_t*)gb, 0.0f, nblocks);
   hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1), 0, s, gb);
+  return hipGetLastError();
+}
+
+// With a global scale given by the caller: the encode pass only (one read of X).
+hipError_t launch_quant_nvfp4_static(const uint16_t* X, uint8_t* Q, uint8_t* S, float g, int M,
+                                     int K, int num_cus, hipStream_t s) {
+  const long long n = (long long)M * K;
+  if (n <= 0) return hipSuccess;
+  const long long nblocks = n / 16;
+  hipLaunchKernelGGL(quant_nvfp4_kernel, dim3(grid_for((nblocks / 2 + 63) / 64, num_cus, 16)),
+                     dim3(kQThreads), 0, s, X, Q, S, (const uint32_t*)nullptr, g, nblocks);
   return hipGetLastError();
 }
 

@@ -197,6 +197,12 @@ fgg_status grouped_w4a16_gemm(const void* A, const void* B, const void* b_scale,
  * value(s) g is 0.  Four kernel launches on `stream` (clear, amax, encode,
  * finalise); no host synchronisation, no allocation.
  *
+ * quantize_nvfp4_static -- the same encoding with the global scale g given by
+ * the caller (a calibrated, static activation scale) instead of amax(X) /
+ * 2688: one kernel launch that reads X once.  Values whose block amax exceeds
+ * 448 * 6 * g saturate (block scale 448, codes clamped to +-6).  g must be a
+ * finite normal positive float (FGG_EINVAL otherwise).
+ *
  * Requirements: X, Q 16-byte aligned (scale: 4-byte for FP8, any for NVFP4;
  * global_scale 4-byte); 1 <= M <= 2^24; 128 <= K <= 2^20, K % 128 == 0; X
  * finite.  Errors as for the GEMMs.
@@ -204,6 +210,8 @@ fgg_status grouped_w4a16_gemm(const void* A, const void* B, const void* b_scale,
 fgg_status quantize_fp8_1x128(const void* X, void* Q, float* scale, int M, int K, void* stream);
 fgg_status quantize_nvfp4(const void* X, void* Q, void* scale, float* global_scale, int M, int K,
                           void* stream);
+fgg_status quantize_nvfp4_static(const void* X, void* Q, void* scale, float global_scale, int M,
+                                 int K, void* stream);
 
 /* ------------------------------------------------------------------------
  * Tile configurations and the ranker.

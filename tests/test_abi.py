@@ -85,6 +85,11 @@ def test_quantizer_validation():
     assert st == 1 and "global_scale" in lib.fgg_last_error().decode()
     assert lib.quantize_nvfp4(P, P, P, P + 2, 8, 256, None) == 2
     assert lib.quantize_nvfp4(P, P + 8, P, P, 8, 256, None) == 2
+    assert lib.quantize_nvfp4_static(P, P, P, 1.0, 8, 200, None) == 1
+    assert lib.quantize_nvfp4_static(P, P + 8, P, 1.0, 8, 256, None) == 2
+    for g in (0.0, -1.0, float("nan"), float("inf"), 1e-40):
+        st = lib.quantize_nvfp4_static(P, P, P, g, 8, 256, None)
+        assert st == 1 and "global_scale" in lib.fgg_last_error().decode()
 
 
 def test_tune_validation_and_cache_without_gpu():

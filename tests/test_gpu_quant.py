@@ -75,6 +75,42 @@ def test_nvfp4_bitwise(case):
     assert np.array_equal(Q, q_ref), (case, int((Q != q_ref).sum()))
 
 
+STATIC_G = {
+    "dynamic": None,       # g = amax / 2688, as the dynamic quantiser takes it
+    "saturating": 1 / 64,  # the dynamic g / 64: large blocks clamp at s = 448, codes at 6
+    "odd": 0.7654321,      # not a power of two
+    "min_normal": float(np.finfo(np.float32).tiny),  # every nonzero block saturates
+    "huge": 1e30,          # most blocks underflow to s = 0 and zero codes
+}
+
+
+@pytest.mark.parametrize("gname", sorted(STATIC_G))
+@pytest.mark.parametrize("case", ["ragged_rows", "heavy_tail", "one_row", "odd_segments"])
+def test_nvfp4_static_scale_bitwise(case, gname):
+    """The given-global-scale quantiser against the oracle with that g."""
+    import torch
+    import fp4_grouped_gemm_amd as fgg
+    M, K, sc, dist = CASES[case]
+    x, t = _bf16(np.random.default_rng(300 + sorted(CASES).index(case)), M, K, sc, dist)
+    x[0, 16:48] = 0.0
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    g_dyn = oq.quantize_nvfp4(x)[2]
+    g = STATIC_G[gname]
+    g = float(g_dyn) if g is None else (float(g_dyn) * g if gname == "saturating" else g)
+    log(f"quantize_nvfp4_static {case} g={gname} M={M} K={K}")
+    Q, S, gt = fgg.quantize_nvfp4(t.cuda(), global_scale=g)
+    Q, S = Q.cpu().numpy(), S.cpu().numpy()
+    q_ref, s_ref, g_ref = oq.quantize_nvfp4(x, g)
+    assert np.float32(gt.cpu().numpy()[0]) == g_ref
+    assert np.array_equal(S, s_ref), (case, gname, int((S != s_ref).sum()))
+    assert np.array_equal(Q, q_ref), (case, gname, int((Q != q_ref).sum()))
+    if gname == "dynamic":  # same g, same bits as the amax-pass quantiser
+        Qd, Sd, _ = _gpu_nvfp4(t)
+        assert np.array_equal(Q, Qd) and np.array_equal(S, Sd)
+    if gname == "saturating":
+        assert (s_ref == 0x7E).any()  # the clamp was reached (E4M3FN 448)
+
+
 def test_every_bf16_value_through_fp8():
     """Every finite BF16 bit pattern as an element next to a block maximum
     of 448 (scale 1.0): each code is the E4M3FN rounding of the value itself
