@@ -57,6 +57,29 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// x / d rounded to nearest even -- the IEEE quotient -- from r = 1 / d (an
+// IEEE division, once per block): q = x r, then two residual corrections
+// q += fma(-d, q, x) r.  The first brings q within one ulp of x / d; from
+// there, with r the correctly rounded reciprocal and no underflow or
+// overflow, one correction gives the correctly rounded quotient (Markstein's
+// theorem).  Callers take this path only when 2^-64 <= d <= 2^64 and every
+// quotient is at most 2^64: the residuals of quotients above 2^-40 are then
+// normal numbers; smaller quotients may come out a little off, but every
+// value below 2^-11 encodes to zero in both formats, and the sign is taken
+// from x (so -0 stays -0).  A multiply, four multiply-adds and a sign copy
+// per value instead of the eleven-instruction division sequence, which had
+// made these encoders ALU-bound.
+__device__ __forceinline__ float div_rn(float x, float d, float r) {
+  float q = x * r;
+  q = fmaf(fmaf(-d, q, x), r, q);
+  q = fmaf(fmaf(-d, q, x), r, q);
+  return __builtin_copysignf(q, x);
+}
+// d and the block maximum a allow div_rn for every value of the block
+__device__ __forceinline__ bool div_rn_ok(float d, float a) {
+  return d >= 0x1p-64f && d <= 0x1p64f && a <= d * 0x1p64f;
+}
+
 // Both encoders give each lane 32 consecutive values (four 16-byte loads in
 // flight per lane, whole 16-byte code stores) and a wave 2048; the 32-value
 // pieces are independent of the rows, as blocks never cross a row.  Lanes
@@ -85,17 +108,29 @@ __global__ __launch_bounds__(kQThreads) void quant_fp8_kernel(const uint16_t* __
       for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[u][i]));
     const float amax = group_max<4>(a);
     const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+    float(&y)[4][8] = v;  // the quotients replace the values
+    if (__builtin_expect(div_rn_ok(s, amax), 1)) {
+      const float r = 1.0f / s;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[u][i] = div_rn(v[u][i], s, r);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[u][i] = v[u][i] / s;
+    }
     u32x4 out[2];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      float y[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(v[u][i] / s, -448.0f), 448.0f);
+      for (int i = 0; i < 8; ++i) y[u][i] = fminf(fmaxf(y[u][i], -448.0f), 448.0f);
       // bytes 0,1 then 2,3 of each word, in value order
-      uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-      lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo, true);
-      uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-      hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)hi, true);
+      uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[u][0], y[u][1], 0, false);
+      lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[u][2], y[u][3], (int)lo, true);
+      uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[u][4], y[u][5], 0, false);
+      hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[u][6], y[u][7], (int)hi, true);
       out[u >> 1][2 * (u & 1)] = lo;
       out[u >> 1][2 * (u & 1) + 1] = hi;
     }
@@ -153,21 +188,44 @@ __device__ __forceinline__ float global_scale(uint32_t amax_bits) {
   return amax > 0.f ? amax / 2688.0f : 1.0f;
 }
 
-// 8 values -> 8 E2M1 codes (element 2j in the low nibble of byte j), given
-// the block's decode scale d (all zero codes when d is 0).
-__device__ __forceinline__ uint32_t e2m1x8(const float v[8], float d) {
+// 8 quotients x / d -> 8 E2M1 codes (element 2j in the low nibble of byte j).
+__device__ __forceinline__ uint32_t e2m1x8(const float y[8]) {
   uint32_t packed = 0;
-  if (d > 0.f) {
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const float y0 = fminf(fmaxf(v[i] / d, -6.0f), 6.0f);
-      const float y1 = fminf(fmaxf(v[i + 1] / d, -6.0f), 6.0f);
-      const uint32_t two =
-          (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0, y0, y1, 1.0f, 0) & 0xFFu;
-      packed |= two << (4 * i);
-    }
+  for (int i = 0; i < 8; i += 2) {
+    const float y0 = fminf(fmaxf(y[i], -6.0f), 6.0f);
+    const float y1 = fminf(fmaxf(y[i + 1], -6.0f), 6.0f);
+    const uint32_t two =
+        (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0, y0, y1, 1.0f, 0) & 0xFFu;
+    packed |= two << (4 * i);
   }
   return packed;
+}
+
+// The 16 codes of a block (two words) from its values and decode scale d:
+// all zero when d is 0.
+__device__ __forceinline__ void e2m1_block(const float v0[8], const float v1[8], float d,
+                                           float a, uint32_t& c0, uint32_t& c1) {
+  c0 = c1 = 0;
+  if (d > 0.f) {
+    float y0[8], y1[8];
+    if (__builtin_expect(div_rn_ok(d, a), 1)) {
+      const float r = 1.0f / d;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        y0[i] = div_rn(v0[i], d, r);
+        y1[i] = div_rn(v1[i], d, r);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        y0[i] = v0[i] / d;
+        y1[i] = v1[i] / d;
+      }
+    }
+    c0 = e2m1x8(y0);
+    c1 = e2m1x8(y1);
+  }
 }
 
 // A lane holds two whole 16-value blocks: no cross-lane reduction.
@@ -200,8 +258,10 @@ __global__ __launch_bounds__(kQThreads) void quant_nvfp4_kernel(const uint16_t* 
       const uint32_t s_code =
           (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s_in, 0.f, 0, false) & 0xFFu;
       const float d = __builtin_amdgcn_cvt_f32_fp8((int)s_code, 0) * g;
-      codes[2 * b] = e2m1x8(v[2 * b], d);
-      codes[2 * b + 1] = e2m1x8(v[2 * b + 1], d);
+      uint32_t c0, c1;
+      e2m1_block(v[2 * b], v[2 * b + 1], d, a, c0, c1);
+      codes[2 * b] = c0;
+      codes[2 * b + 1] = c1;
       sc |= s_code << (8 * b);
     }
     if (w * 64 + lane < pieces) {

@@ -134,6 +134,62 @@ def test_every_bf16_value_through_fp8():
     assert np.array_equal(Q, q_ref), int((Q != q_ref).sum())
 
 
+def _bf16_values(limit):
+    """Every finite BF16 value of magnitude <= limit, as float32."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    v = (bits << 16).view(np.float32)
+    return v[np.isfinite(v) & (np.abs(v) <= limit)]
+
+
+@pytest.mark.parametrize("lead", [613.0, 301.0, 1.7e-5, 3.3e20])
+def test_every_bf16_value_through_fp8_odd_scale(lead):
+    """Every BF16 value up to a block maximum whose scale (lead / 448) is not
+    a power of two: each code follows the IEEE quotient x / scale."""
+    import torch
+    lead = float(torch.tensor(lead).to(torch.bfloat16).float())
+    v = _bf16_values(lead)
+    n = -(-v.size // 127) * 127
+    vals = np.zeros(n, np.float32)
+    vals[:v.size] = v
+    x = np.concatenate([np.full((n // 127, 1), lead, np.float32), vals.reshape(-1, 127)], axis=1)
+    x = x.reshape(-1, 128)
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    assert np.array_equal(t.float().numpy(), x)
+    log(f"every bf16 value through fp8, block max {lead}: {v.size} values")
+    Q, S = _gpu_fp8(t)
+    q_ref, s_ref = oq.quantize_fp8_1x128(x)
+    assert np.array_equal(S.view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(Q, q_ref), int((Q != q_ref).sum())
+
+
+@pytest.mark.parametrize("g", [0.7654321, 3.1e-7, 1.3e9])
+def test_every_bf16_value_through_nvfp4_odd_scale(g):
+    """Every BF16 value up to 6 * 448 * g in blocks led by values that give
+    scale codes of every size, with a static global scale that is not a power
+    of two: each code follows the IEEE quotient x / (value(s) g)."""
+    import torch
+    import fp4_grouped_gemm_amd as fgg
+    g = float(np.float32(g))
+    v = _bf16_values(6 * 448 * g)
+    rng = np.random.default_rng(7)
+    leads = np.abs(rng.choice(v, size=-(-v.size // 15)))
+    n = leads.size * 15
+    vals = np.zeros(n, np.float32)
+    vals[:v.size] = v
+    blocks = vals.reshape(-1, 15)
+    blocks = np.clip(blocks, -leads[:, None], leads[:, None])  # the lead is the block maximum
+    x = np.concatenate([leads[:, None].astype(np.float32), blocks], axis=1)
+    rows = -(-x.shape[0] // 8)
+    x = np.concatenate([x, np.zeros((rows * 8 - x.shape[0], 16), np.float32)]).reshape(rows, 128)
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    assert np.array_equal(t.float().numpy(), x)
+    log(f"every bf16 value through nvfp4, static g {g}: {x.size} values")
+    Q, S, _ = fgg.quantize_nvfp4(t.cuda(), global_scale=g)
+    q_ref, s_ref, _ = oq.quantize_nvfp4(x, g)
+    assert np.array_equal(S.cpu().numpy(), s_ref)
+    assert np.array_equal(Q.cpu().numpy(), q_ref), int((Q.cpu().numpy() != q_ref).sum())
+
+
 def test_every_fp4_rounding_case():
     """Values on a 1/64 grid through [-6.5, 6.5], each 16-block led by 6.0,
     with the tensor maximum 2688: g = 1, every such block gets s = 1.0 and
