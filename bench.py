@@ -12,7 +12,9 @@ one HIP graph and the timed region is one replay of it (after an untimed
 replay), the way a captured MoE layer runs them; --stream times K launches
 issued one by one instead.  The line carries the other mode's figure too
 (ms_per_step_stream or ms_per_step_graph), timed second in the same
-process.  Prints one JSON line.
+process, and `cold_cache`: the median of single launches, each after a read
+of 512 MB that evicts L2 and the last-level cache, beside the median of the
+same single launches warm.  Prints one JSON line.
 
 Default workload: grouped FP8 MoE prefill, G=8, M=8192 routed rows in sorted
 runs (multinomial counts, unaligned to 128), N=4096, K=7168.
@@ -30,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -261,6 +264,53 @@ def time_modes(torch, call, steps: int, timing: str, single: bool = False):
     return ms, other
 
 
+FLUSH_BYTES = 512 << 20  # twice the 256 MB last-level cache
+
+
+def cold_cache_timing(torch, call, launches: int):
+    """Per-launch times with cold caches: before each launch a 512 MB buffer
+    is read (a sum), which leaves L2 and the last-level cache holding other,
+    clean lines -- an overwrite instead would leave dirty lines whose
+    write-back lands in the timed launch -- then HIP events on the current
+    stream bracket that one launch.  Returns (median ms cold, median ms of
+    the same loop without the flush).  Each launch stands alone here, so even
+    the warm figure includes the launch ramp that the back-to-back timing of
+    `time_launches` spreads over many launches."""
+    stream = torch.cuda.current_stream()
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+
+    def median_ms(do_flush: bool) -> float:
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(ev):
+            if do_flush:
+                flush.sum()
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) for a, b in ev)
+
+    cold = median_ms(True)
+    warm = median_ms(False)
+    del flush
+    return cold, warm
+
+
+def cold_cache_entry(torch, call, args, work: float, unit: str, scale: float):
+    """The `cold_cache` object of a result line: `work` units per launch,
+    reported as work / seconds * scale in `unit` (None when switched off)."""
+    if args.cold_launches <= 0 or args.single_timing:
+        return None
+    print("[bench] cold-cache launches", file=sys.stderr, flush=True)
+    cold, warm = cold_cache_timing(torch, call, args.cold_launches)
+    return {"launches": args.cold_launches, "flush_bytes": FLUSH_BYTES,
+            "ms_median": round(cold, 5), "value": round(work / (cold * 1e-3) * scale, 2),
+            "warm_ms_median": round(warm, 5),
+            "warm_value": round(work / (warm * 1e-3) * scale, 2), "unit": unit}
+
+
 def time_launches(torch, call, steps: int, graph: bool = False):
     """Time `steps` calls of `call` (each one kernel launch) on the current
     stream, with HIP events recorded on that stream around the timed region
@@ -314,6 +364,7 @@ def bench_quant(args, torch):
         out = run()
     ms, ms_other = time_modes(torch, run, args.steps, args.timing, args.single_timing)
     ms_launch = ms
+    cold = cold_cache_entry(torch, run, args, quant_bytes(kind, M, K), "GB/s", 1e-9)
     out = run()
     torch.cuda.synchronize()
     nbytes = quant_bytes(kind, M, K)
@@ -334,6 +385,7 @@ def bench_quant(args, torch):
     }
     res["ms_per_step_" + OTHER[args.timing]] = (None if ms_other is None
                                                    else round(ms_other, 5))
+    res["cold_cache"] = cold
     if not args.no_cpu_baseline:
         import oracle.quant as oq
         from threadpoolctl import threadpool_info
@@ -399,6 +451,7 @@ def bench_w4a16(args, torch):
     ms, ms_other = time_modes(torch, call, args.steps, args.timing, args.single_timing)
     ms_launch = ms
     nbytes = w4a16_bytes(p)
+    cold = cold_cache_entry(torch, call, args, nbytes, "GB/s", 1e-9)
     gbps = nbytes / (ms * 1e-3) / 1e9
     gbps_launch = nbytes / (ms_launch * 1e-3) / 1e9
     res = {
@@ -418,6 +471,7 @@ def bench_w4a16(args, torch):
     }
     res["ms_per_step_" + OTHER[args.timing]] = (None if ms_other is None
                                                    else round(ms_other, 5))
+    res["cold_cache"] = cold
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_info
         print("[bench] cpu baseline (oracle, every row)", file=sys.stderr, flush=True)
@@ -459,6 +513,8 @@ def bench_problems(args, torch):
                               args.steps, args.timing, args.single_timing)
     ms_launch = ms
     flops = sum(2.0 * q["M"] * q["N"] * q["K"] for q in probs)
+    cold = cold_cache_entry(torch, lambda: fgg.fp4_gemm_problems(batch, outs, **kw), args, flops,
+                            "TFLOPS", 1e-12)
     tflops = flops / (ms * 1e-3) / 1e12
     tflops_launch = flops / (ms_launch * 1e-3) / 1e12
     out = {
@@ -479,6 +535,7 @@ def bench_problems(args, torch):
     }
     out["ms_per_step_" + OTHER[args.timing]] = (None if ms_other is None
                                                    else round(ms_other, 5))
+    out["cold_cache"] = cold
     if not args.no_cpu_baseline:
         # the oracle on the first rows of every problem, in turn, until the budget
         print("[bench] cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
@@ -567,9 +624,12 @@ def main():
                     help="same as --timing graph")
     ap.add_argument("--stream", dest="timing", action="store_const", const="stream",
                     help="same as --timing stream")
+    ap.add_argument("--cold-launches", type=int, default=20,
+                    help="also time this many single launches with the caches flushed before "
+                         "each (a 512 MB read) and report their median as cold_cache (0: skip)")
     ap.add_argument("--single-timing", action="store_true",
-                    help="time only the chosen mode (profiling runs: every traced dispatch "
-                         "then comes from the mode the line reports)")
+                    help="time only the chosen mode, with no cold-cache launches (profiling "
+                         "runs: every traced dispatch then comes from the mode the line reports)")
     ap.add_argument("--tune-report", action="store_true",
                     help="bounded autotune of every GEMM workload: time the ranker's top-k tile "
                          "configs (the library's *_tune calls), report heuristic top-1 against "
@@ -682,6 +742,7 @@ def main():
     ms_launch = ms
     rr = real_rows(p)
     flops = 2.0 * rr * N * K
+    cold = cold_cache_entry(torch, lambda: run(p, d, out=C, **kw), args, flops, "TFLOPS", 1e-12)
     tflops = flops / (ms * 1e-3) / 1e12
     tflops_launch = flops / (ms_launch * 1e-3) / 1e12
     mma = "fp8" if kind == "fp8" else "fp16"
@@ -713,6 +774,7 @@ def main():
     }
     out["ms_per_step_" + OTHER[args.timing]] = (None if ms_other is None
                                                    else round(ms_other, 5))
+    out["cold_cache"] = cold
     if kind == "fp4":
         out["roofline"]["frac_of_fp4_peak"] = round(tflops_launch / PEAK["fp4"], 4)
     if not args.no_cpu_baseline:
