@@ -624,7 +624,7 @@ def main():
                     help="same as --timing graph")
     ap.add_argument("--stream", dest="timing", action="store_const", const="stream",
                     help="same as --timing stream")
-    ap.add_argument("--cold-launches", type=int, default=20,
+    ap.add_argument("--cold-launches", type=int, default=50,
                     help="also time this many single launches with the caches flushed before "
                          "each (a 512 MB read) and report their median as cold_cache (0: skip)")
     ap.add_argument("--single-timing", action="store_true",
