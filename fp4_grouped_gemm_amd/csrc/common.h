@@ -149,7 +149,10 @@ __device__ __forceinline__ void map_tile(int id, int total, int num_windows, int
 // and the launch lasts as long as that workgroup.  Each workgroup therefore
 // marks these windows (two reads of m_indices per window, into an LDS
 // bitmask) and orders their tiles first: with at most gridDim.x of them,
-// no workgroup gets two.  Each class keeps the XCD-aware order of map_tile.
+// no workgroup gets two.  Each class keeps the XCD-aware order of map_tile;
+// the heavy windows lie far apart in M (often under different experts), so
+// their class goes one window at a time: the tiles an XCD runs together
+// then share an A window instead of touching several windows and experts.
 // Windows beyond kPlanWindows (large M: many tiles per workgroup, where the
 // order matters little) are not planned.  Only the order depends on this
 // estimate; which experts a tile processes is decided from all its rows.
@@ -209,7 +212,7 @@ __device__ __forceinline__ void plan_tile(const uint32_t* bits, int heavy, int i
   const int th = heavy * num_ntiles;
   int cw;
   if (id < th) {
-    map_tile(id, th, heavy, num_ntiles, group_w, cw, ntile);
+    map_tile(id, th, heavy, num_ntiles, 1, cw, ntile);
     window = nth_window(bits, num_windows, cw, true);
   } else {
     map_tile(id - th, total - th, num_windows - heavy, num_ntiles, group_w, cw, ntile);

@@ -431,8 +431,11 @@ hipError_t launch_cfg(const Fp8Args& a, const LaunchOpts& o, hipStream_t s) {
   int grid = (int)(total * split);
   if (o.max_wg > 0 && o.max_wg < grid) grid = o.max_wg;
   // Row windows per tile group (all column tiles of a group run in one XCD,
-  // window fastest): 8 windows measured best on MI355X for the MoE shapes.
-  const int group_w = 8;
+  // window fastest).  4 windows: a model of each XCD's L2 over the tiles in
+  // flight put c2's L2 misses at 770 MB against 1090 MB with 8 (it matches
+  // the measured 1.23 GB and 50% hit rate of that order); measured c2 +3%,
+  // c3 +1% on MI355X.
+  const int group_w = 4;
   hipLaunchKernelGGL(fp8_grouped_kernel<T>, dim3(grid), dim3(T::THREADS), 0, s, a.A, a.B,
                      a.a_scale, a.b_scale, a.m_indices, a.C, a.M, a.N, a.K, a.G, num_windows,
                      num_ntiles, (int)total, group_w, split);
