@@ -223,6 +223,20 @@ def rocprof_summary(root: str, workload: str, kernel: str, command: str) -> str:
         f"dispatches traced: {len(durs)}; mean duration {mean(durs):.2f} us; "
         f"min {min(durs) if durs else float('nan'):.2f} us; max {max(durs) if durs else float('nan'):.2f} us",
     ]
+    # The profiled run's own result line (its stdout, saved beside the CSVs):
+    # its timed region is the last `steps` dispatches of the kernel.
+    run = None
+    log = os.path.join(root, "trace.log")
+    if os.path.exists(log):
+        with open(log) as fh:
+            for line in fh:
+                if line.startswith('{"metric"'):
+                    run = json.loads(line)
+    if run and durs:
+        k = min(int(run["steps"]), len(durs))
+        lines.append(f"timed region of that run (its last {k} dispatches): mean "
+                     f"{mean(durs[-k:]):.2f} us; the run's own line: "
+                     f"{run['roofline']['us_per_launch']} us per step")
     for r in stats:
         lines.append("kernel_stats: " + ", ".join(f"{k}={v}" for k, v in r.items()))
     lines += [
