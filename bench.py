@@ -52,7 +52,8 @@ OTHER = {"graph": "stream", "stream": "graph"}
 WORKLOADS = {
     "c2_moe_fp8": dict(kind="fp8", desc="grouped FP8 MoE prefill, G=8, M=8192, N=4096, K=7168"),
     "c3_skewed_fp8": dict(kind="fp8", desc="skewed grouped FP8, G=32 Zipf(1.2), M=16384 incl. "
-                          "padding, N=2048, K=7168"),
+                          "padding, N=2048, K=7168; runs padded to 128 rows",
+                          run_align=128),
     "c4_dense_nvfp4": dict(kind="fp4", desc="dense NVFP4, M=2048, N=36864, K=4608"),
     "c5_moe_nvfp4": dict(kind="fp4", desc="grouped NVFP4 W4A4 MoE prefill, G=8x8192 rows, "
                          "N=8192, K=8192"),
@@ -611,6 +612,16 @@ def tune_report(args, torch):
         rows.append(dict(workload=name, candidates=rep["tile_id"],
                          us=[round(1e3 * t, 2) for t in rep["ms"]], heuristic=rep["tile_id"][0],
                          best=rep["chosen"], heuristic_loss=round(heur / best - 1.0, 4)))
+        align = w.get("run_align", 0)
+        if align:
+            # the ranker's pick under the workload's run-alignment promise
+            top = fgg.rank_tiles(fgg.FP8 if p["kind"] == "fp8" else fgg.FP4, p["M"], p["N"],
+                                 p["K"], p["G"], num_cus=fgg.device_info()["num_cus"],
+                                 run_align=align)[0]["id"]
+            if top in rep["tile_id"]:
+                t = rep["ms"][rep["tile_id"].index(top)]
+                rows[-1].update(run_align=align, heuristic_aligned=top,
+                                heuristic_aligned_loss=round(t / best - 1.0, 4))
         print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
         del d, p
         torch.cuda.empty_cache()
@@ -641,6 +652,8 @@ def main():
     ap.add_argument("--cold-launches", type=int, default=50,
                     help="also time this many single launches with the caches flushed before "
                          "each (a 512 MB read) and report their median as cold_cache (0: skip)")
+    ap.add_argument("--no-run-align", action="store_true",
+                    help="do not pass the workload's run-alignment promise to the ranker")
     ap.add_argument("--single-timing", action="store_true",
                     help="time only the chosen mode, with no cold-cache launches (profiling "
                          "runs: every traced dispatch then comes from the mode the line reports)")
@@ -732,6 +745,10 @@ def main():
         kw["run_split"] = args.run_split
     if args.max_workgroups:
         kw["max_workgroups"] = args.max_workgroups
+    # the workload's routing promise (its runs start on multiples of this)
+    run_align = WORKLOADS[args.workload].get("run_align", 0) if not args.no_run_align else 0
+    if run_align and p.get("m_indices") is not None:
+        kw["run_align"] = run_align
     tuned = None
     if args.autotune and args.tile is None:
         # the library's bounded autotune, once, untimed: later calls of this
@@ -763,7 +780,7 @@ def main():
     src = kernel_source_hash(args.workload)
     traffic = measured_traffic(args.workload, src)
     tiles = fgg.rank_tiles(fgg.FP8 if kind == "fp8" else fgg.FP4, M, N, K, G,
-                           num_cus=fgg.device_info()["num_cus"])
+                           num_cus=fgg.device_info()["num_cus"], run_align=kw.get("run_align", 0))
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -777,6 +794,7 @@ def main():
                    "tile_choice": ("given" if args.tile is not None
                                    else "bounded autotune" if tuned else "ranker"),
                    "run_split": args.run_split, "max_workgroups": args.max_workgroups,
+                   "run_align": kw.get("run_align", 0),
                    "timing": TIMING[args.timing], "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops_launch, 2), "peak": PEAK[mma],
                      "unit": "TFLOP/s", "frac": round(tflops_launch / PEAK[mma], 4),

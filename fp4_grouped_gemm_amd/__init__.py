@@ -57,7 +57,7 @@ class _Fp4Problem(ctypes.Structure):
 
 class _Options(ctypes.Structure):
     _fields_ = [("tile_id", ctypes.c_int), ("max_workgroups", ctypes.c_int),
-                ("run_split", ctypes.c_int)]
+                ("run_split", ctypes.c_int), ("run_align", ctypes.c_int)]
 
 
 def load_library():
@@ -103,6 +103,8 @@ def load_library():
     lib.fgg_num_tiles.argtypes = [I]
     lib.fgg_rank_tiles.restype = I
     lib.fgg_rank_tiles.argtypes = [I, I, I, I, I, I, ctypes.POINTER(_Tile), I]
+    lib.fgg_rank_tiles_aligned.restype = I
+    lib.fgg_rank_tiles_aligned.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(_Tile), I]
     lib.fgg_device_info.restype = I
     lib.fgg_device_info.argtypes = [ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I),
                                     ctypes.c_char_p, I]
@@ -116,11 +118,11 @@ def _check(status: int):
         raise ValueError(msg or f"fgg status {status}")
 
 
-def _opts(tile_id, max_workgroups, run_split=0):
-    if tile_id is None and not max_workgroups and not run_split:
+def _opts(tile_id, max_workgroups, run_split=0, run_align=0):
+    if tile_id is None and not max_workgroups and not run_split and not run_align:
         return None
     return ctypes.byref(_Options(-1 if tile_id is None else int(tile_id), int(max_workgroups or 0),
-                                 int(run_split or 0)))
+                                 int(run_split or 0), int(run_align or 0)))
 
 
 def _torch():
@@ -190,21 +192,22 @@ def _fp8_call(A, B, a_scale, b_scale, m_indices, out):
 
 
 def grouped_fp8_gemm(A, B, a_scale, b_scale, m_indices, out=None, *, tile_id=None,
-                     max_workgroups=0, run_split=0, stream=None):
+                     max_workgroups=0, run_split=0, run_align=0, stream=None):
     """C[M, N] (bfloat16) of the grouped block-scaled FP8 GEMM.
 
     A [M, K] and B [G, N, K] hold E4M3FN codes; a_scale [M, K/128] and
     b_scale [G, N/128, K/128] are float32; m_indices [M] is int32 (expert id or
     -1).  See include/fgg.h for the exact definition.  tile_id,
-    max_workgroups and run_split are the fields of fgg_options (run_split: 0
-    automatic, -1 never, 1 always run each expert pass of a row window as its
-    own workgroup).
+    max_workgroups, run_split and run_align are the fields of fgg_options
+    (run_split: 0 automatic, -1 never, 1 always run each expert pass of a row
+    window as its own workgroup; run_align > 0: every expert run starts at a
+    multiple of that many rows, a hint for the tile choice).
     """
     torch = _torch()
     C, dev, args = _fp8_call(A, B, a_scale, b_scale, m_indices, out)
     with torch.cuda.device(dev):
-        _check(load_library().grouped_fp8_gemm_ex(*args, _opts(tile_id, max_workgroups, run_split),
-                                                  _stream_ptr(stream, dev)))
+        _check(load_library().grouped_fp8_gemm_ex(
+            *args, _opts(tile_id, max_workgroups, run_split, run_align), _stream_ptr(stream, dev)))
     return C
 
 
@@ -285,7 +288,7 @@ def fp4_gemm(A, B, a_scale, b_scale, alpha, out=None, *, tile_id=None, max_workg
 
 
 def grouped_fp4_gemm(A, B, a_scale, b_scale, m_indices, alpha, out=None, *, tile_id=None,
-                     max_workgroups=0, run_split=0, stream=None):
+                     max_workgroups=0, run_split=0, run_align=0, stream=None):
     """C[M, N] (bfloat16) of the grouped NVFP4 GEMM: B [G, N, K/2], b_scale
     [G, N, K/16]; m_indices int32 [M] routes rows (-1 = padding).  alpha is
     a float (one global scale for every expert) or a float32 device tensor
@@ -302,11 +305,12 @@ def grouped_fp4_gemm(A, B, a_scale, b_scale, m_indices, alpha, out=None, *, tile
             _dev(alpha, "alpha", dev)
             a = list(args)
             a[5] = alpha.data_ptr()
-            _check(lib.grouped_fp4_gemm_alpha_ex(*a, _opts(tile_id, max_workgroups, run_split),
-                                                 _stream_ptr(stream, dev)))
+            _check(lib.grouped_fp4_gemm_alpha_ex(
+                *a, _opts(tile_id, max_workgroups, run_split, run_align), _stream_ptr(stream, dev)))
         else:
-            _check(lib.grouped_fp4_gemm_ex(*args, _opts(tile_id, max_workgroups, run_split),
-                                           _stream_ptr(stream, dev)))
+            _check(lib.grouped_fp4_gemm_ex(
+                *args, _opts(tile_id, max_workgroups, run_split, run_align),
+                _stream_ptr(stream, dev)))
     return C
 
 
@@ -402,12 +406,14 @@ def num_tiles(kind: int) -> int:
     return load_library().fgg_num_tiles(kind)
 
 
-def rank_tiles(kind: int, M: int, N: int, K: int, G: int = 1, num_cus: int = 256):
-    """The ranker's ordered tile configs for a problem (host logic only)."""
+def rank_tiles(kind: int, M: int, N: int, K: int, G: int = 1, num_cus: int = 256,
+               run_align: int = 0):
+    """The ranker's ordered tile configs for a problem (host logic only);
+    run_align as in fgg_options."""
     lib = load_library()
     n = max(1, lib.fgg_num_tiles(kind))
     arr = (_Tile * n)()
-    k = lib.fgg_rank_tiles(kind, M, N, K, G, num_cus, arr, n)
+    k = lib.fgg_rank_tiles_aligned(kind, M, N, K, G, run_align, num_cus, arr, n)
     if k < 0:
         _check(1)
     return [dict(id=t.id, block_m=t.block_m, block_n=t.block_n, waves=t.waves,

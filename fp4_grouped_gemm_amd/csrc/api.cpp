@@ -122,9 +122,12 @@ fgg_status check_common(const char* fn, const void* A, const void* B, const void
 //               busy, tiles / (num_waves * CUs * wg_per_cu);
 //   throughput= per-CU efficiency of the tile shape.
 // The page's 2-CTA and cluster-multicast factors have no gfx950 counterpart.
-float score_tile(const fgg::TileCfg& t, int M, int N, int G, int num_cus) {
+float score_tile(const fgg::TileCfg& t, int M, int N, int G, int num_cus, int run_align) {
   const long long windows = (M + t.block_m - 1) / t.block_m;
-  const long long row_tiles = windows + std::min<long long>(G - 1, windows * 4);
+  // every expert boundary in its own window, unless the runs start on
+  // multiples of the tile height
+  const bool aligned = run_align > 0 && run_align % t.block_m == 0;
+  const long long row_tiles = windows + (aligned ? 0 : std::min<long long>(G - 1, windows * 4));
   const long long ntiles = (N + t.block_n - 1) / t.block_n;
   const double m_eff = (double)M / (double)(row_tiles * t.block_m);
   const double n_eff = (double)N / (double)(ntiles * t.block_n);
@@ -135,12 +138,12 @@ float score_tile(const fgg::TileCfg& t, int M, int N, int G, int num_cus) {
   return (float)(std::min(1.0, m_eff) * n_eff * busy * t.tput);
 }
 
-int rank(int kind, int M, int N, int G, int num_cus, fgg_tile* out, int max_out) {
+int rank(int kind, int M, int N, int G, int num_cus, int run_align, fgg_tile* out, int max_out) {
   const int n = kind == FGG_KIND_FP8 ? fgg::fp8_num_tiles() : fgg::fp4_num_tiles();
   std::vector<fgg_tile> v;
   for (int i = 0; i < n; ++i) {
     const fgg::TileCfg& t = kind == FGG_KIND_FP8 ? fgg::fp8_tile(i) : fgg::fp4_tile(i);
-    fgg_tile r{t.id, t.block_m, t.block_n, t.waves, t.wg_per_cu, score_tile(t, M, N, G, num_cus)};
+    fgg_tile r{t.id, t.block_m, t.block_n, t.waves, t.wg_per_cu, score_tile(t, M, N, G, num_cus, run_align)};
     v.push_back(r);
   }
   std::stable_sort(v.begin(), v.end(), [](const fgg_tile& a, const fgg_tile& b) { return a.score > b.score; });
@@ -209,13 +212,15 @@ fgg_status pick_tile(const char* fn, int kind, int M, int N, int K, int G, int n
     *tile_id = opt->tile_id;
     return FGG_OK;
   }
+  const int align = opt ? opt->run_align : 0;
+  if (align < 0) return fail(FGG_EINVAL, fn, "run_align must be >= 0, got %d", align);
   const int t = tuned_tile(kind, M, N, K, G);
   if (t >= 0) {
     *tile_id = t;
     return FGG_OK;
   }
   fgg_tile best;
-  rank(kind, M, N, G, num_cus, &best, 1);
+  rank(kind, M, N, G, num_cus, align, &best, 1);
   *tile_id = best.id;
   return FGG_OK;
 }
@@ -229,7 +234,7 @@ fgg_status run_tune(const char* fn, int kind, int M, int N, int K, int G, int nu
   if (top_k < 1) return fail(FGG_EINVAL, fn, "top_k must be >= 1, got %d", top_k);
   if (reps < 1 || reps > 100000) return fail(FGG_EINVAL, fn, "reps must be in [1, 100000], got %d", reps);
   fgg_tile cand[FGG_TUNE_MAX];
-  const int n = rank(kind, M, N, G, num_cus, cand, std::min(top_k, FGG_TUNE_MAX));
+  const int n = rank(kind, M, N, G, num_cus, 0, cand, std::min(top_k, FGG_TUNE_MAX));
   hipEvent_t e0 = nullptr, e1 = nullptr;
   hipError_t e = hipEventCreate(&e0);
   if (e == hipSuccess) e = hipEventCreate(&e1);
@@ -292,19 +297,25 @@ int fgg_num_tiles(int kind) {
   return -1;
 }
 
-int fgg_rank_tiles(int kind, int M, int N, int K, int G, int num_cus, fgg_tile* out, int max_out) {
+int fgg_rank_tiles_aligned(int kind, int M, int N, int K, int G, int run_align, int num_cus,
+                           fgg_tile* out, int max_out) {
   const char* fn = "fgg_rank_tiles";
   (void)K;
   if (kind != FGG_KIND_FP8 && kind != FGG_KIND_FP4) return (fail(FGG_EINVAL, fn, "bad kind %d", kind), -1);
   if (!out || max_out < 1) return (fail(FGG_EINVAL, fn, "need an output array"), -1);
   if (M < 1 || N < 1 || G < 1) return (fail(FGG_EINVAL, fn, "sizes must be positive"), -1);
+  if (run_align < 0) return (fail(FGG_EINVAL, fn, "run_align must be >= 0, got %d", run_align), -1);
   if (num_cus <= 0) {
     fgg_status st;
     const DeviceFacts* d = current_device(fn, &st);
     if (!d) return -1;
     num_cus = d->num_cus;
   }
-  return rank(kind, M, N, G, num_cus, out, max_out);
+  return rank(kind, M, N, G, num_cus, run_align, out, max_out);
+}
+
+int fgg_rank_tiles(int kind, int M, int N, int K, int G, int num_cus, fgg_tile* out, int max_out) {
+  return fgg_rank_tiles_aligned(kind, M, N, K, G, 0, num_cus, out, max_out);
 }
 
 fgg_status fgg_device_info(int* num_cus, int* lds_per_block, int* clock_khz, char* arch,

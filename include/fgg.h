@@ -246,6 +246,9 @@ int fgg_num_tiles(int kind);
  * fgg_last_error() set. */
 int fgg_rank_tiles(int kind, int M, int N, int K, int G, int num_cus, fgg_tile* out,
                    int max_out);
+/* The same with the run_align promise of fgg_options (0 = none). */
+int fgg_rank_tiles_aligned(int kind, int M, int N, int K, int G, int run_align, int num_cus,
+                           fgg_tile* out, int max_out);
 
 /* Optional overrides for the *_ex entry points (NULL = defaults). */
 typedef struct {
@@ -258,6 +261,13 @@ typedef struct {
                         * mode uses it when every item runs at once on the
                         * device (small M: latency).  Results are identical
                         * either way.                                         */
+  int run_align;       /* grouped calls: > 0 promises that every expert run
+                        * starts at a row index that is a multiple of
+                        * run_align (MoE alignment padding); the ranker then
+                        * charges no two-expert windows to tile heights that
+                        * divide it.  0: unknown.  Only the tile choice
+                        * depends on it: results are correct whatever the
+                        * routing (and identical to asking for that tile).    */
 } fgg_options;
 
 fgg_status grouped_fp8_gemm_ex(const void* A, const void* B, const float* a_scale,

@@ -178,6 +178,28 @@ def test_ranker_prefers_full_waves():
     assert (top["block_m"], top["block_n"]) != (256, 256)
 
 
+def test_ranker_run_align():
+    """c3's shape (G=32 experts in M=16384 rows, N=2048): without a promise
+    every expert boundary is charged to a window of any height and 256x256
+    ranks first; with runs aligned to 128 rows the 128-row tiles carry no
+    two-expert windows and a 128x256 tile ranks first.  Alignment to 256
+    favours no 128-row shape over 256x256 again.  A dense problem (G=1) is
+    unaffected."""
+    plain = fgg.rank_tiles(fgg.FP8, 16384, 2048, 7168, 32, num_cus=256)
+    assert (plain[0]["block_m"], plain[0]["block_n"]) == (256, 256)
+    a128 = fgg.rank_tiles(fgg.FP8, 16384, 2048, 7168, 32, num_cus=256, run_align=128)
+    assert a128[0]["block_m"] == 128
+    a256 = fgg.rank_tiles(fgg.FP8, 16384, 2048, 7168, 32, num_cus=256, run_align=256)
+    assert (a256[0]["block_m"], a256[0]["block_n"]) == (256, 256)
+    assert a256[0]["score"] > plain[0]["score"]
+    dense = fgg.rank_tiles(fgg.FP4, 2048, 36864, 4608, 1, num_cus=256)
+    assert dense == fgg.rank_tiles(fgg.FP4, 2048, 36864, 4608, 1, num_cus=256, run_align=128)
+    lib = fgg.load_library()
+    arr = (fgg._Tile * 4)()
+    assert lib.fgg_rank_tiles_aligned(fgg.FP8, 64, 128, 128, 2, -1, 256, arr, 4) == -1
+    assert "run_align" in lib.fgg_last_error().decode()
+
+
 def test_device_info_without_gpu():
     torch = pytest.importorskip("torch")
     if torch.cuda.is_available():

@@ -7,7 +7,7 @@ import pytest
 
 import fp4_grouped_gemm_amd as fgg
 from tests.gpu_util import assert_parity, c_bits, log, run, to_dev
-from workloads import make, nvfp4_problem, runs_to_indices
+from workloads import fp8_problem, make, nvfp4_problem, runs_to_indices
 
 pytestmark = pytest.mark.gpu
 
@@ -68,3 +68,27 @@ def test_tune_top1_is_the_heuristic_and_bad_arguments_raise():
     with pytest.raises(ValueError, match="reps"):
         _tune(p, d, top_k=2, reps=0)
     fgg.tune_clear()
+
+
+def test_run_align_changes_only_the_tile():
+    """Runs padded to 128 rows (the MoE alignment step): with run_align=128
+    the ranker picks a 128-row tile here (no two-expert windows) where it
+    otherwise picks a wider one.  The default call with the promise launches
+    exactly that tile (bitwise equal to asking for it) and matches the
+    oracle; so does the call without the promise."""
+    counts = [128 * k for k in (5, 3, 9, 1, 6, 4, 2, 2)]
+    p = fp8_problem(runs_to_indices(counts), 1024, 256, 8, np.random.default_rng(11))
+    M, N, K, G = p["M"], p["N"], p["K"], p["G"]
+    plain = fgg.rank_tiles(fgg.FP8, M, N, K, G, num_cus=fgg.device_info()["num_cus"])[0]["id"]
+    aligned = fgg.rank_tiles(fgg.FP8, M, N, K, G, num_cus=fgg.device_info()["num_cus"],
+                             run_align=128)[0]["id"]
+    assert aligned != plain
+    d = to_dev(p)
+    fgg.tune_clear()
+    log(f"run_align M={M} N={N} K={K} G={G} tiles {plain} -> {aligned}")
+    c_al = run(p, d, run_align=128)
+    assert np.array_equal(c_bits(c_al), c_bits(run(p, d, tile_id=aligned)))
+    assert_parity(p, c_al)
+    assert_parity(p, run(p, d))
+    with pytest.raises(ValueError):
+        run(p, d, run_align=-128)
