@@ -250,7 +250,9 @@ int fgg_rank_tiles(int kind, int M, int N, int K, int G, int num_cus, fgg_tile* 
 int fgg_rank_tiles_aligned(int kind, int M, int N, int K, int G, int run_align, int num_cus,
                            fgg_tile* out, int max_out);
 
-/* Optional overrides for the *_ex entry points (NULL = defaults). */
+/* Optional overrides for the *_ex entry points (NULL = defaults).  Initialise
+ * the whole struct (e.g. `fgg_options o = {-1};` then set fields): a field
+ * left out means 0, and new fields are only ever added at the end. */
 typedef struct {
   int tile_id;         /* -1: use the ranker's top choice                    */
   int max_workgroups;  /* > 0: cap the persistent grid (testing / tuning)    */
