@@ -206,6 +206,11 @@ def test_full_size_sampled(name):
         log(f"{name} full size tile {tile}")
         C = run(p, d, tile_id=tile)
         assert_parity(p, C, rows=rows[::3], what=f"{name}/tile{tile}")
+    if name == "c3_skewed_fp8":  # as the bench launches it: runs padded to 128, promised
+        log(f"{name} full size, run_align=128")
+        C = run(p, d, run_align=128)
+        assert_parity(p, C, rows=rows, what=f"{name}/run_align")
+        assert np.all(c_to_f64(C)[ids < 0] == 0.0)
 
 
 @pytest.mark.slow
