@@ -325,3 +325,35 @@ def test_grid_stride_loops_on_sampled_rows():
     assert g == g_ref
     q_ref, s_ref, _ = oq.quantize_nvfp4(x[rows], g_ref)
     assert np.array_equal(Q[rows], q_ref) and np.array_equal(S[rows], s_ref)
+
+
+@pytest.mark.slow
+def test_bench_shapes_sampled():
+    """The bench's quantiser workloads at full size, as it launches them
+    (seeded N(0,1) BF16 activations: c2's A 8192 x 7168 through FP8, c5's A
+    65536 x 8192 through NVFP4 with the computed and with a calibrated global
+    scale): sampled rows bitwise against the oracle, the global scale exact."""
+    import torch
+    import fp4_grouped_gemm_amd as fgg
+    for M, K, fmt in ((8192, 7168, "fp8"), (65536, 8192, "nvfp4")):
+        rng = np.random.default_rng(0)
+        t = torch.from_numpy(rng.standard_normal((M, K), dtype=np.float32)).to(torch.bfloat16)
+        rows = np.unique(np.concatenate([[0, 1, M - 1], rng.choice(M, 40, replace=False)]))
+        xs = t[torch.from_numpy(rows)].float().numpy()
+        log(f"quantiser {fmt} full size M={M} K={K}")
+        if fmt == "fp8":
+            Q, S = _gpu_fp8(t)
+            q_ref, s_ref = oq.quantize_fp8_1x128(xs)
+            assert np.array_equal(Q[rows], q_ref) and np.array_equal(S[rows], s_ref)
+            continue
+        Q, S, g = _gpu_nvfp4(t)
+        amax = np.float32(float(t.cuda().float().abs().max()))  # the tensor's maximum, exactly
+        g_ref = oq.nvfp4_global_scale(np.array([amax], np.float32))
+        assert g == g_ref
+        q_ref, s_ref, _ = oq.quantize_nvfp4(xs, g_ref)
+        assert np.array_equal(Q[rows], q_ref) and np.array_equal(S[rows], s_ref)
+        g_static = float(t[:64].float().abs().max()) / 2688.0  # the bench's calibration
+        Qs, Ss, _ = fgg.quantize_nvfp4(t.cuda(), global_scale=g_static)
+        q_ref, s_ref, _ = oq.quantize_nvfp4(xs, np.float32(g_static))
+        assert np.array_equal(Qs.cpu().numpy()[rows], q_ref)
+        assert np.array_equal(Ss.cpu().numpy()[rows], s_ref)
