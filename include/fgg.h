@@ -198,13 +198,14 @@ fgg_status grouped_w4a16_gemm(const void* A, const void* B, const void* b_scale,
  * finalise); no host synchronisation, no allocation.
  *
  * quantize_nvfp4_static -- the same encoding with the global scale g given by
- * the caller (a calibrated, static activation scale) instead of amax(X) /
- * 2688: one kernel launch that reads X once.  Values whose block amax exceeds
+ * the caller (a calibrated, static activation scale; the NVFP4 format has one
+ * FP32 scale per tensor, and how it is chosen is left open by the pages)
+ * instead of amax(X) / 2688: one kernel launch that reads X once.  Values whose block amax exceeds
  * 448 * 6 * g saturate (block scale 448, codes clamped to +-6).  g must be a
  * finite normal positive float (FGG_EINVAL otherwise).
  *
  * Requirements: X, Q 16-byte aligned (scale: 4-byte for FP8, any for NVFP4;
- * global_scale 4-byte); 1 <= M <= 2^24; 128 <= K <= 2^20, K % 128 == 0; X
+ * the global_scale pointer of quantize_nvfp4 4-byte); 1 <= M <= 2^24; 128 <= K <= 2^20, K % 128 == 0; X
  * finite.  Errors as for the GEMMs.
  * ------------------------------------------------------------------------ */
 fgg_status quantize_fp8_1x128(const void* X, void* Q, float* scale, int M, int K, void* stream);
