@@ -25,6 +25,8 @@ __all__ = [
 ]
 
 FP8, FP4 = 0, 1
+# fgg_status values (include/fgg.h)
+OK, EINVAL, EUNSUPPORTED, EALIGN, EDEVICE, EHIP = 0, 1, 2, 3, 4, 5
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
@@ -89,9 +91,9 @@ def load_library():
         ("fp4_gemm_problems", [ctypes.POINTER(_Fp4Problem), I, P]),
         ("fp4_gemm_problems_ex", [ctypes.POINTER(_Fp4Problem), I, OPT, P]),
         ("grouped_w4a16_gemm", [P, P, P, P, F, P, I, I, I, I, P]),
-        ("grouped_fp8_gemm_tune", [P, P, P, P, P, P, I, I, I, I, I, I, REP, P]),
-        ("fp4_gemm_tune", [P, P, P, P, F, P, I, I, I, I, I, REP, P]),
-        ("grouped_fp4_gemm_tune", [P, P, P, P, P, F, P, I, I, I, I, I, I, REP, P]),
+        ("grouped_fp8_gemm_tune", [P, P, P, P, P, P, I, I, I, I, I, I, REP, OPT, P]),
+        ("fp4_gemm_tune", [P, P, P, P, F, P, I, I, I, I, I, REP, OPT, P]),
+        ("grouped_fp4_gemm_tune", [P, P, P, P, P, F, P, I, I, I, I, I, I, REP, OPT, P]),
         ("fgg_tuned_tile", [I, I, I, I, I]),
     ):
         fn = getattr(lib, name)
@@ -217,16 +219,19 @@ def _report(r):
 
 
 def grouped_fp8_gemm_tune(A, B, a_scale, b_scale, m_indices, out=None, *, top_k=4, reps=5,
-                          stream=None):
+                          max_workgroups=0, run_split=0, run_align=0, stream=None):
     """Time the ranker's top_k tile configs on these inputs and record the
     fastest for this shape (C ABI grouped_fp8_gemm_tune; synchronises).
+    run_align shapes the ranking the candidates come from; max_workgroups
+    and run_split apply to every timed launch (as for grouped_fp8_gemm).
     Returns (C, report) with report = {tile_id, ms, best, chosen}."""
     torch = _torch()
     C, dev, args = _fp8_call(A, B, a_scale, b_scale, m_indices, out)
     rep = _TuneReport()
     with torch.cuda.device(dev):
-        _check(load_library().grouped_fp8_gemm_tune(*args, int(top_k), int(reps),
-                                                    ctypes.byref(rep), _stream_ptr(stream, dev)))
+        _check(load_library().grouped_fp8_gemm_tune(
+            *args, int(top_k), int(reps), ctypes.byref(rep),
+            _opts(None, max_workgroups, run_split, run_align), _stream_ptr(stream, dev)))
     return C, _report(rep)
 
 
@@ -368,27 +373,30 @@ def fp4_gemm_problems(problems, outs=None, *, tile_id=None, max_workgroups=0, st
     return Cs
 
 
-def fp4_gemm_tune(A, B, a_scale, b_scale, alpha, out=None, *, top_k=4, reps=5, stream=None):
+def fp4_gemm_tune(A, B, a_scale, b_scale, alpha, out=None, *, top_k=4, reps=5,
+                  max_workgroups=0, stream=None):
     """Bounded autotune of fp4_gemm for this shape (as grouped_fp8_gemm_tune)."""
     torch = _torch()
     C, dev, args = _fp4_call(A, B, a_scale, b_scale, None, alpha, out)
     rep = _TuneReport()
     with torch.cuda.device(dev):
         _check(load_library().fp4_gemm_tune(*args, int(top_k), int(reps), ctypes.byref(rep),
+                                            _opts(None, max_workgroups),
                                             _stream_ptr(stream, dev)))
     return C, _report(rep)
 
 
 def grouped_fp4_gemm_tune(A, B, a_scale, b_scale, m_indices, alpha, out=None, *, top_k=4, reps=5,
-                          stream=None):
+                          max_workgroups=0, run_split=0, run_align=0, stream=None):
     """Bounded autotune of grouped_fp4_gemm for this shape (as
     grouped_fp8_gemm_tune)."""
     torch = _torch()
     C, dev, args = _fp4_call(A, B, a_scale, b_scale, m_indices, alpha, out)
     rep = _TuneReport()
     with torch.cuda.device(dev):
-        _check(load_library().grouped_fp4_gemm_tune(*args, int(top_k), int(reps),
-                                                    ctypes.byref(rep), _stream_ptr(stream, dev)))
+        _check(load_library().grouped_fp4_gemm_tune(
+            *args, int(top_k), int(reps), ctypes.byref(rep),
+            _opts(None, max_workgroups, run_split, run_align), _stream_ptr(stream, dev)))
     return C, _report(rep)
 
 

@@ -89,17 +89,27 @@ const DeviceFacts* current_device(const char* fn, fgg_status* st) {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Shape and pointer checks shared by every entry point.  Pure host logic.
+// `k_unit` is the K divisibility the format itself needs (128 for FP8's
+// 1x128 / 128x128 scale blocks, 16 for NVFP4's scale blocks): violating it
+// is FGG_EINVAL.  Shapes inside the method's limits that this library does
+// not implement (N % 128 != 0: partial b_scale blocks; NVFP4 K % 128 != 0)
+// are FGG_EUNSUPPORTED.
 fgg_status check_common(const char* fn, const void* A, const void* B, const void* sa,
                         const void* sb, const void* C, int M, int N, int K, int G,
-                        bool grouped, const void* m_indices, uintptr_t scale_align) {
+                        bool grouped, const void* m_indices, uintptr_t scale_align,
+                        int k_unit = 128) {
   if (!A || !B || !sa || !sb || !C) return fail(FGG_EINVAL, fn, "null pointer among A, B, a_scale, b_scale, C");
   if (grouped && !m_indices) return fail(FGG_EINVAL, fn, "m_indices is null");
   if (M < 1 || M > (1 << 24)) return fail(FGG_EINVAL, fn, "requires 1 <= M <= 2^24, got M=%d", M);
-  if (N < 128 || N > (1 << 19)) return fail(FGG_EINVAL, fn, "requires 128 <= N <= 2^19, got N=%d", N);
-  if (N % 128) return fail(FGG_EINVAL, fn, "requires N %% 128 == 0 (whole b_scale blocks), got N=%d", N);
-  if (K < 128 || K > (1 << 20)) return fail(FGG_EINVAL, fn, "requires 128 <= K <= 2^20, got K=%d", K);
-  if (K % 128) return fail(FGG_EINVAL, fn, "requires K %% 128 == 0, got K=%d", K);
+  if (N < 64 || N > (1 << 19)) return fail(FGG_EINVAL, fn, "requires 64 <= N <= 2^19, got N=%d", N);
+  if (N % 64) return fail(FGG_EINVAL, fn, "requires N %% 64 == 0, got N=%d", N);
+  if (K < k_unit || K > (1 << 20)) return fail(FGG_EINVAL, fn, "requires %d <= K <= 2^20, got K=%d", k_unit, K);
+  if (K % k_unit) return fail(FGG_EINVAL, fn, "requires K %% %d == 0, got K=%d", k_unit, K);
   if (G < 1 || G > (1 << 16)) return fail(FGG_EINVAL, fn, "requires 1 <= G <= 2^16, got G=%d", G);
+  if (N % 128)
+    return fail(FGG_EUNSUPPORTED, fn, "N %% 128 != 0 (N=%d) is not supported: whole 128-column blocks only", N);
+  if (K % 128)
+    return fail(FGG_EUNSUPPORTED, fn, "K %% 128 != 0 (K=%d) is not supported: whole 128-wide K steps only", K);
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16))
     return fail(FGG_EALIGN, fn, "A, B and C must be 16-byte aligned");
   if (!aligned(sa, scale_align) || !aligned(sb, scale_align))
@@ -228,13 +238,23 @@ fgg_status pick_tile(const char* fn, int kind, int M, int N, int K, int G, int n
 // Time the ranker's top candidates with `launch(tile_id)` (returns the
 // launch's hipError_t) and record the fastest.  Bounded: at most
 // FGG_TUNE_MAX configs x (reps + 1) launches.
-template <class Launch>
-fgg_status run_tune(const char* fn, int kind, int M, int N, int K, int G, int num_cus, int top_k,
-                    int reps, fgg_tune_report* report, hipStream_t s, Launch launch) {
+// Arguments of a *_tune call beyond its GEMM's (checked before the device).
+fgg_status check_tune(const char* fn, int top_k, int reps, const fgg_options* opt) {
   if (top_k < 1) return fail(FGG_EINVAL, fn, "top_k must be >= 1, got %d", top_k);
   if (reps < 1 || reps > 100000) return fail(FGG_EINVAL, fn, "reps must be in [1, 100000], got %d", reps);
+  if (opt && opt->tile_id >= 0)
+    return fail(FGG_EINVAL, fn, "tile_id must be -1 when tuning (the tuning chooses it), got %d", opt->tile_id);
+  if (opt && opt->run_align < 0) return fail(FGG_EINVAL, fn, "run_align must be >= 0, got %d", opt->run_align);
+  return FGG_OK;
+}
+
+template <class Launch>
+fgg_status run_tune(const char* fn, int kind, int M, int N, int K, int G, int num_cus, int top_k,
+                    int reps, fgg_tune_report* report, const fgg_options* opt, hipStream_t s,
+                    Launch launch) {
+  const int align = opt ? opt->run_align : 0;
   fgg_tile cand[FGG_TUNE_MAX];
-  const int n = rank(kind, M, N, G, num_cus, 0, cand, std::min(top_k, FGG_TUNE_MAX));
+  const int n = rank(kind, M, N, G, num_cus, align, cand, std::min(top_k, FGG_TUNE_MAX));
   hipEvent_t e0 = nullptr, e1 = nullptr;
   hipError_t e = hipEventCreate(&e0);
   if (e == hipSuccess) e = hipEventCreate(&e1);
@@ -358,15 +378,17 @@ fgg_status grouped_fp8_gemm_ex(const void* A, const void* B, const float* a_scal
 fgg_status grouped_fp8_gemm_tune(const void* A, const void* B, const float* a_scale,
                                  const float* b_scale, const int32_t* m_indices, void* C, int M,
                                  int N, int K, int G, int top_k, int reps,
-                                 fgg_tune_report* report, void* stream) {
+                                 fgg_tune_report* report, const fgg_options* opt, void* stream) {
   const char* fn = "grouped_fp8_gemm_tune";
   fgg::Fp8Args a;
   const DeviceFacts* d = nullptr;
-  fgg_status st = fp8_prepare(fn, A, B, a_scale, b_scale, m_indices, C, M, N, K, G, &a, &d);
+  fgg_status st = check_tune(fn, top_k, reps, opt);
+  if (st != FGG_OK) return st;
+  st = fp8_prepare(fn, A, B, a_scale, b_scale, m_indices, C, M, N, K, G, &a, &d);
   if (st != FGG_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const fgg::LaunchOpts o = launch_opts(nullptr, d);
-  return run_tune(fn, FGG_KIND_FP8, M, N, K, G, d->num_cus, top_k, reps, report, s,
+  const fgg::LaunchOpts o = launch_opts(opt, d);
+  return run_tune(fn, FGG_KIND_FP8, M, N, K, G, d->num_cus, top_k, reps, report, opt, s,
                   [&](int tile) { return fgg::launch_fp8(a, tile, o, s); });
 }
 
@@ -381,7 +403,7 @@ static fgg_status fp4_prepare(const char* fn, const void* A, const void* B, cons
                               const void* b_scale, const int32_t* m_indices, float alpha, void* C,
                               int M, int N, int K, int G, bool grouped, fgg::Fp4Args* a,
                               const DeviceFacts** d, const float* alphas = nullptr) {
-  fgg_status st = check_common(fn, A, B, a_scale, b_scale, C, M, N, K, G, grouped, m_indices, 16);
+  fgg_status st = check_common(fn, A, B, a_scale, b_scale, C, M, N, K, G, grouped, m_indices, 16, 16);
   if (st != FGG_OK) return st;
   if (!std::isfinite(alpha)) return fail(FGG_EINVAL, fn, "alpha must be finite");
   if (!(*d = current_device(fn, &st))) return st;
@@ -409,15 +431,16 @@ static fgg_status fp4_common(const char* fn, const void* A, const void* B, const
 static fgg_status fp4_tune(const char* fn, const void* A, const void* B, const void* a_scale,
                            const void* b_scale, const int32_t* m_indices, float alpha, void* C,
                            int M, int N, int K, int G, bool grouped, int top_k, int reps,
-                           fgg_tune_report* report, void* stream) {
+                           fgg_tune_report* report, const fgg_options* opt, void* stream) {
   fgg::Fp4Args a;
   const DeviceFacts* d = nullptr;
-  fgg_status st = fp4_prepare(fn, A, B, a_scale, b_scale, m_indices, alpha, C, M, N, K, G, grouped,
-                              &a, &d);
+  fgg_status st = check_tune(fn, top_k, reps, opt);
+  if (st != FGG_OK) return st;
+  st = fp4_prepare(fn, A, B, a_scale, b_scale, m_indices, alpha, C, M, N, K, G, grouped, &a, &d);
   if (st != FGG_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const fgg::LaunchOpts o = launch_opts(nullptr, d);
-  return run_tune(fn, FGG_KIND_FP4, M, N, K, G, d->num_cus, top_k, reps, report, s,
+  const fgg::LaunchOpts o = launch_opts(opt, d);
+  return run_tune(fn, FGG_KIND_FP4, M, N, K, G, d->num_cus, top_k, reps, report, opt, s,
                   [&](int tile) { return fgg::launch_fp4(a, tile, o, s); });
 }
 
@@ -449,17 +472,18 @@ fgg_status grouped_fp4_gemm(const void* A, const void* B, const void* a_scale,
 
 fgg_status fp4_gemm_tune(const void* A, const void* B, const void* a_scale, const void* b_scale,
                          float alpha, void* C, int M, int N, int K, int top_k, int reps,
-                         fgg_tune_report* report, void* stream) {
+                         fgg_tune_report* report, const fgg_options* opt, void* stream) {
   return fp4_tune("fp4_gemm_tune", A, B, a_scale, b_scale, nullptr, alpha, C, M, N, K, 1, false,
-                  top_k, reps, report, stream);
+                  top_k, reps, report, opt, stream);
 }
 
 fgg_status grouped_fp4_gemm_tune(const void* A, const void* B, const void* a_scale,
                                  const void* b_scale, const int32_t* m_indices, float alpha,
                                  void* C, int M, int N, int K, int G, int top_k, int reps,
-                                 fgg_tune_report* report, void* stream) {
+                                 fgg_tune_report* report, const fgg_options* opt,
+                                 void* stream) {
   return fp4_tune("grouped_fp4_gemm_tune", A, B, a_scale, b_scale, m_indices, alpha, C, M, N, K, G,
-                  true, top_k, reps, report, stream);
+                  true, top_k, reps, report, opt, stream);
 }
 
 fgg_status grouped_fp4_gemm_alpha_ex(const void* A, const void* B, const void* a_scale,
@@ -500,7 +524,7 @@ fgg_status fp4_gemm_problems_ex(const fgg_fp4_problem* problems, int count,
     char where[64];
     std::snprintf(where, sizeof(where), "%s (problem %d)", fn, g);
     fgg_status st = check_common(where, q.A, q.B, q.a_scale, q.b_scale, q.C, q.M, q.N, q.K, 1,
-                                 false, nullptr, 16);
+                                 false, nullptr, 16, 16);
     if (st != FGG_OK) return st;
     if (!std::isfinite(q.alpha)) return fail(FGG_EINVAL, where, "alpha must be finite");
     set.p[g] = fgg::Fp4Problem{static_cast<const uint8_t*>(q.A), static_cast<const uint8_t*>(q.B),
@@ -532,11 +556,11 @@ fgg_status grouped_w4a16_gemm(const void* A, const void* B, const void* b_scale,
                               int K, int G, void* stream) {
   const char* fn = "grouped_w4a16_gemm";
   // A stands in for a_scale in the shared checks (16-byte aligned, non-null).
-  fgg_status st = check_common(fn, A, B, A, b_scale, C, M, N, K, G, true, m_indices, 16);
+  fgg_status st = check_common(fn, A, B, A, b_scale, C, M, N, K, G, true, m_indices, 16, 16);
   if (st != FGG_OK) return st;
   if (!std::isfinite(b_global)) return fail(FGG_EINVAL, fn, "b_global must be finite");
   if ((long long)M * K * 2 > 0x7FFFFFFFLL)
-    return fail(FGG_EINVAL, fn, "requires M * K * 2 < 2^31 bytes of activations (decode path), got M=%d K=%d", M, K);
+    return fail(FGG_EUNSUPPORTED, fn, "requires M * K * 2 < 2^31 bytes of activations (decode path), got M=%d K=%d", M, K);
   const DeviceFacts* d = current_device(fn, &st);
   if (!d) return st;
   const fgg::W4A16Args a{static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(B),
@@ -554,11 +578,13 @@ void fgg_tune_clear(void) {
 
 // Activation quantisers (the step before the GEMM).
 static fgg_status check_quant(const char* fn, const void* X, const void* Q, const void* S, int M,
-                              int K, uintptr_t scale_align) {
+                              int K, uintptr_t scale_align, int k_unit) {
   if (!X || !Q || !S) return fail(FGG_EINVAL, fn, "null pointer among X, Q, scale");
   if (M < 1 || M > (1 << 24)) return fail(FGG_EINVAL, fn, "requires 1 <= M <= 2^24, got M=%d", M);
-  if (K < 128 || K > (1 << 20)) return fail(FGG_EINVAL, fn, "requires 128 <= K <= 2^20, got K=%d", K);
-  if (K % 128) return fail(FGG_EINVAL, fn, "requires K %% 128 == 0, got K=%d", K);
+  if (K < k_unit || K > (1 << 20)) return fail(FGG_EINVAL, fn, "requires %d <= K <= 2^20, got K=%d", k_unit, K);
+  if (K % k_unit) return fail(FGG_EINVAL, fn, "requires K %% %d == 0, got K=%d", k_unit, K);
+  if (K % 128)
+    return fail(FGG_EUNSUPPORTED, fn, "K %% 128 != 0 (K=%d) is not supported", K);
   if (!aligned(X, 16) || !aligned(Q, 16))
     return fail(FGG_EALIGN, fn, "X and Q must be 16-byte aligned");
   if (!aligned(S, scale_align))
@@ -568,7 +594,7 @@ static fgg_status check_quant(const char* fn, const void* X, const void* Q, cons
 
 fgg_status quantize_fp8_1x128(const void* X, void* Q, float* scale, int M, int K, void* stream) {
   const char* fn = "quantize_fp8_1x128";
-  fgg_status st = check_quant(fn, X, Q, scale, M, K, 4);
+  fgg_status st = check_quant(fn, X, Q, scale, M, K, 4, 128);
   if (st != FGG_OK) return st;
   const DeviceFacts* d = current_device(fn, &st);
   if (!d) return st;
@@ -580,7 +606,7 @@ fgg_status quantize_fp8_1x128(const void* X, void* Q, float* scale, int M, int K
 fgg_status quantize_nvfp4(const void* X, void* Q, void* scale, float* global_scale, int M, int K,
                           void* stream) {
   const char* fn = "quantize_nvfp4";
-  fgg_status st = check_quant(fn, X, Q, scale, M, K, 1);
+  fgg_status st = check_quant(fn, X, Q, scale, M, K, 1, 16);
   if (st != FGG_OK) return st;
   if (!global_scale) return fail(FGG_EINVAL, fn, "global_scale is null");
   if (!aligned(global_scale, 4)) return fail(FGG_EALIGN, fn, "global_scale must be 4-byte aligned");
@@ -595,7 +621,7 @@ fgg_status quantize_nvfp4(const void* X, void* Q, void* scale, float* global_sca
 fgg_status quantize_nvfp4_static(const void* X, void* Q, void* scale, float global_scale, int M,
                                  int K, void* stream) {
   const char* fn = "quantize_nvfp4_static";
-  fgg_status st = check_quant(fn, X, Q, scale, M, K, 1);
+  fgg_status st = check_quant(fn, X, Q, scale, M, K, 1, 16);
   if (st != FGG_OK) return st;
   if (!std::isfinite(global_scale) || !(global_scale >= std::numeric_limits<float>::min()))
     return fail(FGG_EINVAL, fn, "global_scale must be a finite normal positive float, got %g",

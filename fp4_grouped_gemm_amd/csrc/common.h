@@ -257,8 +257,13 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr uint32_t kSkip = 0x80000000u;
 
 // Raw buffer resource over [base, base + bytes), as its four descriptor
-// words (base address, stride 0, size, raw-access flags): loads at offsets
-// past the end return zeros, the out-of-range fill the tail tiles rely on.
+// words (base address, stride 0, size, raw-access flags).  The range check
+// compares the instruction's VGPR offset (plus its immediate offset) with
+// the size; the SGPR offset is added to the address after the check.  So a
+// load whose VGPR offset lies past the end returns zeros without touching
+// memory -- the out-of-range fill the tail tiles rely on -- and every caller
+// keeps its SGPR offset to a displacement that cannot leave the row or
+// block that an in-range VGPR offset points into.
 __device__ __forceinline__ i32x4 rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = (uint64_t)base;
   return (i32x4){(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};

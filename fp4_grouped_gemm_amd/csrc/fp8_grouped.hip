@@ -96,8 +96,12 @@ using namespace lds_dma;
 //  * A/B staging: a tile row is K bytes for both operands; lane l of a
 //    1 KB load writes LDS bytes [16 l, 16 l + 16) = tile row 8 b + l / 8,
 //    physical chunk l % 8, so it fetches logical chunk (l % 8) ^ (row % 8).
-//    Load s of wave w covers rows 8 (s W + w) .. + 7, i.e. the lane offset
-//    plus the uniform s * W * 8 * K, plus the step's kb * 128.
+//    Load s of wave w covers rows 8 (s W + w) .. + 7: the lane's offset
+//    (row and chunk) goes in the instruction's VGPR offset, which the buffer
+//    range check covers, so rows past the tile's last row return zeros
+//    without touching memory; only the step's in-row kb * 128 goes in the
+//    SGPR offset, which the range check leaves out (a chunk of a row inside
+//    the buffer then stays inside that row).
 template <class T>
 struct Pass {
   i32x4 ra, rb;  // A window rows, B[e] column-tile rows
@@ -124,26 +128,30 @@ struct Pass {
     for (int s = 0; s < T::A_LOADS; ++s) {
       const bool need = (a_groups >> (s * T::WAVES + wave)) & 1;
       if (T::STAGES == 2 && !need) continue;
-      dma16(ra, lds_addr(st + (s * T::WAVES + wave) * 1024), need ? lane_off : kSkip,
-            s * T::WAVES * 8 * K + kb * 128);
+      dma16(ra, lds_addr(st + (s * T::WAVES + wave) * 1024),
+            need ? lane_off + (uint32_t)(s * T::WAVES * 8) * K : kSkip, kb * 128);
     }
 #pragma unroll
     for (int s = 0; s < T::B_LOADS; ++s)
-      dma16(rb, lds_addr(st + T::A_BYTES + (s * T::WAVES + wave) * 1024), lane_off,
-            s * T::WAVES * 8 * K + kb * 128);
+      dma16(rb, lds_addr(st + T::A_BYTES + (s * T::WAVES + wave) * 1024),
+            lane_off + (uint32_t)(s * T::WAVES * 8) * K, kb * 128);
   }
 
   // a_scale values of K blocks [c SA_BLK, c SA_BLK + SA_ROW) of every window
   // row, as [row][SA_ROW] floats: one 4-byte direct-to-LDS load per lane,
   // SA_ROW lanes per row (one short piece per row instead of one cache line
-  // per row per step).  Values past the chunk or past the row are unused.
+  // per row per step).  Blocks past the row's last one load from past the
+  // buffer end (zeros, no access); rows past the window's last row fail the
+  // range check likewise.  Values past the chunk are unused.
   __device__ __forceinline__ void stage_scales(float* buf, int c, int wave, int lane) const {
 #pragma unroll
     for (int s = 0; s < T::SA_LOADS; ++s) {
       const int g = (s * T::WAVES + wave) * 64 + lane;  // row g / SA_ROW, block g % SA_ROW
-      const uint32_t off = ((uint32_t)g / T::SA_ROW) * (uint32_t)nkb * 4u +
-                           ((uint32_t)g % T::SA_ROW) * 4u;
-      dma4(rsa, lds_addr(buf + (s * T::WAVES + wave) * 64), off, c * T::SA_BLK * 4);
+      const uint32_t blk = (uint32_t)(c * T::SA_BLK) + (uint32_t)g % T::SA_ROW;
+      const uint32_t off = blk < (uint32_t)nkb
+                               ? ((uint32_t)g / T::SA_ROW * (uint32_t)nkb + blk) * 4u
+                               : kSkip;
+      dma4(rsa, lds_addr(buf + (s * T::WAVES + wave) * 64), off, 0);
     }
   }
 

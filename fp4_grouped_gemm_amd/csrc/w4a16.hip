@@ -116,6 +116,7 @@ struct Ctx {
   const uint8_t* scol[kCB];   // its scale codes
   i32x4 ra;                   // activation buffer resource (whole A)
   uint32_t a_off[kADma];      // this lane's activation chunks: row offset + chunk
+  int a_k[kADma];             // their first K index within a group
   uint32_t lds_a[kADma];      // their LDS destinations (stage 0)
   int ngroups;
   int K;
@@ -123,12 +124,18 @@ struct Ctx {
 };
 
 // Issue group g's activation chunks into LDS stage g % kAStages (group index
-// clamped to the last one past the end).
+// clamped to the last one past the end).  The whole offset is a VGPR offset,
+// which the buffer range check sees; a chunk at or past K (the half-full
+// last group when K is an odd multiple of 128) loads zeros from past the
+// buffer end instead of the next row's values, so no value outside the
+// row's K ever meets a weight (0 x Inf would be NaN).
 __device__ __forceinline__ void load_a(const Ctx& c, uint8_t* ring, int g) {
   const int gc = min(g, c.ngroups - 1);
   const uint32_t st = (uint32_t)((g % kAStages) * kAStage);
 #pragma unroll
-  for (int u = 0; u < kADma; ++u) dma16(c.ra, c.lds_a[u] + st, c.a_off[u], gc * kGroup * 2);
+  for (int u = 0; u < kADma; ++u)
+    dma16(c.ra, c.lds_a[u] + st,
+          gc * kGroup + c.a_k[u] < c.K ? c.a_off[u] + (uint32_t)(gc * kGroup * 2) : kSkip, 0);
   (void)ring;
 }
 
@@ -275,6 +282,7 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_kernel(const uint16_t* __re
         const int p = u * kThreads + tid;
         const int row = p / kChunks, lc = (p % kChunks) ^ row;
         c.a_off[u] = (uint32_t)rows[min(c0 + row, count - 1)] * (uint32_t)K * 2u + (uint32_t)lc * 16u;
+        c.a_k[u] = lc * 8;
         c.lds_a[u] = lds_addr(ring) + (uint32_t)(u * kThreads + wave * 64) * 16u;
       }
       f32x4 acc[kRB][kCB];

@@ -4,8 +4,10 @@
  * C ABI of libfgg.so.  Every pointer argument named A, B, a_scale, b_scale,
  * m_indices or C is a DEVICE pointer (HIP global memory of the current
  * device); sizes are plain ints; `stream` is a hipStream_t passed as void*
- * (NULL = the default stream).  The library reads A, B, the scales and
- * m_indices, writes every element of C (C need not be initialised), keeps no
+ * (NULL = the default stream), so that this header needs no HIP header and
+ * plain C or ctypes callers can use it as it is.  The library reads A, B,
+ * the scales and m_indices, writes every element of C (C need not be
+ * initialised), keeps no
  * pointer after the call returns, allocates no device memory and never
  * synchronises: work is enqueued on `stream` and the call returns.  It never
  * reads m_indices on the host, so a call can be captured in a HIP graph and
@@ -43,10 +45,15 @@ extern "C" {
 
 typedef enum {
   FGG_OK = 0,
-  FGG_EINVAL = 1,   /* null pointer, size out of range, divisibility violated */
-  FGG_EALIGN = 2,   /* a pointer is not 16-byte aligned                        */
-  FGG_EDEVICE = 3,  /* no HIP device, or the current device is not gfx950      */
-  FGG_EHIP = 4      /* a HIP runtime call or kernel launch failed              */
+  FGG_EINVAL = 1,        /* null pointer, size outside the method's limits, a
+                          * divisibility the method itself requires violated  */
+  FGG_EUNSUPPORTED = 2,  /* a shape the method allows but this library does
+                          * not implement (N a multiple of 64 but not of 128;
+                          * NVFP4 K a multiple of 16 but not of 128; a W4A16
+                          * activation array of 2^31 bytes or more)          */
+  FGG_EALIGN = 3,        /* a pointer is not 16-byte aligned (4 for scales)   */
+  FGG_EDEVICE = 4,       /* no HIP device, or the current device is not gfx950 */
+  FGG_EHIP = 5           /* a HIP runtime call or kernel launch failed        */
 } fgg_status;
 
 /* Message for the last non-OK status returned on this thread ("" if none).
@@ -71,10 +78,13 @@ const char* fgg_last_error(void);
  *   C[i, :] = 0 when g is -1 (or out of range).
  *   Accumulation is FP32; the BF16 conversion rounds to nearest even.
  *
- * Requirements (else FGG_EINVAL / FGG_EALIGN): 1 <= M <= 2^24,
- * 128 <= N <= 2^19 with N % 128 == 0, 128 <= K <= 2^20 with K % 128 == 0,
- * 1 <= G <= 2^16, every pointer non-null and 16-byte aligned (a_scale,
- * b_scale and m_indices: 4-byte aligned).
+ * Requirements: 1 <= M <= 2^24, 64 <= N <= 2^19 with N % 64 == 0,
+ * 128 <= K <= 2^20 with K % 128 == 0, 1 <= G <= 2^16, every pointer
+ * non-null (else FGG_EINVAL); N % 128 == 0, whole b_scale blocks (else
+ * FGG_EUNSUPPORTED); A, B and C 16-byte aligned, a_scale, b_scale and
+ * m_indices 4-byte aligned (else FGG_EALIGN).  Rows of A whose m_indices
+ * entry is -1 (or out of range) may hold any bytes: they never reach a
+ * stored output.
  */
 fgg_status grouped_fp8_gemm(const void* A, const void* B, const float* a_scale,
                             const float* b_scale, const int32_t* m_indices, void* C,
@@ -92,8 +102,11 @@ fgg_status grouped_fp8_gemm(const void* A, const void* B, const float* a_scale,
  *
  *   C[i, n] = bf16( alpha * sum_k (A[i,k] a_scale[i,k/16]) (B[n,k] b_scale[n,k/16]) )
  *
- * Requirements: 1 <= M <= 2^24, 128 <= N <= 2^19 with N % 128 == 0,
- * 128 <= K <= 2^20 with K % 128 == 0, pointers non-null and 16-byte aligned.
+ * Requirements: 1 <= M <= 2^24, 64 <= N <= 2^19 with N % 64 == 0,
+ * 16 <= K <= 2^20 with K % 16 == 0 (whole scale blocks), pointers non-null
+ * (else FGG_EINVAL); N % 128 == 0 and K % 128 == 0 (else FGG_EUNSUPPORTED);
+ * pointers 16-byte aligned (else FGG_EALIGN).  A scale code that is an
+ * E4M3FN NaN (0x7F / 0xFF) makes every output it reaches NaN.
  */
 fgg_status fp4_gemm(const void* A, const void* B, const void* a_scale, const void* b_scale,
                     float alpha, void* C, int M, int N, int K, void* stream);
@@ -170,8 +183,10 @@ fgg_status fp4_gemm_problems(const fgg_fp4_problem* problems, int count, void* s
  * bits) and multiplied with FP32 accumulation.  Built for few rows per expert
  * (decode): each expert's weights are read once per 16 of its rows, and an
  * expert with no rows costs no weight traffic.  Requirements as
- * grouped_fp4_gemm (A 16-byte aligned); b_global and A finite; M * K * 2 <
- * 2^31 (the activations of a decode batch).
+ * grouped_fp4_gemm (A 16-byte aligned); b_global finite; M * K * 2 < 2^31,
+ * the activations of a decode batch (else FGG_EUNSUPPORTED).  Rows routed
+ * to an expert must be finite; rows marked -1 (or out of range) may hold
+ * anything, as may the memory around A: neither is ever multiplied.
  */
 fgg_status grouped_w4a16_gemm(const void* A, const void* B, const void* b_scale,
                               const int32_t* m_indices, float b_global, void* C, int M, int N,
@@ -200,13 +215,15 @@ fgg_status grouped_w4a16_gemm(const void* A, const void* B, const void* b_scale,
  * quantize_nvfp4_static -- the same encoding with the global scale g given by
  * the caller (a calibrated, static activation scale; the NVFP4 format has one
  * FP32 scale per tensor, and how it is chosen is left open by the pages)
- * instead of amax(X) / 2688: one kernel launch that reads X once.  Values whose block amax exceeds
- * 448 * 6 * g saturate (block scale 448, codes clamped to +-6).  g must be a
+ * instead of amax(X) / 2688: one kernel launch that reads X once.  Values
+ * whose block amax exceeds 448 * 6 * g saturate (block scale 448, codes clamped to +-6).  g must be a
  * finite normal positive float (FGG_EINVAL otherwise).
  *
- * Requirements: X, Q 16-byte aligned (scale: 4-byte for FP8, any for NVFP4;
- * the global_scale pointer of quantize_nvfp4 4-byte); 1 <= M <= 2^24; 128 <= K <= 2^20, K % 128 == 0; X
- * finite.  Errors as for the GEMMs.
+ * Requirements: 1 <= M <= 2^24; 128 <= K <= 2^20 with K % 128 == 0 for
+ * FP8 (FGG_EINVAL otherwise); for NVFP4 16 <= K <= 2^20 with K % 16 == 0
+ * (FGG_EINVAL) and K % 128 == 0 (FGG_EUNSUPPORTED); X, Q 16-byte aligned
+ * (scale: 4-byte for FP8, any for NVFP4; the global_scale pointer of
+ * quantize_nvfp4 4-byte; FGG_EALIGN); X finite.
  * ------------------------------------------------------------------------ */
 fgg_status quantize_fp8_1x128(const void* X, void* Q, float* scale, int M, int K, void* stream);
 fgg_status quantize_nvfp4(const void* X, void* Q, void* scale, float* global_scale, int M, int K,
@@ -303,9 +320,12 @@ fgg_status fp4_gemm_problems_ex(const fgg_fp4_problem* problems, int count,
  * device.  Timing: three rounds that visit the configs in turn, each visit
  * one untimed launch and then `reps` launches between two HIP events on
  * `stream`; a config's time is its fastest round (so no config pays for the
- * clock ramp of a GPU coming out of idle, whatever its place in the order).  Later calls of that GEMM on that shape with
- * no explicit tile_id launch the recorded config instead of the ranker's
- * top one.  C is overwritten (with the GEMM's result).  The call
+ * clock ramp of a GPU coming out of idle, whatever its place in the order).
+ * Later calls of that GEMM on that shape with no explicit tile_id launch the
+ * recorded config instead of the ranker's top one.  `opt` (may be NULL) is
+ * read as by the *_ex calls: run_align shapes the ranking the candidates
+ * come from, max_workgroups and run_split apply to every timed launch, and
+ * tile_id must be -1 (the tuning chooses it; FGG_EINVAL otherwise).  C is overwritten (with the GEMM's result).  The call
  * synchronises `stream` and is not graph-capturable; it allocates no device
  * memory.  `report` (may be NULL) receives the candidates in ranker order
  * with their milliseconds per launch.  Recorded choices are process-wide
@@ -323,14 +343,15 @@ typedef struct {
 fgg_status grouped_fp8_gemm_tune(const void* A, const void* B, const float* a_scale,
                                  const float* b_scale, const int32_t* m_indices, void* C, int M,
                                  int N, int K, int G, int top_k, int reps,
-                                 fgg_tune_report* report, void* stream);
+                                 fgg_tune_report* report, const fgg_options* opt, void* stream);
 fgg_status fp4_gemm_tune(const void* A, const void* B, const void* a_scale, const void* b_scale,
                          float alpha, void* C, int M, int N, int K, int top_k, int reps,
-                         fgg_tune_report* report, void* stream);
+                         fgg_tune_report* report, const fgg_options* opt, void* stream);
 fgg_status grouped_fp4_gemm_tune(const void* A, const void* B, const void* a_scale,
                                  const void* b_scale, const int32_t* m_indices, float alpha,
                                  void* C, int M, int N, int K, int G, int top_k, int reps,
-                                 fgg_tune_report* report, void* stream);
+                                 fgg_tune_report* report, const fgg_options* opt,
+                                 void* stream);
 
 /* The recorded config for a shape on the current device (kind as
  * fgg_rank_tiles; G = 1 for fp4_gemm), or -1 when none is recorded. */

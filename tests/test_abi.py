@@ -31,6 +31,20 @@ def test_library_exports_every_declared_function():
     assert not missing
 
 
+def test_status_values():
+    """The status codes of the C ABI, by name and number, as the header
+    defines them (the binding's named-check convention of the flashinfer#7877
+    page, "Code analysis 1", with one status per kind of failure)."""
+    src = open(os.path.join(ROOT, "include", "fgg.h")).read()
+    body = src[src.index("typedef enum {"):src.index("} fgg_status;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    vals = dict((k, int(v)) for k, v in re.findall(r"(FGG_\w+)\s*=\s*(\d+)", body))
+    assert vals == {"FGG_OK": 0, "FGG_EINVAL": 1, "FGG_EUNSUPPORTED": 2, "FGG_EALIGN": 3,
+                    "FGG_EDEVICE": 4, "FGG_EHIP": 5}
+    assert (fgg.OK, fgg.EINVAL, fgg.EUNSUPPORTED, fgg.EALIGN, fgg.EDEVICE, fgg.EHIP) == \
+        (0, 1, 2, 3, 4, 5)
+
+
 P = 0x10000  # a 16-byte aligned non-null address; never dereferenced: each
 # call below fails validation before anything touches a device.
 
@@ -46,14 +60,16 @@ def _fp8(A=P, B=P, sa=P, sb=P, mi=P, C=P, M=256, N=256, K=512, G=2):
     (dict(mi=0), 1, "m_indices"),
     (dict(M=0), 1, "M"),
     (dict(M=(1 << 24) + 1), 1, "M"),
-    (dict(N=64), 1, "N"),
-    (dict(N=200), 1, "N % 128"),
+    (dict(N=32), 1, "64 <= N"),
+    (dict(N=200), 1, "N % 64"),
+    (dict(N=64), 2, "N % 128"),
+    (dict(N=192), 2, "N % 128"),
     (dict(K=200), 1, "K % 128"),
     (dict(K=64), 1, "K"),
     (dict(G=0), 1, "G"),
-    (dict(A=P + 8), 2, "aligned"),
-    (dict(C=P + 2), 2, "aligned"),
-    (dict(sa=P + 2), 2, "aligned"),
+    (dict(A=P + 8), 3, "aligned"),
+    (dict(C=P + 2), 3, "aligned"),
+    (dict(sa=P + 2), 3, "aligned"),
 ])
 def test_fp8_validation(kw, status, needle):
     st, msg = _fp8(**kw)
@@ -64,13 +80,15 @@ def test_fp8_validation(kw, status, needle):
 def test_fp4_validation():
     lib = fgg.load_library()
     st = lib.fp4_gemm(P, P, P, P, 1.0, P, 100, 256, 144, None)
-    assert st == 1 and "K % 128" in lib.fgg_last_error().decode()
+    assert st == 2 and "K % 128" in lib.fgg_last_error().decode()
+    st = lib.fp4_gemm(P, P, P, P, 1.0, P, 100, 256, 136, None)
+    assert st == 1 and "K % 16" in lib.fgg_last_error().decode()
     st = lib.fp4_gemm(P, P, P, P, float("inf"), P, 100, 256, 128, None)
     assert st == 1 and "alpha" in lib.fgg_last_error().decode()
     st = lib.grouped_fp4_gemm(P, P, P, P, 0, 1.0, P, 100, 256, 128, 2, None)
     assert st == 1 and "m_indices" in lib.fgg_last_error().decode()
     st = lib.grouped_fp4_gemm(P, P, P + 4, P, P, 1.0, P, 100, 256, 128, 2, None)
-    assert st == 2
+    assert st == 3
 
 
 def test_quantizer_validation():
@@ -78,15 +96,16 @@ def test_quantizer_validation():
     st = lib.quantize_fp8_1x128(P, P, P, 8, 200, None)
     assert st == 1 and lib.fgg_last_error().decode().startswith("quantize_fp8_1x128:")
     assert lib.quantize_fp8_1x128(0, P, P, 8, 256, None) == 1
-    assert lib.quantize_fp8_1x128(P, P, P + 2, 8, 256, None) == 2
-    assert lib.quantize_fp8_1x128(P + 4, P, P, 8, 256, None) == 2
+    assert lib.quantize_fp8_1x128(P, P, P + 2, 8, 256, None) == 3
+    assert lib.quantize_fp8_1x128(P + 4, P, P, 8, 256, None) == 3
     assert lib.quantize_fp8_1x128(P, P, P, 0, 256, None) == 1
     st = lib.quantize_nvfp4(P, P, P, 0, 8, 256, None)
     assert st == 1 and "global_scale" in lib.fgg_last_error().decode()
-    assert lib.quantize_nvfp4(P, P, P, P + 2, 8, 256, None) == 2
-    assert lib.quantize_nvfp4(P, P + 8, P, P, 8, 256, None) == 2
+    assert lib.quantize_nvfp4(P, P, P, P + 2, 8, 256, None) == 3
+    assert lib.quantize_nvfp4(P, P + 8, P, P, 8, 256, None) == 3
     assert lib.quantize_nvfp4_static(P, P, P, 1.0, 8, 200, None) == 1
-    assert lib.quantize_nvfp4_static(P, P + 8, P, 1.0, 8, 256, None) == 2
+    assert lib.quantize_nvfp4_static(P, P, P, 1.0, 8, 144, None) == 2
+    assert lib.quantize_nvfp4_static(P, P + 8, P, 1.0, 8, 256, None) == 3
     for g in (0.0, -1.0, float("nan"), float("inf"), 1e-40):
         st = lib.quantize_nvfp4_static(P, P, P, g, 8, 256, None)
         assert st == 1 and "global_scale" in lib.fgg_last_error().decode()
@@ -98,13 +117,24 @@ def test_tune_validation_and_cache_without_gpu():
     answers -1, and clearing it is always allowed."""
     lib = fgg.load_library()
     rep = fgg._TuneReport()
-    st = lib.grouped_fp8_gemm_tune(P, P, P, P, P, P, 256, 256, 200, 2, 4, 5, ctypes.byref(rep), None)
+    st = lib.grouped_fp8_gemm_tune(P, P, P, P, P, P, 256, 256, 200, 2, 4, 5, ctypes.byref(rep),
+                                   None, None)
     msg = lib.fgg_last_error().decode()
     assert st == 1 and msg.startswith("grouped_fp8_gemm_tune:") and "K % 128" in msg
-    st = lib.fp4_gemm_tune(P, P, P, P, float("nan"), P, 100, 256, 128, 4, 5, None, None)
+    st = lib.fp4_gemm_tune(P, P, P, P, float("nan"), P, 100, 256, 128, 4, 5, None, None, None)
     assert st == 1 and "alpha" in lib.fgg_last_error().decode()
-    st = lib.grouped_fp4_gemm_tune(P, P, P, P, 0, 1.0, P, 100, 256, 128, 2, 4, 5, None, None)
+    st = lib.grouped_fp4_gemm_tune(P, P, P, P, 0, 1.0, P, 100, 256, 128, 2, 4, 5, None, None,
+                                   None)
     assert st == 1 and lib.fgg_last_error().decode().startswith("grouped_fp4_gemm_tune:")
+    # the tuning chooses the tile: an explicit one is an error (before any device call)
+    opt = fgg._Options(0, 0, 0, 128)
+    st = lib.grouped_fp8_gemm_tune(P, P, P, P, P, P, 256, 256, 512, 2, 4, 5, None,
+                                   ctypes.byref(opt), None)
+    assert st == 1 and "tile_id" in lib.fgg_last_error().decode()
+    opt = fgg._Options(-1, 0, 0, -4)
+    st = lib.grouped_fp4_gemm_tune(P, P, P, P, P, 1.0, P, 100, 256, 128, 2, 4, 5, None,
+                                   ctypes.byref(opt), None)
+    assert st == 1 and "run_align" in lib.fgg_last_error().decode()
     assert lib.fgg_tuned_tile(fgg.FP8, 256, 256, 512, 2) == -1
     lib.fgg_tune_clear()
     assert fgg.tuned_tile(fgg.FP4, 2048, 36864, 4608) == -1
@@ -121,17 +151,17 @@ def test_problem_batch_and_expert_alpha_validation():
     arr[1].K = 200
     st = lib.fp4_gemm_problems(arr, 3, None)
     msg = lib.fgg_last_error().decode()
-    assert st == 1 and "problem 1" in msg and "K % 128" in msg
+    assert st == 1 and "problem 1" in msg and "K % 16" in msg
     arr[1].K = 512
     arr[2].alpha = float("inf")
     st = lib.fp4_gemm_problems(arr, 3, None)
     assert st == 1 and "problem 2" in lib.fgg_last_error().decode()
     arr[2].alpha = 1.0
     arr[0].C = P + 4
-    assert lib.fp4_gemm_problems(arr, 3, None) == 2
+    assert lib.fp4_gemm_problems(arr, 3, None) == 3
     st = lib.grouped_fp4_gemm_alpha(P, P, P, P, P, 0, P, 100, 256, 128, 2, None)
     assert st == 1 and "alpha" in lib.fgg_last_error().decode()
-    assert lib.grouped_fp4_gemm_alpha(P, P, P, P, P, P + 2, P, 100, 256, 128, 2, None) == 2
+    assert lib.grouped_fp4_gemm_alpha(P, P, P, P, P, P + 2, P, 100, 256, 128, 2, None) == 3
     st = lib.grouped_fp4_gemm_alpha(P, P, P, P, P, P, P, 100, 256, 100, 2, None)
     assert st == 1 and lib.fgg_last_error().decode().startswith("grouped_fp4_gemm_alpha:")
 
@@ -140,9 +170,13 @@ def test_w4a16_validation():
     lib = fgg.load_library()
     st = lib.grouped_w4a16_gemm(P, P, P, P, 1.0, P, 16, 256, 200, 2, None)
     msg = lib.fgg_last_error().decode()
-    assert st == 1 and msg.startswith("grouped_w4a16_gemm:") and "K % 128" in msg
+    assert st == 1 and msg.startswith("grouped_w4a16_gemm:") and "K % 16" in msg
+    st = lib.grouped_w4a16_gemm(P, P, P, P, 1.0, P, 16, 256, 208, 2, None)
+    assert st == 2 and "K % 128" in lib.fgg_last_error().decode()
     assert lib.grouped_w4a16_gemm(P, P, P, 0, 1.0, P, 16, 256, 256, 2, None) == 1
-    assert lib.grouped_w4a16_gemm(P + 8, P, P, P, 1.0, P, 16, 256, 256, 2, None) == 2
+    assert lib.grouped_w4a16_gemm(P + 8, P, P, P, 1.0, P, 16, 256, 256, 2, None) == 3
+    st = lib.grouped_w4a16_gemm(P, P, P, P, 1.0, P, 1 << 20, 256, 1024, 2, None)
+    assert st == 2 and "2^31" in lib.fgg_last_error().decode()
     st = lib.grouped_w4a16_gemm(P, P, P, P, float("nan"), P, 16, 256, 256, 2, None)
     assert st == 1 and "b_global" in lib.fgg_last_error().decode()
 

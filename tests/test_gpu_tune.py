@@ -92,3 +92,22 @@ def test_run_align_changes_only_the_tile():
     assert_parity(p, run(p, d))
     with pytest.raises(ValueError):
         run(p, d, run_align=-128)
+
+
+def test_tune_takes_the_run_align_promise():
+    """The tuning ranks its candidates under the caller's run_align promise:
+    the first candidate is the aligned ranker's top tile, and the recorded
+    choice matches the oracle."""
+    counts = [128 * k for k in (5, 3, 9, 1, 6, 4, 2, 2)]
+    p = fp8_problem(runs_to_indices(counts), 1024, 256, 8, np.random.default_rng(12))
+    M, N, K, G = p["M"], p["N"], p["K"], p["G"]
+    ncu = fgg.device_info()["num_cus"]
+    aligned = [t["id"] for t in fgg.rank_tiles(fgg.FP8, M, N, K, G, num_cus=ncu, run_align=128)]
+    d = to_dev(p)
+    fgg.tune_clear()
+    log(f"tune with run_align=128 M={M} N={N} K={K} G={G}")
+    C, rep = _tune(p, d, top_k=2, reps=2, run_align=128)
+    assert rep["tile_id"] == aligned[:2]
+    assert_parity(p, C, what="tune with run_align")
+    assert fgg.tuned_tile(fgg.FP8, M, N, K, G) == rep["chosen"]
+    fgg.tune_clear()
