@@ -139,6 +139,14 @@ def algorithmic_bytes(p: dict) -> float:
         (0 if ids is None else M * 4)
 
 
+def host_threads():
+    """(cores this process may run on, BLAS threads the oracle's matrix
+    products use)."""
+    from threadpoolctl import threadpool_info
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return len(os.sched_getaffinity(0)), int(blas)
+
+
 def cpu_baseline(p: dict, C_gpu, seconds: float):
     """Time the oracle on a bounded row sample of the workload (chunks of
     rows in a seeded random order until ``seconds`` of CPU work or all rows),
@@ -146,7 +154,7 @@ def cpu_baseline(p: dict, C_gpu, seconds: float):
     import oracle
     from threadpoolctl import threadpool_info
 
-    from tests.gpu_util import c_to_f64, row_ids
+    from fp4_grouped_gemm_amd.util import c_to_f64, row_ids
     M = p["M"]
     order = np.random.default_rng(1).permutation(M)
     ids_all = row_ids(p)
@@ -172,9 +180,10 @@ def cpu_baseline(p: dict, C_gpu, seconds: float):
     ids = None if ids_all is None else ids_all[rows]
     real = int(rows.size if ids is None else np.count_nonzero(ids >= 0))
     flops = 2.0 * real * p["N"] * p["K"]
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    cores, blas = host_threads()
     res = oracle.check_tolerance(c_to_f64(C_gpu)[rows], ref, ids)
-    base = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOPS", "cores": int(threads),
+    base = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOPS", "cores": cores,
+            "blas_threads": blas,
             "kind": "oracle",
             "sample": f"{rows.size} of {M} rows ({real} non-padding) x all {p['N']} columns of "
                       f"the same workload, float64 NumPy/BLAS, {dt:.1f} s"}
@@ -422,10 +431,10 @@ def bench_quant(args, torch):
             if time.perf_counter() - t0 >= args.cpu_seconds:
                 break
         dt = time.perf_counter() - t0
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        cores, blas = host_threads()
         res["cpu_baseline"] = {
             "value": round(quant_bytes(kind, done, K) / dt / 1e9, 4), "unit": "GB/s",
-            "cores": int(threads), "kind": "oracle",
+            "cores": cores, "blas_threads": blas, "kind": "oracle",
             "sample": f"{done} of {M} rows of the same workload (NumPy float32 decisions, "
                       f"table-search encoders), {dt:.1f} s; the global scale from the GPU run"}
         res["parity_sample"] = {"rows": done, "ok": ok, "bitwise": True}
@@ -445,7 +454,7 @@ def bench_w4a16(args, torch):
     """Grouped W4A16 decode: HBM-bound on the weights; GB/s and µs."""
     import fp4_grouped_gemm_amd as fgg
     import oracle
-    from tests.gpu_util import c_to_f64
+    from fp4_grouped_gemm_amd.util import c_to_f64
     from workloads import make
 
     if not os.path.exists(fgg.library_path()):
@@ -495,9 +504,9 @@ def bench_w4a16(args, torch):
                                         p["b_global"])
         dt = time.perf_counter() - t0
         ok = oracle.check_tolerance(c_to_f64(C), ref, p["m_indices"])["ok"]
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        cores, blas = host_threads()
         res["cpu_baseline"] = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s",
-                               "cores": int(threads), "kind": "oracle",
+                               "cores": cores, "blas_threads": blas, "kind": "oracle",
                                "sample": f"the whole workload ({p['M']} rows), float64 "
                                          f"NumPy/BLAS, {dt:.1f} s"}
         res["parity_sample"] = {"rows": p["M"], "ok": bool(ok)}
@@ -509,7 +518,7 @@ def bench_problems(args, torch):
     fp4_gemm_problems launch per step."""
     import fp4_grouped_gemm_amd as fgg
     import oracle
-    from tests.gpu_util import c_to_f64, to_dev
+    from fp4_grouped_gemm_amd.util import c_to_f64, to_device as to_dev
     from workloads import make
 
     if not os.path.exists(fgg.library_path()):
@@ -570,9 +579,9 @@ def bench_problems(args, torch):
             if time.perf_counter() - t0 >= args.cpu_seconds:
                 break
         dt = time.perf_counter() - t0
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        cores, blas = host_threads()
         out["cpu_baseline"] = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOPS",
-                               "cores": int(threads), "kind": "oracle",
+                               "cores": cores, "blas_threads": blas, "kind": "oracle",
                                "sample": f"first {nrows} rows over the 8 problems x all columns, "
                                          f"float64 NumPy/BLAS, {dt:.1f} s"}
         out["parity_sample"] = {"rows": nrows, "ok": bool(ok)}
@@ -584,7 +593,7 @@ def tune_report(args, torch):
     workload (the measurement the flashinfer#3948 page reports: the top-1
     pick's loss and the geomean loss of tuning only the top candidates)."""
     import fp4_grouped_gemm_amd as fgg
-    from tests.gpu_util import to_dev
+    from fp4_grouped_gemm_amd.util import to_device as to_dev
     from workloads import make
 
     if not os.path.exists(fgg.library_path()):
@@ -635,6 +644,116 @@ def tune_report(args, torch):
                       "geomean_loss": round(geo - 1.0, 4)}), flush=True)
 
 
+def bench_gemm(args, torch, workload: str, cold_launches: int, cpu_seconds: float,
+               primary: bool = True) -> dict:
+    """One GEMM workload: warm-up, the timed region, the cold-cache figure
+    (cold_launches > 0), the oracle baseline on a row sample (cpu_seconds >
+    0); returns the result record.  The launch options of the command line
+    (--tile, --run-split, --max-workgroups, --autotune) apply to the primary
+    workload only."""
+    import fp4_grouped_gemm_amd as fgg
+    from fp4_grouped_gemm_amd.util import run, to_device as to_dev
+    from workloads import make
+    from workloads.gen import real_rows
+
+    if not os.path.exists(fgg.library_path()):
+        from fp4_grouped_gemm_amd.build import build
+        build()
+    print(f"[bench] generating {workload}", file=sys.stderr, flush=True)
+    p = make(workload)
+    d = to_dev(p)
+    kind = WORKLOADS[workload]["kind"]
+    M, N, K, G = p["M"], p["N"], p["K"], p["G"]
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    tile = args.tile if primary else None
+    kw = {} if tile is None else {"tile_id": tile}
+    if primary and args.run_split and p.get("m_indices") is not None:
+        kw["run_split"] = args.run_split
+    if primary and args.max_workgroups:
+        kw["max_workgroups"] = args.max_workgroups
+    # the workload's routing promise (its runs start on multiples of this)
+    run_align = WORKLOADS[workload].get("run_align", 0) if not args.no_run_align else 0
+    if run_align and p.get("m_indices") is not None:
+        kw["run_align"] = run_align
+    tuned = None
+    if primary and args.autotune and tile is None:
+        # the library's bounded autotune, once, untimed: later calls of this
+        # shape launch the config it recorded
+        print("[bench] autotune", file=sys.stderr, flush=True)
+        fgg.tune_clear()
+        tk = dict(top_k=args.top_k, reps=5)
+        if kind == "fp8":
+            _, tuned = fgg.grouped_fp8_gemm_tune(d["A"], d["B"], d["a_scale"], d["b_scale"],
+                                                 d["m_indices"], out=C, **tk)
+        elif p.get("m_indices") is None:
+            _, tuned = fgg.fp4_gemm_tune(d["A"], d["B"], d["a_scale"], d["b_scale"], p["alpha"],
+                                         out=C, **tk)
+        else:
+            _, tuned = fgg.grouped_fp4_gemm_tune(d["A"], d["B"], d["a_scale"], d["b_scale"],
+                                                 d["m_indices"], p["alpha"], out=C, **tk)
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        run(p, d, out=C, **kw)
+    ms, ms_other = time_modes(torch, lambda: run(p, d, out=C, **kw), args.steps, args.timing,
+                             args.single_timing)
+    ms_launch = ms
+    rr = real_rows(p)
+    flops = 2.0 * rr * N * K
+    cold = (cold_cache_entry(torch, lambda: run(p, d, out=C, **kw), args, flops, "TFLOPS", 1e-12)
+            if cold_launches > 0 else None)
+    tflops = flops / (ms * 1e-3) / 1e12
+    tflops_launch = flops / (ms_launch * 1e-3) / 1e12
+    # the MFMA the kernel issues (the exact NVFP4 path runs FP16 MFMAs), and
+    # the peak the fraction is priced against: the input format's own dense
+    # peak (FP8 for FP8, FP4 for NVFP4), with the FP16 fraction kept beside
+    # it for NVFP4 -- the exact path cannot exceed 2.5 / 10.1 of the FP4 peak
+    mma = "fp8" if kind == "fp8" else "fp16"
+    peak_kind = "fp8" if kind == "fp8" else "fp4"
+    src = kernel_source_hash(workload)
+    traffic = measured_traffic(workload, src)
+    tiles = fgg.rank_tiles(fgg.FP8 if kind == "fp8" else fgg.FP4, M, N, K, G,
+                           num_cus=fgg.device_info()["num_cus"], run_align=kw.get("run_align", 0))
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3" if kind == "fp8" else "nvfp4_e2m1",
+        "data": "synthetic (seeded NumPy; quantised on the host, resident in HBM)",
+        "config": {"workload": workload, "desc": WORKLOADS[workload]["desc"],
+                   "M": M, "N": N, "K": K, "G": G, "real_rows": rr,
+                   "tile": (tile if tile is not None
+                            else tuned["chosen"] if tuned else tiles[0]["id"]),
+                   "tile_choice": ("given" if tile is not None
+                                   else "bounded autotune" if tuned else "ranker"),
+                   "run_split": kw.get("run_split", 0),
+                   "max_workgroups": kw.get("max_workgroups", 0),
+                   "run_align": kw.get("run_align", 0),
+                   "timing": TIMING[args.timing], "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops_launch, 2),
+                     "peak": PEAK[peak_kind], "peak_dtype": peak_kind,
+                     "unit": "TFLOP/s", "frac": round(tflops_launch / PEAK[peak_kind], 4),
+                     "traffic": traffic, "mfma_dtype": mma,
+                     "algorithmic_bytes": algorithmic_bytes(p),
+                     "hbm_gbps_algorithmic": round(algorithmic_bytes(p) / (ms_launch * 1e-3) / 1e9, 1),
+                     "us_per_launch": round(ms_launch * 1e3, 2)},
+        "kernel_source_sha": src,
+    }
+    out["ms_per_step_" + OTHER[args.timing]] = (None if ms_other is None
+                                                   else round(ms_other, 5))
+    out["cold_cache"] = cold
+    if kind == "fp4":
+        out["roofline"]["frac_of_fp16_peak"] = round(tflops_launch / PEAK["fp16"], 4)
+    if cpu_seconds > 0:
+        print(f"[bench] cpu baseline (oracle on a row sample of {workload})", file=sys.stderr,
+              flush=True)
+        base, parity = cpu_baseline(p, C, cpu_seconds)
+        out["cpu_baseline"] = base
+        out["parity_sample"] = parity
+    del d, C
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -674,6 +793,10 @@ def main():
                     help="fgg_options.run_split (0 automatic, -1 never, 1 always)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-nvfp4", action="store_true",
+                    help="default workload only: skip the NVFP4 sub-records (c4, c5)")
+    ap.add_argument("--nvfp4-cpu-seconds", type=float, default=8.0,
+                    help="CPU time budget of each NVFP4 sub-record's oracle sample")
     ap.add_argument("--rocprof-summary", default=None, metavar="DIR",
                     help="summarise rocprofv3 CSV output in DIR (see rocprof_summary) and exit")
     ap.add_argument("--kernel", default="fp8_grouped_kernel",
@@ -729,100 +852,20 @@ def main():
         bench_quant(args, torch)
         return
 
-    import fp4_grouped_gemm_amd as fgg
-    from tests.gpu_util import run, to_dev
-    from workloads import make
-    from workloads.gen import real_rows
-
-    if not os.path.exists(fgg.library_path()):
-        from fp4_grouped_gemm_amd.build import build
-        build()
-    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
-    p = make(args.workload)
-    d = to_dev(p)
-    kind = WORKLOADS[args.workload]["kind"]
-    M, N, K, G = p["M"], p["N"], p["K"], p["G"]
-    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    kw = {} if args.tile is None else {"tile_id": args.tile}
-    if args.run_split and p.get("m_indices") is not None:
-        kw["run_split"] = args.run_split
-    if args.max_workgroups:
-        kw["max_workgroups"] = args.max_workgroups
-    # the workload's routing promise (its runs start on multiples of this)
-    run_align = WORKLOADS[args.workload].get("run_align", 0) if not args.no_run_align else 0
-    if run_align and p.get("m_indices") is not None:
-        kw["run_align"] = run_align
-    tuned = None
-    if args.autotune and args.tile is None:
-        # the library's bounded autotune, once, untimed: later calls of this
-        # shape launch the config it recorded
-        print("[bench] autotune", file=sys.stderr, flush=True)
-        fgg.tune_clear()
-        tk = dict(top_k=args.top_k, reps=5)
-        if kind == "fp8":
-            _, tuned = fgg.grouped_fp8_gemm_tune(d["A"], d["B"], d["a_scale"], d["b_scale"],
-                                                 d["m_indices"], out=C, **tk)
-        elif p.get("m_indices") is None:
-            _, tuned = fgg.fp4_gemm_tune(d["A"], d["B"], d["a_scale"], d["b_scale"], p["alpha"],
-                                         out=C, **tk)
-        else:
-            _, tuned = fgg.grouped_fp4_gemm_tune(d["A"], d["B"], d["a_scale"], d["b_scale"],
-                                                 d["m_indices"], p["alpha"], out=C, **tk)
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        run(p, d, out=C, **kw)
-    ms, ms_other = time_modes(torch, lambda: run(p, d, out=C, **kw), args.steps, args.timing,
-                             args.single_timing)
-    ms_launch = ms
-    rr = real_rows(p)
-    flops = 2.0 * rr * N * K
-    cold = cold_cache_entry(torch, lambda: run(p, d, out=C, **kw), args, flops, "TFLOPS", 1e-12)
-    tflops = flops / (ms * 1e-3) / 1e12
-    tflops_launch = flops / (ms_launch * 1e-3) / 1e12
-    # the MFMA the kernel issues (the exact NVFP4 path runs FP16 MFMAs), and
-    # the peak the fraction is priced against: the input format's own dense
-    # peak (FP8 for FP8, FP4 for NVFP4), with the FP16 fraction kept beside
-    # it for NVFP4 -- the exact path cannot exceed 2.5 / 10.1 of the FP4 peak
-    mma = "fp8" if kind == "fp8" else "fp16"
-    peak_kind = "fp8" if kind == "fp8" else "fp4"
-    src = kernel_source_hash(args.workload)
-    traffic = measured_traffic(args.workload, src)
-    tiles = fgg.rank_tiles(fgg.FP8 if kind == "fp8" else fgg.FP4, M, N, K, G,
-                           num_cus=fgg.device_info()["num_cus"], run_align=kw.get("run_align", 0))
-    out = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8_e4m3" if kind == "fp8" else "nvfp4_e2m1",
-        "data": "synthetic (seeded NumPy; quantised on the host, resident in HBM)",
-        "config": {"workload": args.workload, "desc": WORKLOADS[args.workload]["desc"],
-                   "M": M, "N": N, "K": K, "G": G, "real_rows": rr,
-                   "tile": (args.tile if args.tile is not None
-                            else tuned["chosen"] if tuned else tiles[0]["id"]),
-                   "tile_choice": ("given" if args.tile is not None
-                                   else "bounded autotune" if tuned else "ranker"),
-                   "run_split": args.run_split, "max_workgroups": args.max_workgroups,
-                   "run_align": kw.get("run_align", 0),
-                   "timing": TIMING[args.timing], "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(tflops_launch, 2),
-                     "peak": PEAK[peak_kind], "peak_dtype": peak_kind,
-                     "unit": "TFLOP/s", "frac": round(tflops_launch / PEAK[peak_kind], 4),
-                     "traffic": traffic, "mfma_dtype": mma,
-                     "algorithmic_bytes": algorithmic_bytes(p),
-                     "hbm_gbps_algorithmic": round(algorithmic_bytes(p) / (ms_launch * 1e-3) / 1e9, 1),
-                     "us_per_launch": round(ms_launch * 1e3, 2)},
-        "kernel_source_sha": src,
-    }
-    out["ms_per_step_" + OTHER[args.timing]] = (None if ms_other is None
-                                                   else round(ms_other, 5))
-    out["cold_cache"] = cold
-    if kind == "fp4":
-        out["roofline"]["frac_of_fp16_peak"] = round(tflops_launch / PEAK["fp16"], 4)
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
-        base, parity = cpu_baseline(p, C, args.cpu_seconds)
-        out["cpu_baseline"] = base
-        out["parity_sample"] = parity
+    out = bench_gemm(args, torch, args.workload, args.cold_launches,
+                     0.0 if args.no_cpu_baseline else args.cpu_seconds)
+    if args.workload == "c2_moe_fp8" and not args.no_nvfp4:
+        # the NVFP4 half of the metric: the dense (flashinfer#3948 page's
+        # mm_fp4 review shape) and grouped W4A4 (onnxruntime#29824 page)
+        # workloads, each timed the same way, as sub-records of the one line
+        out["nvfp4"] = {}
+        for w in ("c4_dense_nvfp4", "c5_moe_nvfp4"):
+            sub = bench_gemm(args, torch, w, 0,
+                             0.0 if args.no_cpu_baseline else args.nvfp4_cpu_seconds,
+                             primary=False)
+            for k in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data"):
+                sub.pop(k, None)
+            out["nvfp4"][w] = sub
     print(json.dumps(out), flush=True)
 
 

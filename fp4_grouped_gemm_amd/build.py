@@ -43,6 +43,23 @@ def _compile(src: str) -> str:
     return out
 
 
+PROBE_SRC = os.path.join(ROOT, "bench", "mfma_peak.hip")
+PROBE = os.path.join(ROOT, "bench", "mfma_peak")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Build the roofline microbenchmark bench/mfma_peak (a standalone HIP
+    program; not part of the library)."""
+    cmd = [HIPCC, *[f for f in FLAGS if f not in ("-fPIC",) and not f.startswith("-I")],
+           PROBE_SRC, "-o", PROBE]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print("built", PROBE)
+    return PROBE
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:

@@ -59,23 +59,12 @@ struct Fp4Cfg {
 
 __device__ __forceinline__ int swz(int r, int c) { return (r << 7) | ((c ^ (r & 7)) << 4); }
 
-// Two E4M3FN codes (bytes 0 and 1 of `sc`) -> their values as an FP16 pair.
-// Exact: E4M3 has 4 significant bits and spans 2^-9..448.  The code's bits
-// are placed into the FP16 fields (exponent bits at the bottom of FP16's
-// exponent, mantissa at the top of its mantissa, subnormals to subnormals),
-// which gives the value times 2^-8 in both the normal and the subnormal
-// range; one multiply by 256 restores it.  The NaN codes S.1111.111 (E4M3FN
-// has no infinities) would come out as +-480: for them the FP16 exponent
-// and top mantissa bit are set afterwards (OR 0x7E00), which makes the
-// half a NaN whatever its other bits.  A code's low 7 bits plus one carry
-// into bit 7 exactly when they are all ones.
+// Two E4M3FN codes (bytes 0 and 1 of `sc`) -> their values as an FP16 pair,
+// with the hardware's pair convert at scale 1.0: exact (E4M3 has 4
+// significant bits and spans 2^-9..448, all FP16 numbers), and the NaN codes
+// S.1111.111 (E4M3FN has no infinities) come out as FP16 NaNs.
 __device__ __forceinline__ f16x2 e4m3x2_to_f16x2(uint32_t sc) {
-  const uint32_t x = (sc & 0xFFu) | ((sc & 0xFF00u) << 8);
-  const uint32_t mag = x & 0x007F007Fu;
-  const uint32_t bits = (mag << 7) | ((x & 0x00800080u) << 8);
-  const uint32_t nan = (((mag + 0x00010001u) & 0x00800080u) >> 7) * 0x7E00u;
-  const f16x2 v = __builtin_bit_cast(f16x2, bits) * (f16x2){(_Float16)256.0f, (_Float16)256.0f};
-  return __builtin_bit_cast(f16x2, __builtin_bit_cast(uint32_t, v) | nan);
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
 }
 
 // One 32-bit word (8 E2M1 codes, low nibble first) times its block scale ->
@@ -145,26 +134,22 @@ struct Pass {
   }
 
   // Issue the loads of the scale codes of steps [4c, 4c + 4) into group
-  // `grp`: bytes [16c, 16c + 16) of the row's K / 16 codes, as two 8-byte
-  // loads (K / 16 is a multiple of 8, so each half lies inside the row or
-  // wholly past its end).  Each offset, row included, is a VGPR offset, so
-  // the range check sees it: a half past the row's last code, or a row past
-  // the tile's last row, loads zeros without touching memory.  Codes past
-  // the last step are never used.
-  __device__ __forceinline__ i32x4 load_scale_group(__amdgpu_buffer_rsrc_t r, uint32_t row_off,
-                                                    int c, uint32_t Ks) const {
-    const uint32_t b0 = (uint32_t)c * 16u, b1 = b0 + 8u;
-    const i32x2 lo = __builtin_bit_cast(
-        i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, b0 < Ks ? row_off + b0 : kSkip, 0, 0));
-    const i32x2 hi = __builtin_bit_cast(
-        i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, b1 < Ks ? row_off + b1 : kSkip, 0, 0));
-    return (i32x4){lo[0], lo[1], hi[0], hi[1]};
-  }
-  __device__ __forceinline__ void load_scales(int grp, int c, uint32_t Ks) {
+  // `grp`: bytes [16c, 16c + 16) of the row's K / 16 codes, one 16-byte load
+  // per unit with the whole offset (row and group) in the VGPR offset, which
+  // the buffer range check covers dword by dword: a row's half-full last
+  // group (K / 16 an odd multiple of 8) reads the next row's first codes,
+  // or zeros past the tile's last row, never memory past the buffer.  Codes
+  // past the last step are never used.
+  __device__ __forceinline__ void load_scales(int grp, int c) {
+    const uint32_t cb = (uint32_t)c * 16u;
 #pragma unroll
-    for (int u = 0; u < T::A_UNITS; ++u) sa4[grp][u] = load_scale_group(rsa, pas_off[u], c, Ks);
+    for (int u = 0; u < T::A_UNITS; ++u)
+      sa4[grp][u] = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rsa, pas_off[u] + cb, 0, 0));
 #pragma unroll
-    for (int u = 0; u < T::B_UNITS; ++u) sb4[grp][u] = load_scale_group(rsb, bs_off[u], c, Ks);
+    for (int u = 0; u < T::B_UNITS; ++u)
+      sb4[grp][u] = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, bs_off[u] + cb, 0, 0));
   }
 
   // Chunk c of this thread's staging work for a step whose packed codes are
@@ -253,7 +238,7 @@ __device__ __forceinline__ bool kstep(Pass<T>& ps, uint8_t* lds0, uint8_t* lds1,
                                       int tid, int lane, int wm, int wn) {
   if (Q > 0 && ks + Q >= nks) return false;
   ps.load(Q & 1, min(ks + Q + 2, nks - 1));
-  if constexpr (Q % 4 == 0) ps.load_scales((Q / 4 + 1) & 1, (ks + Q) / 4 + 1, (uint32_t)nks * 4u);
+  if constexpr (Q % 4 == 0) ps.load_scales((Q / 4 + 1) & 1, (ks + Q) / 4 + 1);
   mma_step<T, true>(ps, (Q & 1) ? lds1 : lds0, (Q & 1) ? lds0 : lds1, (Q + 1) & 1,
                     ((Q + 1) / 4) & 1, (Q + 1) % 4, tid, lane, wm, wn);
   lds_barrier();
@@ -294,7 +279,7 @@ __device__ __forceinline__ void k_loop(Pass<T>& ps, uint8_t* lds0, uint8_t* lds1
                                        int lane, int wm, int wn) {
   ps.load(0, 0);
   ps.load(1, min(1, nks - 1));
-  ps.load_scales(0, 0, (uint32_t)nks * 4u);
+  ps.load_scales(0, 0);
   ps.stage_all(0, 0, 0, lds0, tid);
   lds_barrier();
   for (int ks = 0; ks < nks; ks += 8)

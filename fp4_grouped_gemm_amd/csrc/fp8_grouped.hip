@@ -35,8 +35,17 @@
 
 #include <climits>
 
+#ifndef FGG_FP8_PF
+#define FGG_FP8_PF 0
+#endif
+
 namespace fgg {
 namespace fp8_detail {
+
+// L2 prefetch distance: with 2 LDS stages, step kb stages step kb + 1 and
+// also touches one 4-byte word of every tile row of step kb + 1 + kPf, so
+// that row's 128-byte line is in L2 when its staging load comes (0: off).
+constexpr int kPf = FGG_FP8_PF;
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int SA_BLK_, int SA_ROW_>
 struct Fp8Cfg {
@@ -70,6 +79,9 @@ struct Fp8Cfg {
   static constexpr int VM_TILE = A_LOADS + B_LOADS;  // loads per step into the A/B ring
   static_assert(WAVES % 2 == 0, "the staging swizzle assumes an even wave count");
   static_assert(WM == 64 && BM <= 512, "one row per lane in the pass masks");
+  // L2 prefetch loads per wave per step (one row per lane; 2-stage shapes)
+  static constexpr int PF_LOADS = (kPf > 0 && STAGES == 2) ? (BM + BN) / 64 / WAVES : 0;
+  static_assert(PF_LOADS == 0 || (BM + BN) % (64 * WAVES) == 0, "prefetch split");
 };
 
 // LDS byte offset of 16-byte chunk `c` (0..7) of tile row `r`.  The chunk
@@ -162,6 +174,24 @@ struct Pass {
   __device__ __forceinline__ float b_scale_of(int kb) const {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bs_vec), kb & 63));
   }
+
+  // L2 prefetch of step kb's tile rows: instruction s of wave w covers row
+  // (s W + w) 64 + lane of [A rows; B rows], one 4-byte direct-to-LDS load
+  // into the wave's scratch slot (its value is never read).  A rows of other
+  // experts are skipped; rows past a tile fail the range check.
+  __device__ __forceinline__ void prefetch(uint8_t* scratch, int kb, int wave, int lane) const {
+#pragma unroll
+    for (int s = 0; s < T::PF_LOADS; ++s) {
+      const int r0 = (s * T::WAVES + wave) * 64;  // uniform
+      if (r0 < T::BM) {
+        const int r = r0 + lane;
+        const bool need = (a_groups >> (r >> 3)) & 1;
+        dma4(ra, lds_addr(scratch + wave * 256), need ? (uint32_t)r * K : kSkip, kb * 128);
+      } else {
+        dma4(rb, lds_addr(scratch + wave * 256), (uint32_t)(r0 - T::BM + lane) * K, kb * 128);
+      }
+    }
+  }
 };
 
 // One K step: start staging step kb + STAGES - 1 into `wr` (if any), then
@@ -173,7 +203,7 @@ struct Pass {
 template <class T>
 __device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* wr,
                                       const float* sa_rd, float* sa_wr, int kb, int lane, int wave,
-                                      int wm, int wn) {
+                                      int wm, int wn, uint8_t* pf_scratch) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   // this step's combined scales; read before any load of this step is issued
   const float sb = ps.b_scale_of(kb);
@@ -189,6 +219,10 @@ __device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* w
     ps.stage_in(wr, kl, wave);
     if (sload) ps.stage_scales(sa_wr, (unsigned)kb / T::SA_BLK + 1, wave, lane);
   }
+  // issued after this step's staging loads, so waiting for those leaves it
+  // in flight (loads complete in issue order)
+  const bool pf = T::PF_LOADS > 0 && kl + kPf < ps.nkb;
+  if (pf) ps.prefetch(pf_scratch, kl + kPf, wave, lane);
   // next chunk of 64 b_scale blocks after the last use of this one (rare:
   // K above 8192; the compiler's wait for it drains the loads in flight)
   if ((kb & 63) == 63 && kb + 1 < ps.nkb) ps.load_b_scales(kb + 1, lane);
@@ -230,8 +264,11 @@ __device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* w
   }
   }
   if constexpr (T::STAGES == 2) {
-    wait_vmem<0>();  // step kb + 1's tiles were issued in this step
-    __syncthreads();
+    // step kb + 1's tiles were issued in this step (the prefetch after them
+    // may stay in flight)
+    if (T::PF_LOADS > 0 && pf) wait_vmem<T::PF_LOADS>();
+    else wait_vmem<0>();
+    lds_barrier();
   } else {
     // Step kb + 1's tiles were issued one step ago: only this step's loads
     // may stay in flight.
@@ -256,6 +293,7 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
   __shared__ int ids[T::BM];
   __shared__ uint32_t plan_bits[kPlanWords];
   __shared__ int plan_heavy;
+  __shared__ __attribute__((aligned(256))) uint8_t pf_scratch[T::PF_LOADS > 0 ? T::WAVES * 256 : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -369,8 +407,8 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
           const bool odd_chunk = ((unsigned)kb / T::SA_BLK) & 1;
           float* sa_rd = odd_chunk ? sa1 : sa0;
           float* sa_wr = odd_chunk ? sa0 : sa1;
-          kstep<T>(ps, lds0, lds1, sa_rd, sa_wr, kb, lane, wave, wm, wn);
-          if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa_rd, sa_wr, kb + 1, lane, wave, wm, wn);
+          kstep<T>(ps, lds0, lds1, sa_rd, sa_wr, kb, lane, wave, wm, wn, pf_scratch);
+          if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa_rd, sa_wr, kb + 1, lane, wave, wm, wn, pf_scratch);
         }
       } else {
         if (nkb > 1) {
@@ -383,12 +421,12 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
         // Six steps per iteration: stage = kb % 3 and scale chunk kb / 3
         // (alternating sa0 / sa1) are then known at compile time.
         for (int kb = 0; kb < nkb; kb += 6) {
-          kstep<T>(ps, lds0, lds2, sa0, sa1, kb, lane, wave, wm, wn);
-          if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa0, sa1, kb + 1, lane, wave, wm, wn);
-          if (kb + 2 < nkb) kstep<T>(ps, lds2, lds1, sa0, sa1, kb + 2, lane, wave, wm, wn);
-          if (kb + 3 < nkb) kstep<T>(ps, lds0, lds2, sa1, sa0, kb + 3, lane, wave, wm, wn);
-          if (kb + 4 < nkb) kstep<T>(ps, lds1, lds0, sa1, sa0, kb + 4, lane, wave, wm, wn);
-          if (kb + 5 < nkb) kstep<T>(ps, lds2, lds1, sa1, sa0, kb + 5, lane, wave, wm, wn);
+          kstep<T>(ps, lds0, lds2, sa0, sa1, kb, lane, wave, wm, wn, pf_scratch);
+          if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa0, sa1, kb + 1, lane, wave, wm, wn, pf_scratch);
+          if (kb + 2 < nkb) kstep<T>(ps, lds2, lds1, sa0, sa1, kb + 2, lane, wave, wm, wn, pf_scratch);
+          if (kb + 3 < nkb) kstep<T>(ps, lds0, lds2, sa1, sa0, kb + 3, lane, wave, wm, wn, pf_scratch);
+          if (kb + 4 < nkb) kstep<T>(ps, lds1, lds0, sa1, sa0, kb + 4, lane, wave, wm, wn, pf_scratch);
+          if (kb + 5 < nkb) kstep<T>(ps, lds2, lds1, sa1, sa0, kb + 5, lane, wave, wm, wn, pf_scratch);
         }
       }
 

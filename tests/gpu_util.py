@@ -6,8 +6,10 @@ import sys
 
 import numpy as np
 
-import fp4_grouped_gemm_amd as fgg
+import fp4_grouped_gemm_amd as fgg  # noqa: F401
 import oracle
+from fp4_grouped_gemm_amd.util import c_to_f64, row_ids, run  # noqa: F401
+from fp4_grouped_gemm_amd.util import to_device as to_dev  # noqa: F401
 
 
 def log(msg: str):
@@ -16,35 +18,9 @@ def log(msg: str):
     sys.stdout.flush()
 
 
-def to_dev(p: dict):
-    import torch
-    d = {}
-    for k in ("A", "B", "a_scale", "b_scale", "m_indices"):
-        v = p.get(k)
-        d[k] = None if v is None else torch.from_numpy(np.ascontiguousarray(v)).cuda()
-    return d
-
-
-def c_to_f64(C) -> np.ndarray:
-    import torch
-    return C.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32).__lshift__(16) \
-        .view(np.float32).astype(np.float64)
-
-
 def c_bits(C) -> np.ndarray:
     import torch
     return C.view(torch.int16).cpu().numpy().view(np.uint16)
-
-
-def run(p: dict, d=None, **kw):
-    """Run the library on problem p (numpy dict) and return the C tensor."""
-    d = d or to_dev(p)
-    if p["kind"] == "fp8":
-        return fgg.grouped_fp8_gemm(d["A"], d["B"], d["a_scale"], d["b_scale"], d["m_indices"], **kw)
-    if p.get("m_indices") is None:
-        return fgg.fp4_gemm(d["A"], d["B"], d["a_scale"], d["b_scale"], p["alpha"], **kw)
-    return fgg.grouped_fp4_gemm(d["A"], d["B"], d["a_scale"], d["b_scale"], d["m_indices"],
-                                p["alpha"], **kw)
 
 
 def ref(p: dict, rows=None, ids=None) -> np.ndarray:
@@ -58,14 +34,6 @@ def ref(p: dict, rows=None, ids=None) -> np.ndarray:
         return oracle.fp4_gemm(p["A"], p["B"], p["a_scale"], p["b_scale"], p["alpha"], rows=rows)
     return oracle.grouped_fp4_gemm(p["A"], p["B"], p["a_scale"], p["b_scale"], m, p["alpha"],
                                    rows=rows)
-
-
-def row_ids(p: dict, rows=None):
-    m = p.get("m_indices")
-    if m is None:
-        return None
-    m = np.where((m >= 0) & (m < p["G"]), m, -1)
-    return m if rows is None else m[rows]
 
 
 def assert_parity(p: dict, C, rows=None, what=""):
