@@ -78,6 +78,11 @@ WORKLOADS = {
     "q_nvfp4_static_c5": dict(kind="quant_nvfp4_static", M=65536, K=8192,
                               desc="BF16 -> NVFP4 activations of c5 with a calibrated global "
                                    "scale (amax of the first 64 rows / 2688), M=65536, K=8192"),
+    # The quantiser fused with the MoE row expansion: c2's A operand built
+    # from 4096 tokens routed top-2 of 8 experts (8192 expanded rows).
+    "q_fp8_expand_c2": dict(kind="quant_fp8_expand", M=8192, K=7168, T=4096, G=8, top_k=2,
+                            desc="token rows -> expert-ordered FP8 1x128 A operand of c2: "
+                                 "4096 BF16 tokens x top-2 of 8 experts (8192 rows), K=7168"),
 }
 QUANT_METRIC = "GB/s (algorithmic bytes / time) and % of HBM peak, activation quantiser"
 
@@ -91,6 +96,7 @@ KERNEL_SOURCES = {
     "quant_fp8": ("quant.hip", "common.h"),
     "quant_nvfp4": ("quant.hip", "common.h"),
     "quant_nvfp4_static": ("quant.hip", "common.h"),
+    "quant_fp8_expand": ("quant.hip", "common.h"),
     "w4a16": ("w4a16.hip", "common.h"),
 }
 
@@ -275,6 +281,8 @@ def quant_bytes(kind: str, M: int, K: int) -> int:
     static one (a given global scale) reads X once and writes no scale."""
     if kind == "quant_fp8":
         return M * K * 2 + M * K + M * (K // 128) * 4
+    if kind == "quant_fp8_expand":  # every expanded row reads its token row
+        return M * K * 2 + M * K + M * (K // 128) * 4 + M * 4
     if kind == "quant_nvfp4_static":
         return M * K * 2 + M * K // 2 + M * (K // 16)
     return M * K * 2 + M * K // 2 + M * (K // 16) + 4
@@ -375,11 +383,23 @@ def bench_quant(args, torch):
     kind, M, K = w["kind"], w["M"], w["K"]
     print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
     rng = np.random.default_rng(0)
-    X = torch.from_numpy(rng.standard_normal((M, K), dtype=np.float32)).to(torch.bfloat16)
+    rows_np = None
+    if kind == "quant_fp8_expand":
+        from workloads import decode_routing, moe_expand
+        T = w["T"]
+        routing = decode_routing(T, w["top_k"], w["G"], rng).reshape(T, w["top_k"])
+        rows_np, _ = moe_expand(routing, w["G"])
+        assert rows_np.size == M
+        X = torch.from_numpy(rng.standard_normal((T, K), dtype=np.float32)).to(torch.bfloat16)
+        rows_d = torch.from_numpy(rows_np).cuda()
+    else:
+        X = torch.from_numpy(rng.standard_normal((M, K), dtype=np.float32)).to(torch.bfloat16)
     Xd = X.cuda()
     g_static = float(X[:64].float().abs().max()) / 2688.0  # a calibration on the first rows
     if kind == "quant_fp8":
         run = lambda: fgg.quantize_fp8_1x128(Xd)
+    elif kind == "quant_fp8_expand":
+        run = lambda: fgg.quantize_fp8_1x128(Xd, rows=rows_d)
     elif kind == "quant_nvfp4_static":
         run = lambda: fgg.quantize_nvfp4(Xd, global_scale=g_static)
     else:
@@ -415,12 +435,14 @@ def bench_quant(args, torch):
         from threadpoolctl import threadpool_info
         print("[bench] cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
         Xf = X.float().numpy()
+        if rows_np is not None:
+            Xf = Xf[rows_np]  # every row maps to a token (no padding rows here)
         Q = [t.cpu().numpy() for t in out]
         done, ok = 0, True
         t0 = time.perf_counter()
         for r0 in range(0, M, 64):
             rows = Xf[r0:r0 + 64]
-            if kind == "quant_fp8":
+            if kind in ("quant_fp8", "quant_fp8_expand"):
                 q, sc = oq.quantize_fp8_1x128(rows)
                 ok &= bool(np.array_equal(q, Q[0][r0:r0 + 64]) and
                            np.array_equal(sc, Q[1][r0:r0 + 64]))

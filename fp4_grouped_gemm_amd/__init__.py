@@ -86,6 +86,8 @@ def load_library():
         ("quantize_fp8_1x128", [P, P, P, I, I, P]),
         ("quantize_nvfp4", [P, P, P, P, I, I, P]),
         ("quantize_nvfp4_static", [P, P, P, F, I, I, P]),
+        ("quantize_fp8_1x128_rows", [P, P, P, P, I, I, I, P]),
+        ("quantize_nvfp4_static_rows", [P, P, P, P, F, I, I, I, P]),
         ("grouped_fp4_gemm_alpha", [P, P, P, P, P, P, P, I, I, I, I, P]),
         ("grouped_fp4_gemm_alpha_ex", [P, P, P, P, P, P, P, I, I, I, I, OPT, P]),
         ("fp4_gemm_problems", [ctypes.POINTER(_Fp4Problem), I, P]),
@@ -444,22 +446,40 @@ def _bf16_matrix(X):
     return _dev(X, "X", X.device)
 
 
-def quantize_fp8_1x128(X, stream=None):
+def _row_map(rows, X):
+    torch = _torch()
+    if rows.dtype != torch.int32 or rows.dim() != 1:
+        raise ValueError("rows must be a 1-D int32 tensor")
+    return _dev(rows, "rows", X.device)
+
+
+def quantize_fp8_1x128(X, stream=None, rows=None):
     """BF16 activations [M, K] -> (E4M3FN codes uint8 [M, K], FP32 scales
-    [M, K/128]): the A operand of grouped_fp8_gemm (C ABI quantize_fp8_1x128)."""
+    [M, K/128]): the A operand of grouped_fp8_gemm (C ABI quantize_fp8_1x128).
+
+    rows (int32 [R], optional): the MoE row expansion fused in -- output row
+    r quantises X[rows[r]], a padding row (zeros) where rows[r] is outside
+    [0, M); the result has R rows (C ABI quantize_fp8_1x128_rows)."""
     torch = _torch()
     lib = load_library()
     X = _bf16_matrix(X)
     M, K = X.shape
-    Q = torch.empty((M, K), dtype=torch.uint8, device=X.device)
-    S = torch.empty((M, max(K // 128, 1)), dtype=torch.float32, device=X.device)
+    R = M if rows is None else rows.shape[0]
+    Q = torch.empty((R, K), dtype=torch.uint8, device=X.device)
+    S = torch.empty((R, max(K // 128, 1)), dtype=torch.float32, device=X.device)
     with torch.cuda.device(X.device):
-        _check(lib.quantize_fp8_1x128(X.data_ptr(), Q.data_ptr(), S.data_ptr(), M, K,
-                                      _stream_ptr(stream, X.device)))
+        if rows is None:
+            _check(lib.quantize_fp8_1x128(X.data_ptr(), Q.data_ptr(), S.data_ptr(), M, K,
+                                          _stream_ptr(stream, X.device)))
+        else:
+            rows = _row_map(rows, X)
+            _check(lib.quantize_fp8_1x128_rows(X.data_ptr(), rows.data_ptr(), Q.data_ptr(),
+                                               S.data_ptr(), R, M, K,
+                                               _stream_ptr(stream, X.device)))
     return Q, S
 
 
-def quantize_nvfp4(X, stream=None, global_scale=None):
+def quantize_nvfp4(X, stream=None, global_scale=None, rows=None):
     """BF16 activations [M, K] -> (packed E2M1 uint8 [M, K/2], E4M3FN scale
     codes uint8 [M, K/16], FP32 global scale as a 1-element device tensor):
     the A operand of fp4_gemm / grouped_fp4_gemm, whose alpha is this global
@@ -467,15 +487,29 @@ def quantize_nvfp4(X, stream=None, global_scale=None):
 
     global_scale: None computes g = amax(X) / 2688 on the device; a Python
     float is a calibrated, static g (C ABI quantize_nvfp4_static: one pass
-    over X, block amaxes above 448 * 6 * g saturate)."""
+    over X, block amaxes above 448 * 6 * g saturate).
+
+    rows (int32 [R], optional; needs a static global_scale): the MoE row
+    expansion fused in, as for quantize_fp8_1x128 (C ABI
+    quantize_nvfp4_static_rows)."""
     torch = _torch()
     lib = load_library()
     X = _bf16_matrix(X)
     M, K = X.shape
-    Q = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
-    S = torch.empty((M, max(K // 16, 1)), dtype=torch.uint8, device=X.device)
+    R = M if rows is None else rows.shape[0]
+    Q = torch.empty((R, K // 2), dtype=torch.uint8, device=X.device)
+    S = torch.empty((R, max(K // 16, 1)), dtype=torch.uint8, device=X.device)
     with torch.cuda.device(X.device):
-        if global_scale is None:
+        if rows is not None:
+            if global_scale is None:
+                raise ValueError("the row-expansion variant needs a static global_scale")
+            gs = float(global_scale)
+            rows = _row_map(rows, X)
+            _check(lib.quantize_nvfp4_static_rows(X.data_ptr(), rows.data_ptr(), Q.data_ptr(),
+                                                  S.data_ptr(), gs, R, M, K,
+                                                  _stream_ptr(stream, X.device)))
+            g = torch.full((1,), gs, dtype=torch.float32, device=X.device)
+        elif global_scale is None:
             g = torch.empty((1,), dtype=torch.float32, device=X.device)
             _check(lib.quantize_nvfp4(X.data_ptr(), Q.data_ptr(), S.data_ptr(), g.data_ptr(),
                                       M, K, _stream_ptr(stream, X.device)))

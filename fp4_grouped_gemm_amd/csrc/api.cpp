@@ -635,4 +635,45 @@ fgg_status quantize_nvfp4_static(const void* X, void* Q, void* scale, float glob
                                                      static_cast<hipStream_t>(stream)));
 }
 
+// Row-expansion variants: output row r from token row rows[r].
+static fgg_status check_rows(const char* fn, const int32_t* rows, int R, int T, int K) {
+  if (!rows) return fail(FGG_EINVAL, fn, "rows is null");
+  if (!aligned(rows, 4)) return fail(FGG_EALIGN, fn, "rows must be 4-byte aligned");
+  if (T < 1 || T > (1 << 24)) return fail(FGG_EINVAL, fn, "requires 1 <= T <= 2^24, got T=%d", T);
+  if ((long long)R * (K / 32) > 0x7FFFFFFFLL)
+    return fail(FGG_EUNSUPPORTED, fn, "requires R * K / 32 < 2^31, got R=%d K=%d", R, K);
+  return FGG_OK;
+}
+
+fgg_status quantize_fp8_1x128_rows(const void* X, const int32_t* rows, void* Q, float* scale,
+                                   int R, int T, int K, void* stream) {
+  const char* fn = "quantize_fp8_1x128_rows";
+  fgg_status st = check_quant(fn, X, Q, scale, R, K, 4, 128);
+  if (st != FGG_OK) return st;
+  if ((st = check_rows(fn, rows, R, T, K)) != FGG_OK) return st;
+  const DeviceFacts* d = current_device(fn, &st);
+  if (!d) return st;
+  return launched(fn, fgg::launch_quant_fp8(static_cast<const uint16_t*>(X), static_cast<uint8_t*>(Q),
+                                            scale, R, K, d->num_cus,
+                                            static_cast<hipStream_t>(stream), rows, T));
+}
+
+fgg_status quantize_nvfp4_static_rows(const void* X, const int32_t* rows, void* Q, void* scale,
+                                      float global_scale, int R, int T, int K, void* stream) {
+  const char* fn = "quantize_nvfp4_static_rows";
+  fgg_status st = check_quant(fn, X, Q, scale, R, K, 1, 16);
+  if (st != FGG_OK) return st;
+  if ((st = check_rows(fn, rows, R, T, K)) != FGG_OK) return st;
+  if (!std::isfinite(global_scale) || !(global_scale >= std::numeric_limits<float>::min()))
+    return fail(FGG_EINVAL, fn, "global_scale must be a finite normal positive float, got %g",
+                (double)global_scale);
+  const DeviceFacts* d = current_device(fn, &st);
+  if (!d) return st;
+  return launched(fn, fgg::launch_quant_nvfp4_static(static_cast<const uint16_t*>(X),
+                                                     static_cast<uint8_t*>(Q),
+                                                     static_cast<uint8_t*>(scale), global_scale, R,
+                                                     K, d->num_cus,
+                                                     static_cast<hipStream_t>(stream), rows, T));
+}
+
 }  // extern "C"

@@ -103,12 +103,15 @@ hipError_t launch_fp4(const Fp4Args& a, int tile_id, const LaunchOpts& o, hipStr
 hipError_t launch_fp4_problems(const Fp4ProblemSet& set, int tile_id, const LaunchOpts& o,
                                hipStream_t s);
 hipError_t launch_w4a16(const W4A16Args& a, hipStream_t s);
+// rows (may be null): output row r quantises input row rows[r] of X's T
+// rows, zeros when rows[r] is outside [0, T) (the MoE row expansion).
 hipError_t launch_quant_fp8(const uint16_t* X, uint8_t* Q, float* scale, int M, int K,
-                            int num_cus, hipStream_t s);
+                            int num_cus, hipStream_t s, const int32_t* rows = nullptr, int T = 0);
 hipError_t launch_quant_nvfp4(const uint16_t* X, uint8_t* Q, uint8_t* S, float* g, int M, int K,
                               int num_cus, hipStream_t s);
 hipError_t launch_quant_nvfp4_static(const uint16_t* X, uint8_t* Q, uint8_t* S, float g, int M,
-                                     int K, int num_cus, hipStream_t s);
+                                     int K, int num_cus, hipStream_t s,
+                                     const int32_t* rows = nullptr, int T = 0);
 
 // --------------------------------------------------------- device helpers
 #ifdef __HIPCC__

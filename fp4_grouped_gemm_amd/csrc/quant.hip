@@ -87,12 +87,46 @@ __device__ __forceinline__ bool div_rn_ok(float d, float a) {
 // valid or not as a whole, so their values reach no valid block.
 constexpr int kQThreads = 256;
 
+// Where the values of an output row come from.  rows == nullptr: output row
+// r is input row r (X read as a flat array).  Otherwise output row r is
+// input row rows[r] of the T rows of X, and an entry outside [0, T) gives a
+// row of zeros: the row expansion of an MoE layer, which copies each
+// token's activations to the rows of the experts it is routed to (in expert
+// order, with padding rows), fused with the quantisation of those rows
+// (the onnxruntime#29824 page, "Code analysis 1": expandInputRowsKernel
+// quantises while it expands).  Pieces are indexed in 32 bits (the host
+// checks R * K / 32 < 2^31).
+struct RowMap {
+  const int32_t* rows;
+  uint32_t ppr;  // 32-value pieces per row, K / 32
+  int T;
+};
+
+__device__ __forceinline__ void load_piece(const uint16_t* X, long long q, const RowMap& m,
+                                           float v[4][8]) {
+  if (m.rows == nullptr) {
+    load32(X + q * 32, v);
+    return;
+  }
+  const uint32_t qq = (uint32_t)q;
+  const uint32_t r = qq / m.ppr, c = qq - r * m.ppr;
+  const int src = m.rows[r];
+  if (src >= 0 && src < m.T) {
+    load32(X + ((long long)src * m.ppr + c) * 32, v);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
+  }
+}
+
 // ------------------------------------------------------------- FP8 1x128
 // A 128-value block is 4 lanes.
 __global__ __launch_bounds__(kQThreads) void quant_fp8_kernel(const uint16_t* __restrict__ X,
                                                               uint8_t* __restrict__ Q,
                                                               float* __restrict__ scale,
-                                                              long long nblocks) {
+                                                              long long nblocks, RowMap map) {
   const int lane = threadIdx.x & 63;
   const long long waves = (long long)gridDim.x * (kQThreads / 64);
   const long long pieces = nblocks * 4;
@@ -100,7 +134,7 @@ __global__ __launch_bounds__(kQThreads) void quant_fp8_kernel(const uint16_t* __
        w * 64 < pieces; w += waves) {
     const long long q = min(w * 64 + lane, pieces - 1);
     float v[4][8];
-    load32(X + q * 32, v);
+    load_piece(X, q, map, v);
     float a = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -233,7 +267,8 @@ __global__ __launch_bounds__(kQThreads) void quant_nvfp4_kernel(const uint16_t* 
                                                                 uint8_t* __restrict__ Q,
                                                                 uint8_t* __restrict__ S,
                                                                 const uint32_t* amax_bits,
-                                                                float g_given, long long nblocks) {
+                                                                float g_given, long long nblocks,
+                                                                RowMap map) {
   const int lane = threadIdx.x & 63;
   // the global scale: from the amax pass, or given by the caller (static)
   const float g = amax_bits ? global_scale(amax_bits[0]) : g_given;
@@ -244,7 +279,7 @@ __global__ __launch_bounds__(kQThreads) void quant_nvfp4_kernel(const uint16_t* 
        w * 64 < pieces; w += waves) {
     const long long q = min(w * 64 + lane, pieces - 1);
     float v[4][8];
-    load32(X + q * 32, v);
+    load_piece(X, q, map, v);
     u32x4 codes;
     uint32_t sc = 0;
 #pragma unroll
@@ -289,11 +324,13 @@ int grid_for(long long waves, int num_cus, int per_cu) {
 using namespace quant_detail;
 
 hipError_t launch_quant_fp8(const uint16_t* X, uint8_t* Q, float* scale, int M, int K,
-                            int num_cus, hipStream_t s) {
+                            int num_cus, hipStream_t s, const int32_t* rows, int T) {
   const long long nblocks = (long long)M * (K / 128);
   if (nblocks <= 0) return hipSuccess;
+  if (rows && nblocks * 4 > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  const RowMap map{rows, (uint32_t)(K / 32), T};
   hipLaunchKernelGGL(quant_fp8_kernel, dim3(grid_for((nblocks * 4 + 63) / 64, num_cus, 8)),
-                     dim3(kQThreads), 0, s, X, Q, scale, nblocks);
+                     dim3(kQThreads), 0, s, X, Q, scale, nblocks, map);
   return hipGetLastError();
 }
 
@@ -308,19 +345,23 @@ hipError_t launch_quant_nvfp4(const uint16_t* X, uint8_t* Q, uint8_t* S, float* 
                      s, X, n8, gb);
   const long long nblocks = n / 16;
   hipLaunchKernelGGL(quant_nvfp4_kernel, dim3(grid_for((nblocks / 2 + 63) / 64, num_cus, 16)),
-                     dim3(kQThreads), 0, s, X, Q, S, (const uint32_t*)gb, 0.0f, nblocks);
+                     dim3(kQThreads), 0, s, X, Q, S, (const uint32_t*)gb, 0.0f, nblocks,
+                     RowMap{nullptr, (uint32_t)(K / 32), 0});
   hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1), 0, s, gb);
   return hipGetLastError();
 }
 
 // With a global scale given by the caller: the encode pass only (one read of X).
 hipError_t launch_quant_nvfp4_static(const uint16_t* X, uint8_t* Q, uint8_t* S, float g, int M,
-                                     int K, int num_cus, hipStream_t s) {
+                                     int K, int num_cus, hipStream_t s, const int32_t* rows,
+                                     int T) {
   const long long n = (long long)M * K;
   if (n <= 0) return hipSuccess;
   const long long nblocks = n / 16;
+  if (rows && nblocks / 2 > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  const RowMap map{rows, (uint32_t)(K / 32), T};
   hipLaunchKernelGGL(quant_nvfp4_kernel, dim3(grid_for((nblocks / 2 + 63) / 64, num_cus, 16)),
-                     dim3(kQThreads), 0, s, X, Q, S, (const uint32_t*)nullptr, g, nblocks);
+                     dim3(kQThreads), 0, s, X, Q, S, (const uint32_t*)nullptr, g, nblocks, map);
   return hipGetLastError();
 }
 

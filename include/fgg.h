@@ -181,8 +181,13 @@ fgg_status fp4_gemm_problems(const fgg_fp4_problem* problems, int count, void* s
  *
  * Weights are dequantised exactly (E2M1 x E4M3 has at most 6 significant
  * bits) and multiplied with FP32 accumulation.  Built for few rows per expert
- * (decode): each expert's weights are read once per 16 of its rows, and an
- * expert with no rows costs no weight traffic.  Requirements as
+ * (decode): m_indices is scanned 1024 entries at a time, and an expert's
+ * weights are streamed once per 32 of its rows found in a scan (rounded up
+ * per scan).  So for M <= 1024 every expert's weights stream
+ * ceil(rows_e / 32) times, and an expert with no rows costs no weight
+ * traffic; for larger M each further scan that holds rows of an expert
+ * streams its weights again (results are the same at any M; prefill-sized
+ * batches belong on grouped_fp4_gemm after quantize_nvfp4).  Requirements as
  * grouped_fp4_gemm (A 16-byte aligned); b_global finite; M * K * 2 < 2^31,
  * the activations of a decode batch (else FGG_EUNSUPPORTED).  Rows routed
  * to an expert must be finite; rows marked -1 (or out of range) may hold
@@ -230,6 +235,32 @@ fgg_status quantize_nvfp4(const void* X, void* Q, void* scale, float* global_sca
                           void* stream);
 fgg_status quantize_nvfp4_static(const void* X, void* Q, void* scale, float global_scale, int M,
                                  int K, void* stream);
+
+/*
+ * quantize_fp8_1x128_rows, quantize_nvfp4_static_rows -- the same encodings,
+ * fused with the row expansion of an MoE layer (the onnxruntime#29824 page,
+ * "Code analysis 1": expandInputRowsKernel quantises while it copies each
+ * token's activations to the rows of the experts it is routed to).
+ *
+ *   X     [T, K]   BF16 token activations
+ *   rows  [R]      int32, device: output row r holds token rows[r]; a value
+ *                  outside [0, T) makes row r a padding row, encoded as
+ *                  zeros (FP8: codes 0, scale 1.0; NVFP4: codes 0, scale
+ *                  code 0).  Read on the device at every launch.
+ *   Q, scale       as quantize_fp8_1x128 / quantize_nvfp4_static with R rows
+ *
+ * Row r of the output equals the row-wise quantisation of X[rows[r]] (the
+ * encodings are per row), so with rows sorted by expert the result is the
+ * A operand of grouped_fp8_gemm / grouped_fp4_gemm directly.  One kernel
+ * launch reading each routed token row once per expert it goes to.
+ * Requirements as the row-wise quantisers with M = R, plus 1 <= T <= 2^24,
+ * rows non-null and 4-byte aligned, and R * K / 32 < 2^31
+ * (FGG_EUNSUPPORTED).
+ */
+fgg_status quantize_fp8_1x128_rows(const void* X, const int32_t* rows, void* Q, float* scale,
+                                   int R, int T, int K, void* stream);
+fgg_status quantize_nvfp4_static_rows(const void* X, const int32_t* rows, void* Q, void* scale,
+                                      float global_scale, int R, int T, int K, void* stream);
 
 /* ------------------------------------------------------------------------
  * Tile configurations and the ranker.

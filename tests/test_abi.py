@@ -240,3 +240,19 @@ def test_device_info_without_gpu():
         pytest.skip("a GPU is present")
     with pytest.raises(ValueError):
         fgg.device_info()
+
+
+def test_expand_quantizer_validation():
+    lib = fgg.load_library()
+    st = lib.quantize_fp8_1x128_rows(P, 0, P, P, 8, 4, 256, None)
+    assert st == 1 and "rows" in lib.fgg_last_error().decode()
+    assert lib.quantize_fp8_1x128_rows(P, P + 2, P, P, 8, 4, 256, None) == 3
+    st = lib.quantize_fp8_1x128_rows(P, P, P, P, 8, 0, 256, None)
+    assert st == 1 and "T" in lib.fgg_last_error().decode()
+    assert lib.quantize_fp8_1x128_rows(P, P, P, P, 8, 4, 200, None) == 1
+    st = lib.quantize_fp8_1x128_rows(P, P, P, P, 1 << 24, 4, 1 << 20, None)
+    assert st == 2 and "2^31" in lib.fgg_last_error().decode()
+    st = lib.quantize_nvfp4_static_rows(P, P, P, P, 0.0, 8, 4, 256, None)
+    assert st == 1 and "global_scale" in lib.fgg_last_error().decode()
+    assert lib.quantize_nvfp4_static_rows(P, P, P, P, 1.0, 8, 4, 144, None) == 2
+    assert lib.quantize_nvfp4_static_rows(P + 8, P, P, P, 1.0, 8, 4, 256, None) == 3

@@ -52,6 +52,12 @@ CASES = {
     "rows_past_one_scan": lambda: _prob(np.random.default_rng(7).integers(-1, 2, 2500), N=128,
                                         K=256, G=2, seed=7),
     "single_expert": lambda: _prob([0] * 20, N=192 * 2, K=256, G=1, seed=8),
+    # the scan bound: 1024 rows are one scan of m_indices, 1025 two (the
+    # last row alone in the second), each with rows of every expert
+    "scan_bound_1024": lambda: _prob(np.random.default_rng(9).integers(-1, 3, 1024), N=128,
+                                     K=256, G=3, seed=9),
+    "scan_bound_1025": lambda: _prob(np.random.default_rng(10).integers(-1, 3, 1025), N=128,
+                                     K=256, G=3, seed=10),
 }
 
 

@@ -23,4 +23,6 @@ from .gen import (  # noqa: F401
     w4a16_problem,
     decode_routing,
     runs_to_indices,
+    moe_expand,
+    bf16_activations,
 )

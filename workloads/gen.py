@@ -135,6 +135,34 @@ def decode_routing(tokens: int, top_k: int, G: int, rng) -> np.ndarray:
         .astype(np.int32)
 
 
+def moe_expand(routing, G: int, pad_to: int = 1):
+    """The row expansion of an MoE layer: routing [T, top_k] holds each
+    token's experts; the expanded batch lists, expert by expert (tokens in
+    order within an expert), one row per (token, expert) pair, each expert's
+    run padded with padding rows to a multiple of pad_to.  Returns (rows,
+    m_indices): rows[r] is the token of expanded row r (-1 for padding) and
+    m_indices[r] its expert (-1 for padding)."""
+    routing = np.asarray(routing)
+    T = routing.shape[0]
+    rows, ids = [], []
+    for g in range(G):
+        tok = np.nonzero((routing == g).any(axis=1))[0].astype(np.int32)
+        pad = (-tok.size) % pad_to
+        rows += [tok, np.full(pad, -1, np.int32)]
+        ids += [np.full(tok.size, g, np.int32), np.full(pad, -1, np.int32)]
+    assert T >= 1
+    return np.concatenate(rows).astype(np.int32), np.concatenate(ids).astype(np.int32)
+
+
+def bf16_activations(T: int, K: int, rng) -> tuple:
+    """N(0,1) activations rounded to BF16 (nearest even): (float32 values,
+    uint16 bit patterns)."""
+    X = _draw(rng, "normal", (T, K))
+    u = X.view(np.uint32)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32), bits
+
+
 def _zipf_counts(rng, G=32, total_rows=16384, start_T=14336, s=1.2, pad_to=128):
     p = (np.arange(1, G + 1, dtype=np.float64)) ** (-s)
     p /= p.sum()
