@@ -621,7 +621,7 @@ def tune_report(args, torch):
     if not os.path.exists(fgg.library_path()):
         from fp4_grouped_gemm_amd.build import build
         build()
-    rows, ratios = [], []
+    rows, ratios, lit_ratios = [], [], []
     for name, w in WORKLOADS.items():
         if w["kind"] not in ("fp8", "fp4"):
             continue  # the quantisers, W4A16 and the problem batch have no tile choice to tune
@@ -646,6 +646,15 @@ def tune_report(args, torch):
         rows.append(dict(workload=name, candidates=rep["tile_id"],
                          us=[round(1e3 * t, 2) for t in rep["ms"]], heuristic=rep["tile_id"][0],
                          best=rep["chosen"], heuristic_loss=round(heur / best - 1.0, 4)))
+        # the page's literal score form, ranked on the same shape: its top-1's
+        # time among the timed candidates (all configs when top_k covers them)
+        lit = fgg.rank_tiles(fgg.FP8 if p["kind"] == "fp8" else fgg.FP4, p["M"], p["N"], p["K"],
+                             p["G"], num_cus=fgg.device_info()["num_cus"],
+                             run_align=w.get("run_align", 0), variant=fgg.SCORE_LITERAL)[0]["id"]
+        if lit in rep["tile_id"]:
+            t_lit = rep["ms"][rep["tile_id"].index(lit)]
+            lit_ratios.append(t_lit / best)
+            rows[-1].update(literal=lit, literal_loss=round(t_lit / best - 1.0, 4))
         align = w.get("run_align", 0)
         if align:
             # the ranker's pick under the workload's run-alignment promise
@@ -660,10 +669,15 @@ def tune_report(args, torch):
         del d, p
         torch.cuda.empty_cache()
     geo = float(np.exp(np.mean(np.log(ratios))))
-    print(json.dumps({"metric": "bounded autotune: heuristic top-1 time / best-of-top-k time",
-                      "top_k": args.top_k, "workloads": rows,
-                      "geomean_heuristic_over_best": round(geo, 4),
-                      "geomean_loss": round(geo - 1.0, 4)}), flush=True)
+    res = {"metric": "bounded autotune: heuristic top-1 time / best-of-top-k time",
+           "top_k": args.top_k, "workloads": rows,
+           "geomean_heuristic_over_best": round(geo, 4),
+           "geomean_loss": round(geo - 1.0, 4)}
+    if len(lit_ratios) == len(ratios):
+        geo_l = float(np.exp(np.mean(np.log(lit_ratios))))
+        res.update(geomean_literal_over_best=round(geo_l, 4),
+                   geomean_literal_loss=round(geo_l - 1.0, 4))
+    print(json.dumps(res), flush=True)
 
 
 def bench_gemm(args, torch, workload: str, cold_launches: int, cpu_seconds: float,
@@ -776,6 +790,47 @@ def bench_gemm(args, torch, workload: str, cold_launches: int, cpu_seconds: floa
     return out
 
 
+def tput_sweep(args, torch):
+    """Per-CU throughput of every tile config on problems that every config
+    tiles into whole waves of the device (so the ranker's other terms are
+    1), relative to the best config: the measurement behind the ranker's
+    `throughput` constants."""
+    import fp4_grouped_gemm_amd as fgg
+    from fp4_grouped_gemm_amd.util import run, to_device as to_dev
+    from workloads import fp8_problem, nvfp4_problem
+    rng = np.random.default_rng(0)
+    out = {"metric": "tile config throughput, relative to the best config", "kinds": {}}
+    for kind, name in ((fgg.FP8, "fp8"), (fgg.FP4, "fp4")):
+        print(f"[bench] tput sweep {name}", file=sys.stderr, flush=True)
+        if kind == fgg.FP8:
+            # 8192 x 8192 x 7168, one expert: 1024 / 2048 / 2048 / 4096 tiles
+            p = fp8_problem(np.zeros(8192, np.int32), 8192, 7168, 1, rng)
+        else:
+            p = nvfp4_problem(None, 8192, 8192, 4096, 1, rng)
+        d = to_dev(p)
+        C = torch.empty((p["M"], p["N"]), dtype=torch.bfloat16, device="cuda")
+        flops = 2.0 * p["M"] * p["N"] * p["K"]
+        tiles = fgg.rank_tiles(kind, p["M"], p["N"], p["K"], p["G"],
+                               num_cus=fgg.device_info()["num_cus"])
+        res = {}
+        for t in sorted(tiles, key=lambda t: t["id"]):
+            call = lambda: run(p, d, out=C, tile_id=t["id"])  # noqa: E731
+            for _ in range(3):
+                call()
+            ms = min(time_launches(torch, call, 10, True)[0] for _ in range(3))
+            res[t["id"]] = dict(block_m=t["block_m"], block_n=t["block_n"], waves=t["waves"],
+                                wg_per_cu=t["wg_per_cu"], us=round(ms * 1e3, 1),
+                                tflops=round(flops / (ms * 1e-3) / 1e12, 1),
+                                tput_constant=round(t["tput"], 3))
+        best = max(r["tflops"] for r in res.values())
+        for r in res.values():
+            r["tput_measured"] = round(r["tflops"] / best, 3)
+        out["kinds"][name] = dict(M=p["M"], N=p["N"], K=p["K"], tiles=res)
+        del d, C, p
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -806,6 +861,10 @@ def main():
                          "configs (the library's *_tune calls), report heuristic top-1 against "
                          "the best of the k, and the geomean loss; one JSON line")
     ap.add_argument("--top-k", type=int, default=4)
+    ap.add_argument("--tput-sweep", action="store_true",
+                    help="time every tile config on problems that fill whole waves for all of "
+                         "them and print each config's throughput relative to the best (the "
+                         "ranker's throughput constants); one JSON line")
     ap.add_argument("--autotune", action="store_true",
                     help="GEMM workloads: run the library's bounded autotune of the ranker's "
                          "top-k configs once (untimed) and time the config it records")
@@ -857,6 +916,10 @@ def main():
 
     if args.tune_report:
         tune_report(args, torch)
+        return
+
+    if args.tput_sweep:
+        tput_sweep(args, torch)
         return
 
     if WORKLOADS[args.workload]["kind"] == "w4a16":

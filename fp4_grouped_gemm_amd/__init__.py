@@ -37,7 +37,11 @@ def library_path() -> str:
 
 class _Tile(ctypes.Structure):
     _fields_ = [("id", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
-                ("waves", ctypes.c_int), ("wg_per_cu", ctypes.c_int), ("score", ctypes.c_float)]
+                ("waves", ctypes.c_int), ("wg_per_cu", ctypes.c_int), ("score", ctypes.c_float),
+                ("tput", ctypes.c_float)]
+
+
+SCORE_KEPT, SCORE_LITERAL = 0, 1  # FGG_SCORE_* (score forms of the ranker)
 
 
 TUNE_MAX = 8  # FGG_TUNE_MAX
@@ -109,6 +113,8 @@ def load_library():
     lib.fgg_rank_tiles.argtypes = [I, I, I, I, I, I, ctypes.POINTER(_Tile), I]
     lib.fgg_rank_tiles_aligned.restype = I
     lib.fgg_rank_tiles_aligned.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(_Tile), I]
+    lib.fgg_rank_tiles_variant.restype = I
+    lib.fgg_rank_tiles_variant.argtypes = [I, I, I, I, I, I, I, I, ctypes.POINTER(_Tile), I]
     lib.fgg_device_info.restype = I
     lib.fgg_device_info.argtypes = [ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I),
                                     ctypes.c_char_p, I]
@@ -417,17 +423,18 @@ def num_tiles(kind: int) -> int:
 
 
 def rank_tiles(kind: int, M: int, N: int, K: int, G: int = 1, num_cus: int = 256,
-               run_align: int = 0):
+               run_align: int = 0, variant: int = SCORE_KEPT):
     """The ranker's ordered tile configs for a problem (host logic only);
-    run_align as in fgg_options."""
+    run_align as in fgg_options; variant selects the score form
+    (SCORE_KEPT, the one the entry points use, or SCORE_LITERAL)."""
     lib = load_library()
     n = max(1, lib.fgg_num_tiles(kind))
     arr = (_Tile * n)()
-    k = lib.fgg_rank_tiles_aligned(kind, M, N, K, G, run_align, num_cus, arr, n)
+    k = lib.fgg_rank_tiles_variant(kind, M, N, K, G, run_align, variant, num_cus, arr, n)
     if k < 0:
         _check(1)
     return [dict(id=t.id, block_m=t.block_m, block_n=t.block_n, waves=t.waves,
-                 wg_per_cu=t.wg_per_cu, score=t.score) for t in arr[:k]]
+                 wg_per_cu=t.wg_per_cu, score=t.score, tput=t.tput) for t in arr[:k]]
 
 
 def device_info():

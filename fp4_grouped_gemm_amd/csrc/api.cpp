@@ -132,7 +132,8 @@ fgg_status check_common(const char* fn, const void* A, const void* B, const void
 //               busy, tiles / (num_waves * CUs * wg_per_cu);
 //   throughput= per-CU efficiency of the tile shape.
 // The page's 2-CTA and cluster-multicast factors have no gfx950 counterpart.
-float score_tile(const fgg::TileCfg& t, int M, int N, int G, int num_cus, int run_align) {
+float score_tile(const fgg::TileCfg& t, int M, int N, int G, int num_cus, int run_align,
+                 int variant = FGG_SCORE_KEPT) {
   const long long windows = (M + t.block_m - 1) / t.block_m;
   // every expert boundary in its own window, unless the runs start on
   // multiples of the tile height
@@ -145,15 +146,19 @@ float score_tile(const fgg::TileCfg& t, int M, int N, int G, int num_cus, int ru
   const long long slots = (long long)std::max(1, num_cus) * t.wg_per_cu;
   const long long num_waves = (tiles + slots - 1) / slots;
   const double busy = (double)tiles / (double)(num_waves * slots);
+  if (variant == FGG_SCORE_LITERAL)  // the page's printed form, for comparison
+    return (float)(std::min(1.0, m_eff) * n_eff * t.tput / ((double)num_waves * t.block_n));
   return (float)(std::min(1.0, m_eff) * n_eff * busy * t.tput);
 }
 
-int rank(int kind, int M, int N, int G, int num_cus, int run_align, fgg_tile* out, int max_out) {
+int rank(int kind, int M, int N, int G, int num_cus, int run_align, fgg_tile* out, int max_out,
+         int variant = FGG_SCORE_KEPT) {
   const int n = kind == FGG_KIND_FP8 ? fgg::fp8_num_tiles() : fgg::fp4_num_tiles();
   std::vector<fgg_tile> v;
   for (int i = 0; i < n; ++i) {
     const fgg::TileCfg& t = kind == FGG_KIND_FP8 ? fgg::fp8_tile(i) : fgg::fp4_tile(i);
-    fgg_tile r{t.id, t.block_m, t.block_n, t.waves, t.wg_per_cu, score_tile(t, M, N, G, num_cus, run_align)};
+    fgg_tile r{t.id, t.block_m, t.block_n, t.waves, t.wg_per_cu,
+               score_tile(t, M, N, G, num_cus, run_align, variant), t.tput};
     v.push_back(r);
   }
   std::stable_sort(v.begin(), v.end(), [](const fgg_tile& a, const fgg_tile& b) { return a.score > b.score; });
@@ -317,9 +322,11 @@ int fgg_num_tiles(int kind) {
   return -1;
 }
 
-int fgg_rank_tiles_aligned(int kind, int M, int N, int K, int G, int run_align, int num_cus,
-                           fgg_tile* out, int max_out) {
+int fgg_rank_tiles_variant(int kind, int M, int N, int K, int G, int run_align, int variant,
+                           int num_cus, fgg_tile* out, int max_out) {
   const char* fn = "fgg_rank_tiles";
+  if (variant != FGG_SCORE_KEPT && variant != FGG_SCORE_LITERAL)
+    return (fail(FGG_EINVAL, fn, "bad score variant %d", variant), -1);
   (void)K;
   if (kind != FGG_KIND_FP8 && kind != FGG_KIND_FP4) return (fail(FGG_EINVAL, fn, "bad kind %d", kind), -1);
   if (!out || max_out < 1) return (fail(FGG_EINVAL, fn, "need an output array"), -1);
@@ -331,7 +338,13 @@ int fgg_rank_tiles_aligned(int kind, int M, int N, int K, int G, int run_align, 
     if (!d) return -1;
     num_cus = d->num_cus;
   }
-  return rank(kind, M, N, G, num_cus, run_align, out, max_out);
+  return rank(kind, M, N, G, num_cus, run_align, out, max_out, variant);
+}
+
+int fgg_rank_tiles_aligned(int kind, int M, int N, int K, int G, int run_align, int num_cus,
+                           fgg_tile* out, int max_out) {
+  return fgg_rank_tiles_variant(kind, M, N, K, G, run_align, FGG_SCORE_KEPT, num_cus, out,
+                                max_out);
 }
 
 int fgg_rank_tiles(int kind, int M, int N, int K, int G, int num_cus, fgg_tile* out, int max_out) {

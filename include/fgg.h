@@ -282,6 +282,8 @@ typedef struct {
   int waves;       /* 64-lane wavefronts per workgroup                      */
   int wg_per_cu;   /* workgroups resident per compute unit                  */
   float score;     /* ranker score (higher is better); 0 = not applicable   */
+  float tput;      /* the shape's relative per-CU throughput (1.0 = best),
+                    * the ranker's throughput term                         */
 } fgg_tile;
 
 /* Number of compiled tile configs for `kind`, or -1 for a bad kind. */
@@ -298,6 +300,23 @@ int fgg_rank_tiles(int kind, int M, int N, int K, int G, int num_cus, fgg_tile* 
 /* The same with the run_align promise of fgg_options (0 = none). */
 int fgg_rank_tiles_aligned(int kind, int M, int N, int K, int G, int run_align, int num_cus,
                            fgg_tile* out, int max_out);
+
+/* The ranking under a chosen form of the score (for comparing them; the
+ * entry points always use FGG_SCORE_KEPT):
+ *   FGG_SCORE_KEPT     m_eff * n_eff * busy * throughput, busy = tiles /
+ *                      (num_waves * CUs * wg_per_cu): the page's structure
+ *                      with the division by num_waves read as the busy
+ *                      fraction of the last wave.  It equals throughput /
+ *                      (num_waves * CUs * wg_per_cu * BM * BN) up to the
+ *                      constant M * N, i.e. the inverse of a predicted
+ *                      time (rounds of tiles times the per-tile time).
+ *   FGG_SCORE_LITERAL  m_eff * n_eff * throughput / (num_waves * tile_n),
+ *                      the page's printed form ("Code analysis 2") with
+ *                      the terms defined as above. */
+#define FGG_SCORE_KEPT 0
+#define FGG_SCORE_LITERAL 1
+int fgg_rank_tiles_variant(int kind, int M, int N, int K, int G, int run_align, int variant,
+                           int num_cus, fgg_tile* out, int max_out);
 
 /* Optional overrides for the *_ex entry points (NULL = defaults).  Initialise
  * the whole struct (e.g. `fgg_options o = {-1};` then set fields): a field

@@ -256,3 +256,29 @@ def test_expand_quantizer_validation():
     assert st == 1 and "global_scale" in lib.fgg_last_error().decode()
     assert lib.quantize_nvfp4_static_rows(P, P, P, P, 1.0, 8, 4, 144, None) == 2
     assert lib.quantize_nvfp4_static_rows(P + 8, P, P, P, 1.0, 8, 4, 256, None) == 3
+
+
+def test_ranker_score_forms():
+    """The kept score equals throughput / (num_waves * slots * BM * BN) up to
+    the constant M * N (a predicted-time form); the literal page form also
+    divides by tile_n and keeps num_waves whole.  Both rank every config;
+    on a problem where every shape fills whole waves they can disagree only
+    through tile_n."""
+    for kind in (fgg.FP8, fgg.FP4):
+        for (M, N, G) in ((8192, 4096, 8), (16384, 2048, 32), (2048, 36864, 1), (777, 256, 8)):
+            kept = fgg.rank_tiles(kind, M, N, 7168, G, num_cus=256)
+            for t in kept:
+                bm, bn = t["block_m"], t["block_n"]
+                windows = -(-M // bm)
+                row_tiles = windows + min(G - 1, windows * 4)
+                tiles = row_tiles * -(-N // bn)
+                slots = 256 * t["wg_per_cu"]
+                waves = -(-tiles // slots)
+                assert M <= row_tiles * bm  # m_eff <= 1: the identity below holds
+                pred = M * N * t["tput"] / (bm * bn * waves * slots)
+                assert abs(t["score"] - pred) <= 1e-5 * max(1.0, pred)
+            lit = fgg.rank_tiles(kind, M, N, 7168, G, num_cus=256, variant=fgg.SCORE_LITERAL)
+            assert sorted(t["id"] for t in lit) == sorted(t["id"] for t in kept)
+    lib = fgg.load_library()
+    arr = (fgg._Tile * 4)()
+    assert lib.fgg_rank_tiles_variant(fgg.FP8, 64, 128, 128, 2, 0, 7, 256, arr, 4) == -1
