@@ -23,6 +23,7 @@
 // bytes, 4 scale bytes per row); a tile row of 64 FP16 values is 128 bytes,
 // stored as eight 16-byte chunks XOR-swizzled by row.
 #include "common.h"
+#include "offsets.h"
 
 #include <algorithm>
 #include <climits>
@@ -126,11 +127,11 @@ struct Pass {
 #pragma unroll
     for (int u = 0; u < T::A_UNITS; ++u)
       qa[set][u] = __builtin_bit_cast(
-          i32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, pa_off[u], ks * (T::BK / 2), 0));
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, pa_off[u], off::fp4_code_soff(ks), 0));
 #pragma unroll
     for (int u = 0; u < T::B_UNITS; ++u)
       qb[set][u] = __builtin_bit_cast(
-          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[u], ks * (T::BK / 2), 0));
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[u], off::fp4_code_soff(ks), 0));
   }
 
   // Issue the loads of the scale codes of steps [4c, 4c + 4) into group
@@ -141,15 +142,14 @@ struct Pass {
   // or zeros past the tile's last row, never memory past the buffer.  Codes
   // past the last step are never used.
   __device__ __forceinline__ void load_scales(int grp, int c) {
-    const uint32_t cb = (uint32_t)c * 16u;
 #pragma unroll
     for (int u = 0; u < T::A_UNITS; ++u)
       sa4[grp][u] = __builtin_bit_cast(
-          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rsa, pas_off[u] + cb, 0, 0));
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off::fp4_scale_voff(pas_off[u], c), 0, 0));
 #pragma unroll
     for (int u = 0; u < T::B_UNITS; ++u)
       sb4[grp][u] = __builtin_bit_cast(
-          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, bs_off[u] + cb, 0, 0));
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, off::fp4_scale_voff(bs_off[u], c), 0, 0));
   }
 
   // Chunk c of this thread's staging work for a step whose packed codes are
@@ -258,14 +258,14 @@ __device__ __forceinline__ void init_offsets(Pass<T>& ps, int tid, uint32_t Kp, 
 #pragma unroll
   for (int u = 0; u < T::A_UNITS; ++u) {
     const int g = tid + u * T::THREADS;
-    ps.a_off[u] = (uint32_t)(g >> 1) * Kp + (uint32_t)(g & 1) * 16u;
-    ps.as_off[u] = (uint32_t)(g >> 1) * Ks;
+    ps.a_off[u] = off::fp4_code_voff(g, Kp);
+    ps.as_off[u] = off::fp4_scale_row_off(g, Ks);
   }
 #pragma unroll
   for (int u = 0; u < T::B_UNITS; ++u) {
     const int g = tid + u * T::THREADS;
-    ps.b_off[u] = (uint32_t)(g >> 1) * Kp + (uint32_t)(g & 1) * 16u;
-    ps.bs_off[u] = (uint32_t)(g >> 1) * Ks;
+    ps.b_off[u] = off::fp4_code_voff(g, Kp);
+    ps.bs_off[u] = off::fp4_scale_row_off(g, Ks);
   }
 }
 

@@ -32,6 +32,7 @@
 //    re-initialises all pipeline state (LDS stages, accumulators, expert
 //    cursor) per tile and per pass.
 #include "common.h"
+#include "offsets.h"
 
 #include <climits>
 
@@ -141,12 +142,12 @@ struct Pass {
       const bool need = (a_groups >> (s * T::WAVES + wave)) & 1;
       if (T::STAGES == 2 && !need) continue;
       dma16(ra, lds_addr(st + (s * T::WAVES + wave) * 1024),
-            need ? lane_off + (uint32_t)(s * T::WAVES * 8) * K : kSkip, kb * 128);
+            off::fp8_tile_voff(lane_off, s, T::WAVES, K, need), off::fp8_step_soff(kb));
     }
 #pragma unroll
     for (int s = 0; s < T::B_LOADS; ++s)
       dma16(rb, lds_addr(st + T::A_BYTES + (s * T::WAVES + wave) * 1024),
-            lane_off + (uint32_t)(s * T::WAVES * 8) * K, kb * 128);
+            off::fp8_tile_voff(lane_off, s, T::WAVES, K, true), off::fp8_step_soff(kb));
   }
 
   // a_scale values of K blocks [c SA_BLK, c SA_BLK + SA_ROW) of every window
@@ -159,11 +160,8 @@ struct Pass {
 #pragma unroll
     for (int s = 0; s < T::SA_LOADS; ++s) {
       const int g = (s * T::WAVES + wave) * 64 + lane;  // row g / SA_ROW, block g % SA_ROW
-      const uint32_t blk = (uint32_t)(c * T::SA_BLK) + (uint32_t)g % T::SA_ROW;
-      const uint32_t off = blk < (uint32_t)nkb
-                               ? ((uint32_t)g / T::SA_ROW * (uint32_t)nkb + blk) * 4u
-                               : kSkip;
-      dma4(rsa, lds_addr(buf + (s * T::WAVES + wave) * 64), off, 0);
+      dma4(rsa, lds_addr(buf + (s * T::WAVES + wave) * 64),
+           off::fp8_scale_voff(g, c, T::SA_BLK, T::SA_ROW, nkb), 0);
     }
   }
 
@@ -308,11 +306,7 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
   // row of this lane inside its load's 8-row group, and its swizzled chunk;
   // the group's first row 8 (s W + w) has bits 1..3 equal to 4 (w % 2)
   // because W is even, so the swizzle does not depend on s.
-  {
-    const int r8 = lane >> 3;
-    const int chunk = (lane & 7) ^ ((((wave & 1) << 3) + r8) >> 1 & 7);
-    ps.lane_off = (uint32_t)(wave * 8 + r8) * (uint32_t)K + (uint32_t)(chunk << 4);
-  }
+  ps.lane_off = off::fp8_lane_off(wave, lane, (uint32_t)K);
 
   // With split > 1 every pass of a tile is its own work item (the tile
   // order then needs no plan: no item costs more than one pass).

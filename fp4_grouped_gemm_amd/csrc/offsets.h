@@ -1,0 +1,74 @@
+// Buffer offsets of the staging loads, shared by the kernels (device) and a
+// host check that enumerates every load of a launch (tests/offsets_check.cpp).
+// Plain integer arithmetic, no HIP types.
+//
+// Every staging load reads through a raw buffer resource over one tile's
+// rows (or a whole operand).  The resource's range check covers the VGPR
+// offset of the load; the functions below put each lane's row (and the
+// parts that depend on the lane) in that offset, so that a row past the
+// tile's last row fails the check and reads zeros, and keep the SGPR
+// offset to a displacement inside the row.  kSkip is past every buffer
+// (all are below 2^31 bytes): loads that are not needed read zeros there.
+#pragma once
+
+#include <stdint.h>
+
+#ifdef __HIPCC__
+#define FGG_HD __host__ __device__ __forceinline__
+#else
+#define FGG_HD inline
+#endif
+
+namespace fgg {
+namespace off {
+
+constexpr uint32_t kSkip = 0x80000000u;
+
+// ---- grouped FP8 (tile rows of K bytes, K steps of 128 bytes) -------------
+// One 16-byte direct-to-LDS load per lane moves 8 tile rows (64 lanes x 16
+// bytes); lane l covers row 8 b + l / 8 of load b and reads the 16-byte chunk
+// that the XOR swizzle of the LDS layout puts at physical chunk l % 8:
+// logical chunk (l % 8) ^ ((row >> 1) & 7).  For load s of wave w (W waves,
+// W even), row = 8 (s W + w) + l / 8, and (row >> 1) & 7 depends on w % 2
+// and l / 8 only.
+FGG_HD uint32_t fp8_lane_off(int wave, int lane, uint32_t K) {
+  const int r8 = lane >> 3;
+  const int chunk = (lane & 7) ^ (((((wave & 1) << 3) + r8) >> 1) & 7);
+  return (uint32_t)(wave * 8 + r8) * K + (uint32_t)(chunk << 4);
+}
+// VGPR offset of load s (rows 8 (s W + w) ..) of a wave; kSkip when the load
+// is not needed.  The SGPR offset is fp8_step_soff(kb).
+FGG_HD uint32_t fp8_tile_voff(uint32_t lane_off, int s, int waves, uint32_t K, bool need) {
+  return need ? lane_off + (uint32_t)(s * waves * 8) * K : kSkip;
+}
+FGG_HD uint32_t fp8_step_soff(int kb) { return (uint32_t)kb * 128u; }
+// a_scale chunk c (sa_blk K blocks of every tile row, sa_row floats per row
+// in LDS): 4-byte load g of the chunk reads row g / sa_row, block
+// c sa_blk + g % sa_row; blocks past the row's last read zeros.
+FGG_HD uint32_t fp8_scale_voff(int g, int c, int sa_blk, int sa_row, int nkb) {
+  const uint32_t blk = (uint32_t)(c * sa_blk) + (uint32_t)g % (uint32_t)sa_row;
+  return blk < (uint32_t)nkb ? ((uint32_t)g / (uint32_t)sa_row * (uint32_t)nkb + blk) * 4u : kSkip;
+}
+
+// ---- NVFP4 (rows of Kp = K / 2 packed bytes and Ks = K / 16 scale bytes) --
+// Staging unit g covers half a 64-element K step of tile row g / 2: the 16
+// packed bytes at g % 2 * 16 of the step; the step's 32 bytes are the SGPR
+// offset fp4_code_soff(ks).
+FGG_HD uint32_t fp4_code_voff(int g, uint32_t Kp) {
+  return (uint32_t)(g >> 1) * Kp + (uint32_t)(g & 1) * 16u;
+}
+FGG_HD uint32_t fp4_code_soff(int ks) { return (uint32_t)ks * 32u; }
+// The scale codes of four steps [4c, 4c + 4) of row g / 2: 16 bytes at 16 c
+// of the row, the whole offset in the VGPR (row_off = row * Ks, or kSkip).
+FGG_HD uint32_t fp4_scale_row_off(int g, uint32_t Ks) { return (uint32_t)(g >> 1) * Ks; }
+FGG_HD uint32_t fp4_scale_voff(uint32_t row_off, int c) { return row_off + (uint32_t)c * 16u; }
+
+// ---- W4A16 (BF16 activation rows of K values, groups of 256) --------------
+// Chunk lc (8 values) of group gc of activation row `row`; chunks at or past
+// K read zeros.
+FGG_HD uint32_t w4a16_act_voff(uint32_t row, int lc, int gc, int K) {
+  return gc * 256 + lc * 8 < K ? row * (uint32_t)K * 2u + (uint32_t)(gc * 512 + lc * 16) : kSkip;
+}
+
+}  // namespace off
+}  // namespace fgg

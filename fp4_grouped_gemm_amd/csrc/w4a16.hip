@@ -34,6 +34,7 @@
 //    activation operand and lane (c, q) of the weight operand hold the same
 //    eight k, so every k pairs with itself.
 #include "common.h"
+#include "offsets.h"
 
 #include <climits>
 #include <utility>
@@ -110,13 +111,14 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t word, float s) {
 // LDS byte offset of 16-byte chunk c (0..31) of activation row r (0..31).
 __device__ __forceinline__ int a_swz(int r, int c) { return r * (kGroup * 2) + ((c ^ r) << 4); }
 static_assert(kChunks == kRows, "the chunk swizzle uses the row's 5 bits");
+static_assert(kGroup == 256, "off::w4a16_act_voff assumes groups of 256 values");
 
 struct Ctx {
   const uint8_t* bcol[kCB];   // weight row of this lane's column, per column block
   const uint8_t* scol[kCB];   // its scale codes
   i32x4 ra;                   // activation buffer resource (whole A)
-  uint32_t a_off[kADma];      // this lane's activation chunks: row offset + chunk
-  int a_k[kADma];             // their first K index within a group
+  uint32_t a_row[kADma];      // this lane's activation chunks: their rows
+  int a_lc[kADma];            // and logical chunks (8 values each) within a group
   uint32_t lds_a[kADma];      // their LDS destinations (stage 0)
   int ngroups;
   int K;
@@ -134,8 +136,7 @@ __device__ __forceinline__ void load_a(const Ctx& c, uint8_t* ring, int g) {
   const uint32_t st = (uint32_t)((g % kAStages) * kAStage);
 #pragma unroll
   for (int u = 0; u < kADma; ++u)
-    dma16(c.ra, c.lds_a[u] + st,
-          gc * kGroup + c.a_k[u] < c.K ? c.a_off[u] + (uint32_t)(gc * kGroup * 2) : kSkip, 0);
+    dma16(c.ra, c.lds_a[u] + st, off::w4a16_act_voff(c.a_row[u], c.a_lc[u], gc, c.K), 0);
   (void)ring;
 }
 
@@ -281,8 +282,8 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_kernel(const uint16_t* __re
       for (int u = 0; u < kADma; ++u) {
         const int p = u * kThreads + tid;
         const int row = p / kChunks, lc = (p % kChunks) ^ row;
-        c.a_off[u] = (uint32_t)rows[min(c0 + row, count - 1)] * (uint32_t)K * 2u + (uint32_t)lc * 16u;
-        c.a_k[u] = lc * 8;
+        c.a_row[u] = (uint32_t)rows[min(c0 + row, count - 1)];
+        c.a_lc[u] = lc;
         c.lds_a[u] = lds_addr(ring) + (uint32_t)(u * kThreads + wave * 64) * 16u;
       }
       f32x4 acc[kRB][kCB];

@@ -1,0 +1,133 @@
+// Host check of the staging loads' buffer offsets (fp4_grouped_gemm_amd/
+// csrc/offsets.h, the functions the kernels call): for every tile config,
+// every load of a pass is enumerated on tail shapes (a tile's last rows,
+// short and long K), and every access whose VGPR offset passes the range
+// check must lie inside the row it is meant for and inside the buffer; an
+// access that fails the check reads zeros and touches nothing.
+//
+//   g++ -O1 -std=c++17 -I fp4_grouped_gemm_amd/csrc tests/offsets_check.cpp -o offsets_check
+//
+// Exit status 0 and a summary line when every access is in bounds.
+#include <cstdint>
+#include <cstdio>
+#include <vector>
+
+#include "offsets.h"
+
+using namespace fgg::off;
+
+static long long checked = 0, skipped = 0, bad = 0;
+
+// An access of `size` bytes at voff + soff through a buffer of `records`
+// bytes, meant for bytes [lo, hi) of the buffer.
+static void access(uint64_t voff, uint64_t soff, uint64_t size, uint64_t records, uint64_t lo,
+                   uint64_t hi, const char* what) {
+  if (voff >= records) {  // fails the range check: zeros, no access
+    ++skipped;
+    return;
+  }
+  ++checked;
+  const uint64_t a = voff + soff, b = a + size;
+  if (a < lo || b > hi || b > records) {
+    if (++bad <= 10)
+      std::printf("OUT OF BOUNDS %s: [%llu, %llu) not in [%llu, %llu), records %llu\n", what,
+                  (unsigned long long)a, (unsigned long long)b, (unsigned long long)lo,
+                  (unsigned long long)hi, (unsigned long long)records);
+  }
+}
+
+struct Fp8Cfg {
+  int BM, BN, WAVES, SA_BLK, SA_ROW;
+};
+
+static void check_fp8(const Fp8Cfg& c, int rows, int K, bool is_a) {
+  const int nkb = K / 128;
+  const int tile_rows = is_a ? c.BM : c.BN;
+  const int loads = tile_rows / 8 / c.WAVES;
+  const uint64_t records = (uint64_t)rows * K;
+  for (int w = 0; w < c.WAVES; ++w)
+    for (int lane = 0; lane < 64; ++lane) {
+      const uint32_t lo = fp8_lane_off(w, lane, (uint32_t)K);
+      for (int s = 0; s < loads; ++s) {
+        const uint64_t row = 8ull * (s * c.WAVES + w) + lane / 8;
+        const uint32_t v = fp8_tile_voff(lo, s, c.WAVES, (uint32_t)K, true);
+        if (v != kSkip && v / K != row) {
+          ++bad;
+          std::printf("FP8 load s=%d w=%d lane=%d reads row %u, not %llu\n", s, w, lane, v / K,
+                      (unsigned long long)row);
+        }
+        for (int kb = 0; kb < nkb; ++kb)
+          access(v, fp8_step_soff(kb), 16, records, row * K, (row + 1) * K,
+                 is_a ? "fp8 A tile" : "fp8 B tile");
+        // a load that is not needed
+        access(fp8_tile_voff(lo, s, c.WAVES, (uint32_t)K, false), 0, 16, records, 0, 0,
+               "fp8 skipped load");
+      }
+    }
+  if (is_a) {  // the a_scale chunks of the tile rows
+    const uint64_t srec = (uint64_t)rows * nkb * 4;
+    const int chunks = (nkb + c.SA_BLK - 1) / c.SA_BLK + 1;
+    for (int ch = 0; ch < chunks; ++ch)
+      for (int g = 0; g < c.BM * c.SA_ROW; ++g) {
+        const uint64_t row = g / c.SA_ROW;
+        access(fp8_scale_voff(g, ch, c.SA_BLK, c.SA_ROW, nkb), 0, 4, srec, row * nkb * 4,
+               (row + 1) * nkb * 4, "fp8 a_scale");
+      }
+  }
+}
+
+static void check_fp4(int BM, int rows, int K) {
+  const uint32_t Kp = K / 2, Ks = K / 16;
+  const int nks = K / 64;
+  const uint64_t crec = (uint64_t)rows * Kp, srec = (uint64_t)rows * Ks;
+  for (int g = 0; g < 2 * BM; ++g) {
+    const uint64_t row = g / 2;
+    const uint32_t v = fp4_code_voff(g, Kp);
+    for (int ks = 0; ks < nks; ++ks)
+      access(v, fp4_code_soff(ks), 16, crec, row * Kp, (row + 1) * Kp, "fp4 codes");
+    // scale groups up to one past the last (the kernel loads a group ahead);
+    // only the codes of steps below nks are used, and those must be in the
+    // row; the rest of a 16-byte load may run into the next row, and past
+    // the buffer's end the range check (dword by dword) returns zeros
+    const uint32_t ro = fp4_scale_row_off(g, Ks);
+    for (int c = 0; c <= nks / 4 + 1; ++c) {
+      const int used = nks - 4 * c < 4 ? nks - 4 * c : 4;
+      if (used <= 0) {
+        access(fp4_scale_voff(ro, c), 0, 0, srec, 0, srec, "fp4 scales past the last step");
+        continue;
+      }
+      access(fp4_scale_voff(ro, c), 0, 4ull * used, srec, row * Ks, (row + 1) * Ks,
+             "fp4 scales (used bytes)");
+    }
+  }
+}
+
+static void check_w4a16(int M, int K) {
+  const uint64_t rec = (uint64_t)M * K * 2;
+  const int ngroups = (K + 255) / 256;
+  for (int row : {0, M / 2, M - 1})
+    for (int gc = 0; gc < ngroups; ++gc)
+      for (int lc = 0; lc < 32; ++lc)
+        access(w4a16_act_voff((uint32_t)row, lc, gc, K), 0, 16, rec, (uint64_t)row * K * 2,
+               (uint64_t)(row + 1) * K * 2, "w4a16 activations");
+}
+
+int main() {
+  const Fp8Cfg fp8[] = {{256, 256, 8, 8, 8}, {256, 128, 4, 3, 4}, {128, 256, 4, 3, 4},
+                        {128, 128, 4, 3, 4}};
+  for (const Fp8Cfg& c : fp8)
+    for (int K : {128, 384, 640, 7168})
+      for (int rows : {1, 7, 8, 9, 63, 64, 65, 127, 128, 129, 255, 256}) {
+        if (rows <= c.BM) check_fp8(c, rows, K, true);
+        if (rows <= c.BN) check_fp8(c, rows, K, false);
+      }
+  for (int BM : {128, 256})
+    for (int K : {128, 256, 384, 640, 4608})
+      for (int rows : {1, 2, 63, 64, 65, 127, 128, 255, 256})
+        if (rows <= BM) check_fp4(BM, rows, K);
+  for (int K : {128, 384, 640, 1408, 8192})
+    for (int M : {1, 2, 33, 1025}) check_w4a16(M, K);
+  std::printf("offsets: %lld accesses checked in range, %lld skipped by the range check, %lld out of "
+              "bounds\n", checked, skipped, bad);
+  return bad == 0 ? 0 : 1;
+}
