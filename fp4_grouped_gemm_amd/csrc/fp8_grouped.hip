@@ -85,21 +85,23 @@ struct Fp8Cfg {
   static_assert(PF_LOADS == 0 || (BM + BN) % (64 * WAVES) == 0, "prefetch split");
 };
 
-// LDS byte offset of 16-byte chunk `c` (0..7) of tile row `r`.  The chunk
-// is XOR-swizzled with bits 1..3 of the row, so the 16 rows that one
-// fragment read touches (128-byte rows, two per 256-byte bank line) land on
-// 16 distinct bank groups.
-__device__ __forceinline__ int swz(int r, int c) { return (r << 7) | ((c ^ ((r >> 1) & 7)) << 4); }
+// LDS byte offset of 16-byte chunk `c` (0..7) of tile row `r`: an XOR
+// swizzle whose key (offsets.h) keeps every cycle of a fragment read free of
+// bank conflicts.
+__device__ __forceinline__ int swz(int r, int c) { return off::fp8_lds_off(r, c); }
 
 // Fragment of 16 rows x 128 K bytes for v_mfma_*_16x16x128 with 8-bit
 // operands: lane l holds row (l % 16) and K bytes [32 q, 32 q + 32), q = l / 16.
 // The A and B operands use the same lane/K assignment, so the product sums
 // over every k exactly once whatever order the hardware uses inside a lane.
+// row0 is a multiple of 16 and the swizzle key reads row bits 1..3 only, so
+// the lane's part of the offset does not depend on row0.
 __device__ __forceinline__ i32x8 read_frag(const uint8_t* tile, int row0, int lane) {
-  const int r = row0 + (lane & 15);
+  const uint8_t* p = tile + row0 * 128;
+  const int r = lane & 15;
   const int q = lane >> 4;
-  const i32x4 lo = *reinterpret_cast<const i32x4*>(tile + swz(r, 2 * q));
-  const i32x4 hi = *reinterpret_cast<const i32x4*>(tile + swz(r, 2 * q + 1));
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(p + swz(r, 2 * q));
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(p + swz(r, 2 * q + 1));
   return (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -108,7 +110,7 @@ using namespace lds_dma;
 // Per-pass state: buffer resources, offsets, the b_scale row, accumulators.
 //  * A/B staging: a tile row is K bytes for both operands; lane l of a
 //    1 KB load writes LDS bytes [16 l, 16 l + 16) = tile row 8 b + l / 8,
-//    physical chunk l % 8, so it fetches logical chunk (l % 8) ^ (row % 8).
+//    physical chunk l % 8, so it fetches logical chunk (l % 8) ^ key(row).
 //    Load s of wave w covers rows 8 (s W + w) .. + 7: the lane's offset
 //    (row and chunk) goes in the instruction's VGPR offset, which the buffer
 //    range check covers, so rows past the tile's last row return zeros

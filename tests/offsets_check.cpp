@@ -3,7 +3,9 @@
 // every load of a pass is enumerated on tail shapes (a tile's last rows,
 // short and long K), and every access whose VGPR offset passes the range
 // check must lie inside the row it is meant for and inside the buffer; an
-// access that fails the check reads zeros and touches nothing.
+// access that fails the check reads zeros and touches nothing.  The FP8
+// tiles' LDS layout is checked too: the loads put every chunk where the
+// fragment reads look for it, and those reads are free of bank conflicts.
 //
 //   g++ -O1 -std=c++17 -I fp4_grouped_gemm_amd/csrc tests/offsets_check.cpp -o offsets_check
 //
@@ -76,6 +78,45 @@ static void check_fp8(const Fp8Cfg& c, int rows, int K, bool is_a) {
   }
 }
 
+// The LDS side of the FP8 staging: the direct-to-LDS loads (lane l of load
+// b writes bytes [16 l, 16 l + 16) of the load's 1 KB) must put tile row r,
+// chunk c where the fragment reads look for it (fp8_lds_off), and each
+// 16-lane cycle of a fragment read (lanes with equal bit 5 and equal parity
+// of bits 2..4) must hit 16 distinct 16-byte bank groups.
+static long long layout_checked = 0;
+static void check_fp8_layout(const Fp8Cfg& c, int tile_rows) {
+  const uint32_t K = 1024;  // any row length: the chunk is the in-row offset
+  std::vector<int> at(tile_rows * 8, -1);  // physical 16-byte slot -> row * 8 + chunk
+  for (int w = 0; w < c.WAVES; ++w)
+    for (int lane = 0; lane < 64; ++lane)
+      for (int s = 0; s < tile_rows / 8 / c.WAVES; ++s) {
+        const uint32_t v = fp8_tile_voff(fp8_lane_off(w, lane, K), s, c.WAVES, K, true);
+        const int slot = (s * c.WAVES + w) * 64 + lane;
+        at[slot] = (int)(v / K) * 8 + (int)(v % K) / 16;
+      }
+  for (int row = 0; row < tile_rows; ++row)
+    for (int ch = 0; ch < 8; ++ch) {
+      ++layout_checked;
+      if (at[fp8_lds_off(row, ch) / 16] != row * 8 + ch && ++bad <= 10)
+        std::printf("FP8 LDS layout: row %d chunk %d is not where the fragment read looks\n", row,
+                    ch);
+    }
+  for (int r0 = 0; r0 < tile_rows; r0 += 16)
+    for (int half = 0; half < 2; ++half)
+      for (int cyc = 0; cyc < 4; ++cyc) {
+        int seen = 0;
+        for (int lane = 0; lane < 64; ++lane) {
+          const int par = ((lane >> 2) ^ (lane >> 3) ^ (lane >> 4)) & 1;
+          if (((lane >> 5) & 1) * 2 + par != cyc) continue;
+          const int bank = (fp8_lds_off(r0 + (lane & 15), 2 * (lane >> 4) + half) / 16) % 16;
+          seen |= 1 << bank;
+        }
+        ++layout_checked;
+        if (seen != 0xffff && ++bad <= 10)
+          std::printf("FP8 fragment read rows %d.. half %d cycle %d: bank conflict\n", r0, half, cyc);
+      }
+}
+
 static void check_fp4(int BM, int rows, int K) {
   const uint32_t Kp = K / 2, Ks = K / 16;
   const int nks = K / 64;
@@ -115,6 +156,10 @@ static void check_w4a16(int M, int K) {
 int main() {
   const Fp8Cfg fp8[] = {{256, 256, 8, 8, 8}, {256, 128, 4, 3, 4}, {128, 256, 4, 3, 4},
                         {128, 128, 4, 3, 4}};
+  for (const Fp8Cfg& c : fp8) {
+    check_fp8_layout(c, c.BM);
+    check_fp8_layout(c, c.BN);
+  }
   for (const Fp8Cfg& c : fp8)
     for (int K : {128, 384, 640, 7168})
       for (int rows : {1, 7, 8, 9, 63, 64, 65, 127, 128, 129, 255, 256}) {
@@ -127,7 +172,7 @@ int main() {
         if (rows <= BM) check_fp4(BM, rows, K);
   for (int K : {128, 384, 640, 1408, 8192})
     for (int M : {1, 2, 33, 1025}) check_w4a16(M, K);
-  std::printf("offsets: %lld accesses checked in range, %lld skipped by the range check, %lld out of "
-              "bounds\n", checked, skipped, bad);
+  std::printf("offsets: %lld accesses checked in range, %lld skipped by the range check, %lld LDS "
+              "layout and bank checks, %lld failed\n", checked, skipped, layout_checked, bad);
   return bad == 0 ? 0 : 1;
 }

@@ -1,7 +1,9 @@
 """The staging loads' buffer offsets (csrc/offsets.h, the arithmetic the
 kernels call) checked on the host: tests/offsets_check.cpp enumerates every
 load of every tile config on tail shapes and asserts that each access that
-passes the buffer range check lies inside its row and its buffer."""
+passes the buffer range check lies inside its row and its buffer, that the
+FP8 tiles land in LDS where the fragment reads look for them, and that those
+reads are free of bank conflicts under gfx950's lane grouping."""
 import os
 import shutil
 import subprocess
@@ -22,4 +24,4 @@ def test_staging_offsets_stay_in_bounds():
         r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     print(r.stdout)
     assert r.returncode == 0, r.stdout
-    assert "0 out of bounds" in r.stdout
+    assert " 0 failed" in r.stdout
