@@ -36,17 +36,8 @@
 
 #include <climits>
 
-#ifndef FGG_FP8_PF
-#define FGG_FP8_PF 0
-#endif
-
 namespace fgg {
 namespace fp8_detail {
-
-// L2 prefetch distance: with 2 LDS stages, step kb stages step kb + 1 and
-// also touches one 4-byte word of every tile row of step kb + 1 + kPf, so
-// that row's 128-byte line is in L2 when its staging load comes (0: off).
-constexpr int kPf = FGG_FP8_PF;
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int SA_BLK_, int SA_ROW_>
 struct Fp8Cfg {
@@ -80,9 +71,6 @@ struct Fp8Cfg {
   static constexpr int VM_TILE = A_LOADS + B_LOADS;  // loads per step into the A/B ring
   static_assert(WAVES % 2 == 0, "the staging swizzle assumes an even wave count");
   static_assert(WM == 64 && BM <= 512, "one row per lane in the pass masks");
-  // L2 prefetch loads per wave per step (one row per lane; 2-stage shapes)
-  static constexpr int PF_LOADS = (kPf > 0 && STAGES == 2) ? (BM + BN) / 64 / WAVES : 0;
-  static_assert(PF_LOADS == 0 || (BM + BN) % (64 * WAVES) == 0, "prefetch split");
 };
 
 // LDS byte offset of 16-byte chunk `c` (0..7) of tile row `r`: an XOR
@@ -134,11 +122,12 @@ struct Pass {
   bool active;                    // this wave's 64 rows hold a row of this pass
   f32x4 acc[T::TM][T::TN];
 
-  __device__ __forceinline__ void stage_in(uint8_t* st, int kb, int wave) const {
-    // Groups of rows of other experts are not needed.  With 3 stages their
-    // loads go past the buffer end (zeros, no memory traffic), so that every
-    // step issues the same number of loads, which the waits count; with 2
-    // stages (the wait is for all loads) they are skipped.
+  // Step kb's A tile into stage `st`.  Groups of rows of other experts are
+  // not needed.  With 3 stages their loads go past the buffer end (zeros, no
+  // memory traffic), so that every step issues the same number of loads,
+  // which the waits count; with 2 stages (the wait is for all loads) they
+  // are skipped.
+  __device__ __forceinline__ void stage_a(uint8_t* st, int kb, int wave) const {
 #pragma unroll
     for (int s = 0; s < T::A_LOADS; ++s) {
       const bool need = (a_groups >> (s * T::WAVES + wave)) & 1;
@@ -146,10 +135,16 @@ struct Pass {
       dma16(ra, lds_addr(st + (s * T::WAVES + wave) * 1024),
             off::fp8_tile_voff(lane_off, s, T::WAVES, K, need), off::fp8_step_soff(kb));
     }
+  }
+  __device__ __forceinline__ void stage_b(uint8_t* st, int kb, int wave) const {
 #pragma unroll
     for (int s = 0; s < T::B_LOADS; ++s)
       dma16(rb, lds_addr(st + T::A_BYTES + (s * T::WAVES + wave) * 1024),
             off::fp8_tile_voff(lane_off, s, T::WAVES, K, true), off::fp8_step_soff(kb));
+  }
+  __device__ __forceinline__ void stage_in(uint8_t* st, int kb, int wave) const {
+    stage_a(st, kb, wave);
+    stage_b(st, kb, wave);
   }
 
   // a_scale values of K blocks [c SA_BLK, c SA_BLK + SA_ROW) of every window
@@ -167,50 +162,65 @@ struct Pass {
     }
   }
 
-  // Blocks [kb, kb + 64) of the b_scale row into bs_vec (kb a multiple of 64).
+  // Blocks [kb, kb + 64) of the b_scale row into bs_vec (kb a multiple of
+  // 64).  The value is used at once (the empty asm reads it), so the compiler
+  // waits for this load here and nowhere else: its own waits do not see the
+  // staging loads (inline assembly), and a wait for this load placed inside
+  // the K loop would drain them.
   __device__ __forceinline__ void load_b_scales(int kb, int lane) {
     bs_vec = kb + lane < nkb ? bs_row[kb + lane] : 0.f;
+    asm volatile("" ::"v"(bs_vec));
   }
   __device__ __forceinline__ float b_scale_of(int kb) const {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bs_vec), kb & 63));
   }
-
-  // L2 prefetch of step kb's tile rows: instruction s of wave w covers row
-  // (s W + w) 64 + lane of [A rows; B rows], one 4-byte direct-to-LDS load
-  // into the wave's scratch slot (its value is never read).  A rows of other
-  // experts are skipped; rows past a tile fail the range check.
-  __device__ __forceinline__ void prefetch(uint8_t* scratch, int kb, int wave, int lane) const {
-#pragma unroll
-    for (int s = 0; s < T::PF_LOADS; ++s) {
-      const int r0 = (s * T::WAVES + wave) * 64;  // uniform
-      if (r0 < T::BM) {
-        const int r = r0 + lane;
-        const bool need = (a_groups >> (r >> 3)) & 1;
-        dma4(ra, lds_addr(scratch + wave * 256), need ? (uint32_t)r * K : kSkip, kb * 128);
-      } else {
-        dma4(rb, lds_addr(scratch + wave * 256), (uint32_t)(r0 - T::BM + lane) * K, kb * 128);
-      }
-    }
-  }
 };
+
+// MFMA slot t of a K step (t = j TM + i: column subtile j, row subtile i,
+// j-major) and the promotion of slot t - LAG: the partial of an MFMA is
+// promoted LAG MFMAs later, from a small ring, so the FMAs overlap the
+// following MFMAs and few partials are live at once; the next column
+// subtile's B fragment is read TM MFMAs before its first use.
+constexpr int kLag = 3;
+template <class T>
+__device__ __forceinline__ void mfma_slot(Pass<T>& ps, int t, i32x8& bf, i32x8& bnext,
+                                          const i32x8* af, f32x4* ring, float* s, const float* sa,
+                                          float sb, const uint8_t* rb, int wn, int lane) {
+  constexpr int NT = T::TM * T::TN;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  if (t < NT) {
+    const int j = t / T::TM, i = t % T::TM;
+    if (i == 0) {
+      if (j > 0) bf = bnext;
+      if (j + 1 < T::TN) bnext = read_frag(rb, wn * T::WN + (j + 1) * 16, lane);
+    }
+    ring[t % (kLag + 1)] =
+        __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], zero, 0, 0, 0, 127, 0, 127);
+  }
+  if (t >= kLag) {
+    const int u = t - kLag;
+    const int j = u / T::TM, i = u % T::TM;
+    // the combined scale of row subtile i at its first use, so that the
+    // wait for its a_scale read comes after the first MFMAs
+    if (j == 0) s[i] = sa[i] * sb;
+    ps.acc[i][j] += ring[u % (kLag + 1)] * s[i];
+  }
+  // Keep this order: left to itself the scheduler moves the FMAs next to
+  // the MFMA whose result they read and the fragment reads next to their
+  // use, which stalls on both latencies.
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // One K step: start staging step kb + STAGES - 1 into `wr` (if any), then
 // compute step kb from `rd`, then wait for step kb + 1's tiles and barrier.
 // `rd` and `wr` are distinct __shared__ arrays (likewise the a_scale chunk
 // buffers), which lets the compiler see that the LDS reads of `rd` do not
-// depend on the loads still filling `wr`.  The partial of column subtile j is
-// promoted into the FP32 accumulator while the MFMAs of subtile j+1 run.
+// depend on the loads still filling `wr`.
 template <class T>
 __device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* wr,
                                       const float* sa_rd, float* sa_wr, int kb, int lane, int wave,
-                                      int wm, int wn, uint8_t* pf_scratch) {
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  // this step's combined scales; read before any load of this step is issued
+                                      int wm, int wn) {
   const float sb = ps.b_scale_of(kb);
-  float s[T::TM];
-#pragma unroll
-  for (int i = 0; i < T::TM; ++i)
-    s[i] = sa_rd[(wm * T::WM + i * 16 + (lane & 15)) * T::SA_ROW + (unsigned)kb % T::SA_BLK] * sb;
   const int kl = kb + T::STAGES - 1;  // the step whose tiles this step loads
   const bool load = kl < ps.nkb;
   // the next a_scale chunk, at the first step of a chunk (implies `load`)
@@ -219,55 +229,28 @@ __device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* w
     ps.stage_in(wr, kl, wave);
     if (sload) ps.stage_scales(sa_wr, (unsigned)kb / T::SA_BLK + 1, wave, lane);
   }
-  // issued after this step's staging loads, so waiting for those leaves it
-  // in flight (loads complete in issue order)
-  const bool pf = T::PF_LOADS > 0 && kl + kPf < ps.nkb;
-  if (pf) ps.prefetch(pf_scratch, kl + kPf, wave, lane);
-  // next chunk of 64 b_scale blocks after the last use of this one (rare:
-  // K above 8192; the compiler's wait for it drains the loads in flight)
-  if ((kb & 63) == 63 && kb + 1 < ps.nkb) ps.load_b_scales(kb + 1, lane);
   if (ps.active) {
-  // B fragment first: the first MFMA then waits for it and A fragment 0 only
-  const uint8_t* rb = rd + T::A_BYTES;
-  i32x8 bf = read_frag(rb, wn * T::WN, lane);
-  i32x8 af[T::TM];
+    constexpr int NT = T::TM * T::TN;
+    const uint8_t* rb = rd + T::A_BYTES;
+    i32x8 bf, bnext, af[T::TM];
+    f32x4 ring[kLag + 1];
+    float sa[T::TM], s[T::TM];
+    // B fragment first: the first MFMA then waits for it and A fragment 0
+    // only; the a_scale values of the lane's rows after the fragments
+    bf = read_frag(rb, wn * T::WN, lane);
 #pragma unroll
-  for (int i = 0; i < T::TM; ++i) af[i] = read_frag(rd, wm * T::WM + i * 16, lane);
-  i32x8 bnext = bf;
-  // MFMA t = (column subtile j, row subtile i) in j-major order; its partial
-  // is promoted LAG MFMAs later, from a small ring, so the FMAs overlap the
-  // following MFMAs and few partials are live at once; the next column
-  // subtile's B fragment is read TM MFMAs before its first use.
-  constexpr int NT = T::TM * T::TN;
-  constexpr int LAG = 3;
-  f32x4 ring[LAG + 1];
+    for (int i = 0; i < T::TM; ++i) af[i] = read_frag(rd, wm * T::WM + i * 16, lane);
+    bnext = bf;
 #pragma unroll
-  for (int t = 0; t < NT + LAG; ++t) {
-    if (t < NT) {
-      const int j = t / T::TM, i = t % T::TM;
-      if (i == 0) {
-        if (j > 0) bf = bnext;
-        if (j + 1 < T::TN) bnext = read_frag(rb, wn * T::WN + (j + 1) * 16, lane);
-      }
-      ring[t % (LAG + 1)] =
-          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], zero, 0, 0, 0, 127, 0, 127);
-    }
-    if (t >= LAG) {
-      const int u = t - LAG;
-      const int j = u / T::TM, i = u % T::TM;
-      ps.acc[i][j] += ring[u % (LAG + 1)] * s[i];
-    }
-    // Keep this order: left to itself the scheduler moves the FMAs next to
-    // the MFMA whose result they read and the fragment reads next to their
-    // use, which stalls on both latencies.
+    for (int i = 0; i < T::TM; ++i)
+      sa[i] = sa_rd[(wm * T::WM + i * 16 + (lane & 15)) * T::SA_ROW + (unsigned)kb % T::SA_BLK];
     __builtin_amdgcn_sched_barrier(0);
-  }
+#pragma unroll
+    for (int t = 0; t < NT + kLag; ++t) mfma_slot<T>(ps, t, bf, bnext, af, ring, s, sa, sb, rb, wn, lane);
   }
   if constexpr (T::STAGES == 2) {
-    // step kb + 1's tiles were issued in this step (the prefetch after them
-    // may stay in flight)
-    if (T::PF_LOADS > 0 && pf) wait_vmem<T::PF_LOADS>();
-    else wait_vmem<0>();
+    // step kb + 1's tiles were issued in this step
+    wait_vmem<0>();
     lds_barrier();
   } else {
     // Step kb + 1's tiles were issued one step ago: only this step's loads
@@ -277,6 +260,9 @@ __device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* w
     else wait_vmem<T::VM_TILE>();
     lds_barrier();
   }
+  // next chunk of 64 b_scale blocks (K above 8192; its wait drains the
+  // loads in flight, once every 64 steps)
+  if ((kb & 63) == 63 && kb + 1 < ps.nkb) ps.load_b_scales(kb + 1, lane);
 }
 
 template <class T>
@@ -293,7 +279,6 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
   __shared__ int ids[T::BM];
   __shared__ uint32_t plan_bits[kPlanWords];
   __shared__ int plan_heavy;
-  __shared__ __attribute__((aligned(256))) uint8_t pf_scratch[T::PF_LOADS > 0 ? T::WAVES * 256 : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -396,15 +381,15 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
       ps.stage_scales(sa0, 0, wave, lane);
       if constexpr (T::STAGES == 2) {
         wait_vmem<0>();
-        __syncthreads();
+        lds_barrier();
         // K steps two at a time (LDS stage parity), scale chunks of SA_BLK
         // steps alternate between sa0 and sa1.
         for (int kb = 0; kb < nkb; kb += 2) {
           const bool odd_chunk = ((unsigned)kb / T::SA_BLK) & 1;
           float* sa_rd = odd_chunk ? sa1 : sa0;
           float* sa_wr = odd_chunk ? sa0 : sa1;
-          kstep<T>(ps, lds0, lds1, sa_rd, sa_wr, kb, lane, wave, wm, wn, pf_scratch);
-          if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa_rd, sa_wr, kb + 1, lane, wave, wm, wn, pf_scratch);
+          kstep<T>(ps, lds0, lds1, sa_rd, sa_wr, kb, lane, wave, wm, wn);
+          if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa_rd, sa_wr, kb + 1, lane, wave, wm, wn);
         }
       } else {
         if (nkb > 1) {
@@ -417,12 +402,12 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
         // Six steps per iteration: stage = kb % 3 and scale chunk kb / 3
         // (alternating sa0 / sa1) are then known at compile time.
         for (int kb = 0; kb < nkb; kb += 6) {
-          kstep<T>(ps, lds0, lds2, sa0, sa1, kb, lane, wave, wm, wn, pf_scratch);
-          if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa0, sa1, kb + 1, lane, wave, wm, wn, pf_scratch);
-          if (kb + 2 < nkb) kstep<T>(ps, lds2, lds1, sa0, sa1, kb + 2, lane, wave, wm, wn, pf_scratch);
-          if (kb + 3 < nkb) kstep<T>(ps, lds0, lds2, sa1, sa0, kb + 3, lane, wave, wm, wn, pf_scratch);
-          if (kb + 4 < nkb) kstep<T>(ps, lds1, lds0, sa1, sa0, kb + 4, lane, wave, wm, wn, pf_scratch);
-          if (kb + 5 < nkb) kstep<T>(ps, lds2, lds1, sa1, sa0, kb + 5, lane, wave, wm, wn, pf_scratch);
+          kstep<T>(ps, lds0, lds2, sa0, sa1, kb, lane, wave, wm, wn);
+          if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa0, sa1, kb + 1, lane, wave, wm, wn);
+          if (kb + 2 < nkb) kstep<T>(ps, lds2, lds1, sa0, sa1, kb + 2, lane, wave, wm, wn);
+          if (kb + 3 < nkb) kstep<T>(ps, lds0, lds2, sa1, sa0, kb + 3, lane, wave, wm, wn);
+          if (kb + 4 < nkb) kstep<T>(ps, lds1, lds0, sa1, sa0, kb + 4, lane, wave, wm, wn);
+          if (kb + 5 < nkb) kstep<T>(ps, lds2, lds1, sa1, sa0, kb + 5, lane, wave, wm, wn);
         }
       }
 
