@@ -43,20 +43,24 @@ def _compile(src: str) -> str:
     return out
 
 
-PROBE_SRC = os.path.join(ROOT, "bench", "mfma_peak.hip")
+PROBES = ["mfma_peak", "lds_banks"]
 PROBE = os.path.join(ROOT, "bench", "mfma_peak")
 
 
 def build_probe(verbose: bool = False) -> str:
-    """Build the roofline microbenchmark bench/mfma_peak (a standalone HIP
-    program; not part of the library)."""
-    cmd = [HIPCC, *[f for f in FLAGS if f not in ("-fPIC",) and not f.startswith("-I")],
-           PROBE_SRC, "-o", PROBE]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
-    if verbose:
-        print("built", PROBE)
+    """Build the microbenchmarks in bench/ (standalone HIP programs, not part
+    of the library): mfma_peak (roofline legs) and lds_banks (LDS
+    bank-conflict patterns)."""
+    for name in PROBES:
+        src = os.path.join(ROOT, "bench", name + ".hip")
+        exe = os.path.join(ROOT, "bench", name)
+        cmd = [HIPCC, *[f for f in FLAGS if f not in ("-fPIC",) and not f.startswith("-I")],
+               src, "-o", exe]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        if verbose:
+            print("built", exe)
     return PROBE
 
 
