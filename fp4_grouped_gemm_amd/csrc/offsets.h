@@ -78,6 +78,16 @@ FGG_HD uint32_t fp4_scale_row_off(int g, uint32_t Ks) { return (uint32_t)(g >> 1
 FGG_HD uint32_t fp4_scale_voff(uint32_t row_off, int c) { return row_off + (uint32_t)c * 16u; }
 
 // ---- W4A16 (BF16 activation rows of K values, groups of 256) --------------
+// LDS layout of a staged activation group: row r (0..31) at 512 r, its
+// 16-byte chunk c (0..31) at physical chunk c ^ w4a16_swz_key(r).  A
+// fragment read gives lane l row 16 rb + l % 16 and chunk 8 (l / 16) + t;
+// under the 16-lane read grouping (see the FP8 layout above) the key (row
+// bits 0, 1, 2 ^ 3, 3, 4) gives each cycle's lanes 16 distinct bank groups
+// (row bits 0..4 as the key would give 8).
+FGG_HD int w4a16_swz_key(int row) {
+  return (row & 3) | ((((row >> 2) ^ (row >> 3)) & 1) << 2) | (row & 24);
+}
+FGG_HD int w4a16_lds_off(int row, int chunk) { return row * 512 + ((chunk ^ w4a16_swz_key(row)) << 4); }
 // Chunk lc (8 values) of group gc of activation row `row`; chunks at or past
 // K read zeros.
 FGG_HD uint32_t w4a16_act_voff(uint32_t row, int lc, int gc, int K) {

@@ -108,9 +108,11 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t word, float s) {
   return r;
 }
 
-// LDS byte offset of 16-byte chunk c (0..31) of activation row r (0..31).
-__device__ __forceinline__ int a_swz(int r, int c) { return r * (kGroup * 2) + ((c ^ r) << 4); }
-static_assert(kChunks == kRows, "the chunk swizzle uses the row's 5 bits");
+// LDS byte offset of 16-byte chunk c (0..31) of activation row r (0..31):
+// an XOR swizzle whose key (offsets.h) keeps every cycle of a fragment read
+// free of bank conflicts.
+__device__ __forceinline__ int a_swz(int r, int c) { return off::w4a16_lds_off(r, c); }
+static_assert(kChunks == kRows && kGroup * 2 == 512, "the chunk swizzle uses the row's 5 bits");
 static_assert(kGroup == 256, "off::w4a16_act_voff assumes groups of 256 values");
 
 struct Ctx {
@@ -276,12 +278,12 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_kernel(const uint16_t* __re
     for (int c0 = 0; c0 < count; c0 += kRows) {
       // This thread's activation chunks: LDS chunk p = u * 256 + tid of a
       // stage is row p / kChunks, physical chunk p % kChunks, which holds
-      // logical chunk (p % kChunks) ^ row; rows past the chunk read a valid
-      // row and are never stored.
+      // logical chunk (p % kChunks) ^ key(row); rows past the chunk read a
+      // valid row and are never stored.
 #pragma unroll
       for (int u = 0; u < kADma; ++u) {
         const int p = u * kThreads + tid;
-        const int row = p / kChunks, lc = (p % kChunks) ^ row;
+        const int row = p / kChunks, lc = (p % kChunks) ^ off::w4a16_swz_key(row);
         c.a_row[u] = (uint32_t)rows[min(c0 + row, count - 1)];
         c.a_lc[u] = lc;
         c.lds_a[u] = lds_addr(ring) + (uint32_t)(u * kThreads + wave * 64) * 16u;

@@ -4,8 +4,9 @@
 // short and long K), and every access whose VGPR offset passes the range
 // check must lie inside the row it is meant for and inside the buffer; an
 // access that fails the check reads zeros and touches nothing.  The FP8
-// tiles' LDS layout is checked too: the loads put every chunk where the
-// fragment reads look for it, and those reads are free of bank conflicts.
+// tiles' and the W4A16 activation stage's LDS layouts are checked too: the
+// loads put every chunk where the fragment reads look for it, and those
+// reads are free of bank conflicts.
 //
 //   g++ -O1 -std=c++17 -I fp4_grouped_gemm_amd/csrc tests/offsets_check.cpp -o offsets_check
 //
@@ -117,6 +118,33 @@ static void check_fp8_layout(const Fp8Cfg& c, int tile_rows) {
       }
 }
 
+// The W4A16 activation stage: staging chunk p (row p / 32, physical chunk
+// p % 32) fetches logical chunk (p % 32) ^ key(row), which must be where
+// the fragment reads look for it; each 16-lane cycle of a read (rows
+// 16 rb + l % 16, chunk 8 (l / 16) + t) must hit 16 distinct bank groups.
+static void check_w4a16_layout() {
+  for (int p = 0; p < 32 * 32; ++p) {
+    const int row = p / 32, phys = p % 32;
+    const int lc = phys ^ w4a16_swz_key(row);
+    ++layout_checked;
+    if (w4a16_lds_off(row, lc) != row * 512 + phys * 16 && ++bad <= 10)
+      std::printf("W4A16 layout: row %d chunk %d misplaced\n", row, lc);
+  }
+  for (int rb = 0; rb < 2; ++rb)
+    for (int t = 0; t < 8; ++t)
+      for (int cyc = 0; cyc < 4; ++cyc) {
+        int seen = 0;
+        for (int lane = 0; lane < 64; ++lane) {
+          const int par = ((lane >> 2) ^ (lane >> 3) ^ (lane >> 4)) & 1;
+          if (((lane >> 5) & 1) * 2 + par != cyc) continue;
+          seen |= 1 << ((w4a16_lds_off(16 * rb + (lane & 15), 8 * (lane >> 4) + t) / 16) % 16);
+        }
+        ++layout_checked;
+        if (seen != 0xffff && ++bad <= 10)
+          std::printf("W4A16 read rb %d t %d cycle %d: bank conflict\n", rb, t, cyc);
+      }
+}
+
 static void check_fp4(int BM, int rows, int K) {
   const uint32_t Kp = K / 2, Ks = K / 16;
   const int nks = K / 64;
@@ -172,6 +200,7 @@ int main() {
         if (rows <= BM) check_fp4(BM, rows, K);
   for (int K : {128, 384, 640, 1408, 8192})
     for (int M : {1, 2, 33, 1025}) check_w4a16(M, K);
+  check_w4a16_layout();
   std::printf("offsets: %lld accesses checked in range, %lld skipped by the range check, %lld LDS "
               "layout and bank checks, %lld failed\n", checked, skipped, layout_checked, bad);
   return bad == 0 ? 0 : 1;
