@@ -90,14 +90,14 @@ QUANT_METRIC = "GB/s (algorithmic bytes / time) and % of HBM peak, activation qu
 # Source files each workload's kernels are built from: a committed traffic
 # profile stays valid while these are unchanged.
 KERNEL_SOURCES = {
-    "fp8": ("fp8_grouped.hip", "common.h"),
-    "fp4": ("fp4.hip", "common.h"),
-    "fp4_problems": ("fp4.hip", "common.h"),
+    "fp8": ("fp8_grouped.hip", "common.h", "offsets.h"),
+    "fp4": ("fp4.hip", "common.h", "offsets.h"),
+    "fp4_problems": ("fp4.hip", "common.h", "offsets.h"),
     "quant_fp8": ("quant.hip", "common.h"),
     "quant_nvfp4": ("quant.hip", "common.h"),
     "quant_nvfp4_static": ("quant.hip", "common.h"),
     "quant_fp8_expand": ("quant.hip", "common.h"),
-    "w4a16": ("w4a16.hip", "common.h"),
+    "w4a16": ("w4a16.hip", "common.h", "offsets.h"),
 }
 
 
