@@ -311,6 +311,31 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
     const int col0 = ntile * T::BN;
 
     __syncthreads();  // the previous tile is done with ids[] and the stages
+
+    // Rows (A) and columns (B) of this tile that exist; loads past them
+    // read zeros and those rows / columns are never stored.
+    const int rows_a = min(T::BM, M - row0);
+    const int rows_b = min(T::BN, N - col0);
+    ps.ra = rsrc(A + (size_t)row0 * K, (uint32_t)rows_a * (uint32_t)K);
+    ps.rsa = rsrc(a_scale + (size_t)row0 * nkb, (uint32_t)rows_a * (uint32_t)nkb * 4u);
+    const int wcol0 = col0 + wn * T::WN;
+
+    // The A tiles of the first two K steps and the first a_scale chunk
+    // depend on the window only, not on the routing: the 3-stage shapes
+    // issue them now, every row group, so that they travel with the
+    // m_indices reads instead of after them, and the first pass that runs
+    // uses them (rows of other experts are computed and never stored).  The
+    // 2-stage 256x256 shape, which holds all 256 VGPRs in its K loop, does
+    // not: there the early offsets spill.
+    bool a_pre = false;
+    if constexpr (T::STAGES > 2) {
+      ps.a_groups = ~0ull;
+      ps.stage_a(lds0, 0, wave);
+      ps.stage_scales(sa0, 0, wave, lane);
+      if (nkb > 1) ps.stage_a(lds1, 1, wave);
+      a_pre = true;
+    }
+
     for (int r = tid; r < T::BM; r += T::THREADS) {
       const int gr = row0 + r;
       int e = -2;  // past the end of A: never stored
@@ -330,14 +355,6 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
       if (ids[r] == -1 && col < N && run_sel == 0)
         *reinterpret_cast<uint4*>(C + (size_t)(row0 + r) * N + col) = make_uint4(0, 0, 0, 0);
     }
-
-    // Rows (A) and columns (B) of this tile that exist; loads past them
-    // read zeros and those rows / columns are never stored.
-    const int rows_a = min(T::BM, M - row0);
-    const int rows_b = min(T::BN, N - col0);
-    ps.ra = rsrc(A + (size_t)row0 * K, (uint32_t)rows_a * (uint32_t)K);
-    ps.rsa = rsrc(a_scale + (size_t)row0 * nkb, (uint32_t)rows_a * (uint32_t)nkb * 4u);
-    const int wcol0 = col0 + wn * T::WN;
 
     // One pass per distinct expert present in the window, in increasing id.
     int cur = -1;
@@ -376,11 +393,18 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) ps.acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+      // Step 0's tiles and the b_scale row travel together; the b_scale
+      // row is waited for at once (load_b_scales), which also waits for
+      // step 0.  With 3 stages, step 1 is issued after that wait.
+      if (!a_pre) {
+        ps.stage_a(lds0, 0, wave);
+        ps.stage_scales(sa0, 0, wave, lane);
+      }
+      ps.stage_b(lds0, 0, wave);
       ps.load_b_scales(0, lane);
-      ps.stage_in(lds0, 0, wave);
-      ps.stage_scales(sa0, 0, wave, lane);
+      wait_vmem<0>();
       if constexpr (T::STAGES == 2) {
-        wait_vmem<0>();
+        a_pre = false;
         lds_barrier();
         // K steps two at a time (LDS stage parity), scale chunks of SA_BLK
         // steps alternate between sa0 and sa1.
@@ -393,11 +417,10 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
         }
       } else {
         if (nkb > 1) {
-          ps.stage_in(lds1, 1, wave);
-          wait_vmem<T::VM_TILE>();  // step 0 and the first scale chunk
-        } else {
-          wait_vmem<0>();
+          if (!a_pre) ps.stage_a(lds1, 1, wave);
+          ps.stage_b(lds1, 1, wave);
         }
+        a_pre = false;
         lds_barrier();
         // Six steps per iteration: stage = kb % 3 and scale chunk kb / 3
         // (alternating sa0 / sa1) are then known at compile time.
@@ -427,6 +450,10 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
         }
       }
     }
+    // No pass ran (a window of padding rows only, or a split item past the
+    // window's last expert): the early A loads are still writing the stages;
+    // let them land before the stages change hands or the workgroup ends.
+    if (a_pre) wait_vmem<0>();
   }
 }
 
