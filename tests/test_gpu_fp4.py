@@ -129,3 +129,14 @@ def test_full_size_sampled(name):
     C = run(p, d)
     assert_parity(p, C, rows=rows, what=name)
     assert np.all(np.isfinite(c_to_f64(C)))
+    # Every tile shape accumulates each output over the same K steps with the
+    # same MFMA, so all of them give the same bits: compared on every element,
+    # and each against the oracle on a sample of rows.
+    bits = c_bits(C).copy()
+    del C
+    for tile in FP4_TILES:
+        log(f"{name} full size tile {tile}")
+        Ct = run(p, d, tile_id=tile)
+        assert_parity(p, Ct, rows=rows[::4], what=f"{name}/tile{tile}")
+        assert np.array_equal(c_bits(Ct), bits), (name, tile)
+        del Ct
