@@ -85,13 +85,16 @@ struct LaunchOpts {
 // window run side by side (the window-segment program of the flashinfer#7877
 // page, "Code analysis 2": one CTA per expert run of a 128-row window, used
 // when all of them fit in a single wave of the GPU).  The host cannot read
-// m_indices, so it sizes for the most passes a window can need, min(G, BM);
-// items past a window's last expert end at once.  Automatic mode splits only
-// when every item of the launch runs at once on the device (tiles * split
-// workgroups fit the CUs); then the launch lasts about one pass.
+// m_indices, so a tile gets one item per expert: item r runs expert r's pass
+// if the window holds a row of it and ends at once otherwise.  Knowing its
+// expert from its index, an item can fetch that expert's B before the
+// routing arrives.  Automatic mode splits only when every item of the
+// launch runs at once on the device (tiles * G workgroups fit the CUs);
+// then the launch lasts about one pass.
 inline int split_items(int mode, bool grouped, int G, int BM, long long tiles, int slots) {
+  (void)BM;
   if (!grouped || G < 2 || mode < 0) return 1;
-  const long long s = G < BM ? G : BM;
+  const long long s = G;
   if (tiles * s > 0x7FFFFFFFLL) return 1;
   if (mode == 0 && tiles * s > slots) return 1;
   return (int)s;

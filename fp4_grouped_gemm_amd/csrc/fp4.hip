@@ -323,7 +323,7 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const int tile = split > 1 ? item / split : item;
-    const int run_sel = split > 1 ? item % split : 0;  // which pass this item runs
+    const int run_sel = split > 1 ? item % split : 0;  // split mode: this item's expert
     int window, ntile;
     plan_tile(plan_bits, heavy, tile, num_windows, num_ntiles, group_w, window, ntile);
     const int row0 = window * T::BM;
@@ -357,19 +357,27 @@ __global__ __launch_bounds__(T::THREADS) void fp4_gemm_kernel(
     ps.rsa = rsrc(a_scale + (size_t)row0 * Ks, rows_a * Ks);
     const int wcol0 = col0 + wn * T::WN;
 
+    // One pass per distinct expert present in the window, in increasing id;
+    // in split mode, one pass for expert run_sel if the window holds a row
+    // of it.  Every wave takes the same passes.
     int cur = -1;
     for (int pass = 0;; ++pass) {
-      int e = INT_MAX;
-      for (int r = lane; r < T::BM; r += 64) {
-        const int v = ids[r];
-        if (v > cur && v < e) e = v;
-      }
-      e = __builtin_amdgcn_readfirstlane(wave_min(e));  // same in every wave
-      if (e == INT_MAX) break;
-      cur = e;
-      if (split > 1 && pass != run_sel) {
-        if (pass > run_sel) break;
-        continue;
+      int e;
+      if (split > 1) {
+        if (pass > 0) break;
+        e = run_sel;
+        bool has = false;
+        for (int r = lane; r < T::BM; r += 64) has |= ids[r] == e;
+        if (__ballot(has) == 0) break;
+      } else {
+        e = INT_MAX;
+        for (int r = lane; r < T::BM; r += 64) {
+          const int v = ids[r];
+          if (v > cur && v < e) e = v;
+        }
+        e = __builtin_amdgcn_readfirstlane(wave_min(e));
+        if (e == INT_MAX) break;
+        cur = e;
       }
 
 #pragma unroll

@@ -167,9 +167,19 @@ struct Pass {
   // waits for this load here and nowhere else: its own waits do not see the
   // staging loads (inline assembly), and a wait for this load placed inside
   // the K loop would drain them.
-  __device__ __forceinline__ void load_b_scales(int kb, int lane) {
+  __device__ __forceinline__ void issue_b_scales(int kb, int lane) {
     bs_vec = kb + lane < nkb ? bs_row[kb + lane] : 0.f;
+  }
+  __device__ __forceinline__ void load_b_scales(int kb, int lane) {
+    issue_b_scales(kb, lane);
     asm volatile("" ::"v"(bs_vec));
+  }
+  // B[e]'s rows of this column tile and the b_scale row of this wave's
+  // 128-column block.
+  __device__ __forceinline__ void set_expert(const uint8_t* B, const float* b_scale, int e, int N,
+                                             int col0, int wcol0, int rows_b) {
+    rb = rsrc(B + ((size_t)e * N + col0) * K, (uint32_t)rows_b * K);
+    bs_row = b_scale + ((size_t)e * (N >> 7) + (min(wcol0, N - 1) >> 7)) * nkb;
   }
   __device__ __forceinline__ float b_scale_of(int kb) const {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bs_vec), kb & 63));
@@ -304,7 +314,7 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const int tile = split > 1 ? item / split : item;
-    const int run_sel = split > 1 ? item % split : 0;  // which pass this item runs
+    const int run_sel = split > 1 ? item % split : 0;  // split mode: this item's expert
     int window, ntile;
     plan_tile(plan_bits, heavy, tile, num_windows, num_ntiles, group_w, window, ntile);
     const int row0 = window * T::BM;
@@ -327,13 +337,23 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
     // uses them (rows of other experts are computed and never stored).  The
     // 2-stage 256x256 shape, which holds all 256 VGPRs in its K loop, does
     // not: there the early offsets spill.
-    bool a_pre = false;
+    // In split mode the item's expert is known before the routing is read
+    // (item r of a tile runs expert r), so its B tiles of those steps and its
+    // b_scale row go out now as well.
+    bool a_pre = false, b_pre = false;
     if constexpr (T::STAGES > 2) {
       ps.a_groups = ~0ull;
       ps.stage_a(lds0, 0, wave);
       ps.stage_scales(sa0, 0, wave, lane);
       if (nkb > 1) ps.stage_a(lds1, 1, wave);
       a_pre = true;
+      if (split > 1) {
+        ps.set_expert(B, b_scale, run_sel, N, col0, wcol0, rows_b);
+        ps.stage_b(lds0, 0, wave);
+        ps.issue_b_scales(0, lane);
+        if (nkb > 1) ps.stage_b(lds1, 1, wave);
+        b_pre = true;
+      }
     }
 
     for (int r = tid; r < T::BM; r += T::THREADS) {
@@ -356,21 +376,27 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
         *reinterpret_cast<uint4*>(C + (size_t)(row0 + r) * N + col) = make_uint4(0, 0, 0, 0);
     }
 
-    // One pass per distinct expert present in the window, in increasing id.
+    // One pass per distinct expert present in the window, in increasing id;
+    // in split mode, one pass for expert run_sel if the window holds a row
+    // of it.  Every wave takes the same passes.
     int cur = -1;
     for (int pass = 0;; ++pass) {
-      int e = INT_MAX;
-      for (int r = lane; r < T::BM; r += 64) {
-        const int v = ids[r];
-        if (v > cur && v < e) e = v;
-      }
-      // identical in every wave, so every wave takes the same passes
-      e = __builtin_amdgcn_readfirstlane(wave_min(e));
-      if (e == INT_MAX) break;
-      cur = e;
-      if (split > 1 && pass != run_sel) {
-        if (pass > run_sel) break;
-        continue;
+      int e;
+      if (split > 1) {
+        if (pass > 0) break;
+        e = run_sel;
+        bool has = false;
+        for (int r = lane; r < T::BM; r += 64) has |= ids[r] == e;
+        if (__ballot(has) == 0) break;
+      } else {
+        e = INT_MAX;
+        for (int r = lane; r < T::BM; r += 64) {
+          const int v = ids[r];
+          if (v > cur && v < e) e = v;
+        }
+        e = __builtin_amdgcn_readfirstlane(wave_min(e));
+        if (e == INT_MAX) break;
+        cur = e;
       }
 
       // Which rows this pass needs: A loads of 8-row groups without a row of
@@ -386,23 +412,26 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
         ps.a_groups = __ballot(g);
         ps.active = __ballot(ids[wm * T::WM + lane] == e) != 0;
       }
-      ps.rb = rsrc(B + ((size_t)e * N + col0) * K, (uint32_t)rows_b * (uint32_t)K);
-      ps.bs_row = b_scale + ((size_t)e * (N >> 7) + (min(wcol0, N - 1) >> 7)) * nkb;
+      ps.set_expert(B, b_scale, e, N, col0, wcol0, rows_b);
 #pragma unroll
       for (int i = 0; i < T::TM; ++i)
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) ps.acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-      // Step 0's tiles and the b_scale row travel together; the b_scale
-      // row is waited for at once (load_b_scales), which also waits for
-      // step 0.  With 3 stages, step 1 is issued after that wait.
+      // Step 0's tiles and the b_scale row travel together (unless issued
+      // early); the b_scale row is waited for at once (load_b_scales), which
+      // also waits for step 0.  With 3 stages, step 1 is issued after that
+      // wait.
       if (!a_pre) {
         ps.stage_a(lds0, 0, wave);
         ps.stage_scales(sa0, 0, wave, lane);
       }
-      ps.stage_b(lds0, 0, wave);
-      ps.load_b_scales(0, lane);
+      if (!b_pre) {
+        ps.stage_b(lds0, 0, wave);
+        ps.load_b_scales(0, lane);
+      }
       wait_vmem<0>();
+      asm volatile("" ::"v"(ps.bs_vec));
       if constexpr (T::STAGES == 2) {
         a_pre = false;
         lds_barrier();
@@ -418,9 +447,9 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
       } else {
         if (nkb > 1) {
           if (!a_pre) ps.stage_a(lds1, 1, wave);
-          ps.stage_b(lds1, 1, wave);
+          if (!b_pre) ps.stage_b(lds1, 1, wave);
         }
-        a_pre = false;
+        a_pre = b_pre = false;
         lds_barrier();
         // Six steps per iteration: stage = kb % 3 and scale chunk kb / 3
         // (alternating sa0 / sa1) are then known at compile time.
@@ -450,10 +479,11 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
         }
       }
     }
-    // No pass ran (a window of padding rows only, or a split item past the
-    // window's last expert): the early A loads are still writing the stages;
-    // let them land before the stages change hands or the workgroup ends.
-    if (a_pre) wait_vmem<0>();
+    // No pass ran (a window of padding rows only, or a split item whose
+    // expert has no row in the window): the early loads are still writing
+    // the stages; let them land before the stages change hands or the
+    // workgroup ends.
+    if (a_pre || b_pre) wait_vmem<0>();
   }
 }
 
