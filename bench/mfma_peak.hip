@@ -25,6 +25,15 @@
 //     prefill shape streamed through LDS rings of different depth and K
 //     width with direct-to-LDS loads, no compute (loads alone), plus the
 //     same stream with every load an L2 hit.
+//  6. HBM read only: 1 GiB streamed with 16-byte loads, 4 or 8 in flight per
+//     lane, nothing written but one word per thread (the ceiling of kernels
+//     that mostly read, such as the decode GEMM and the quantisers).
+//  7. Launch floor and dependent-load latency: an empty kernel, and one
+//     thread running a chain of n dependent 4-byte loads (scalar or vector)
+//     from a 256 KB table (cache-resident after the first launch) before one
+//     store, each captured
+//     100 times in a HIP graph (and also launched 100 times on a stream),
+//     microseconds per launch; the slope over n is one load round trip.
 //
 // Every launch below is sized on the host: grids are whole multiples of the
 // work each workgroup owns, and every LDS and global index is masked into
@@ -379,6 +388,145 @@ double run_copy(int cus) {
   return 2.0 * bytes * reps / (ms * 1e-3) / 1e9;  // GB/s, read + write
 }
 
+// ------------------------------------------------------- 6. HBM read only
+// n is a multiple of U x the grid's thread count (checked by the caller).
+template <int U>
+__global__ __launch_bounds__(256) void read16(const i32x4* __restrict__ src, int* __restrict__ out,
+                                              long long n) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  i32x4 x = {0, 0, 0, 0};
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += U * stride) {
+    i32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u];
+  }
+  out[(long long)blockIdx.x * blockDim.x + threadIdx.x] = x[0] ^ x[1] ^ x[2] ^ x[3];
+}
+
+template <int U>
+double run_read(int cus, int wg_per_cu) {
+  const long long bytes = 1ll << 30, n = bytes / 16;
+  const int grid = cus * wg_per_cu;
+  if (n % ((long long)U * grid * 256)) {
+    std::fprintf(stderr, "read size not a multiple of the grid's work\n");
+    std::exit(1);
+  }
+  i32x4* a;
+  int* out;
+  CHECK(hipMalloc(&a, bytes));
+  CHECK(hipMalloc(&out, sizeof(int) * grid * 256));
+  CHECK(hipMemset(a, 1, bytes));
+  for (int i = 0; i < 3; ++i) hipLaunchKernelGGL(read16<U>, dim3(grid), dim3(256), 0, 0, a, out, n);
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  const int reps = 10;
+  CHECK(hipEventRecord(e0, 0));
+  for (int i = 0; i < reps; ++i) hipLaunchKernelGGL(read16<U>, dim3(grid), dim3(256), 0, 0, a, out, n);
+  CHECK(hipEventRecord(e1, 0));
+  CHECK(hipEventSynchronize(e1));
+  float ms = 0.f;
+  CHECK(hipEventElapsedTime(&ms, e0, e1));
+  CHECK(hipFree(a));
+  CHECK(hipFree(out));
+  CHECK(hipEventDestroy(e0));
+  CHECK(hipEventDestroy(e1));
+  return (double)bytes * reps / (ms * 1e-3) / 1e9;  // GB/s read
+}
+
+// ---------------------------------------- 7. launch floor, load round trip
+__global__ void empty_kernel() {}
+
+// One thread: n dependent loads (each index comes from the previous load,
+// masked into the table), then one store.  VEC keeps the index in a vector
+// register, so the loads take the vector memory path (L1, L2) that the
+// GEMMs' loads take; otherwise the compiler, seeing a uniform index, issues
+// scalar loads through the scalar cache.
+template <bool VEC>
+__global__ void chase(const unsigned* __restrict__ table, unsigned mask, int n,
+                      unsigned* __restrict__ out) {
+  unsigned i = blockIdx.x;
+  for (int k = 0; k < n; ++k) {
+    if (VEC) asm volatile("" : "+v"(i));
+    i = table[i & mask];
+  }
+  out[blockIdx.x] = i;
+}
+
+// Microseconds per launch of `launch` (which enqueues one kernel on the
+// given stream): 100 launches captured in a HIP graph (best of 3 replays),
+// and 100 plain launches on the same stream.
+template <class F>
+void launch_us(F launch, double& graph_us, double& stream_us) {
+  const int reps = 100;
+  hipStream_t s;
+  CHECK(hipStreamCreate(&s));
+  hipGraph_t g;
+  hipGraphExec_t ge;
+  CHECK(hipStreamBeginCapture(s, hipStreamCaptureModeGlobal));
+  for (int i = 0; i < reps; ++i) launch(s);
+  CHECK(hipStreamEndCapture(s, &g));
+  CHECK(hipGraphInstantiate(&ge, g, nullptr, nullptr, 0));
+  CHECK(hipGraphLaunch(ge, s));
+  CHECK(hipStreamSynchronize(s));
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  graph_us = 1e30;
+  for (int r = 0; r < 3; ++r) {
+    CHECK(hipEventRecord(e0, s));
+    CHECK(hipGraphLaunch(ge, s));
+    CHECK(hipEventRecord(e1, s));
+    CHECK(hipEventSynchronize(e1));
+    float ms = 0.f;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    graph_us = std::min(graph_us, (double)ms * 1e3 / reps);
+  }
+  CHECK(hipEventRecord(e0, s));
+  for (int i = 0; i < reps; ++i) launch(s);
+  CHECK(hipEventRecord(e1, s));
+  CHECK(hipEventSynchronize(e1));
+  float ms = 0.f;
+  CHECK(hipEventElapsedTime(&ms, e0, e1));
+  stream_us = ms * 1e3 / reps;
+  CHECK(hipGraphExecDestroy(ge));
+  CHECK(hipGraphDestroy(g));
+  CHECK(hipEventDestroy(e0));
+  CHECK(hipEventDestroy(e1));
+  CHECK(hipStreamDestroy(s));
+}
+
+void run_latency() {
+  const unsigned len = 1u << 16, mask = len - 1;  // 256 KB table
+  std::vector<unsigned> h(len);
+  for (unsigned i = 0; i < len; ++i) h[i] = (i + 16411u) & mask;  // a new cache line every hop
+  unsigned *table, *out;
+  CHECK(hipMalloc(&table, sizeof(unsigned) * len));
+  CHECK(hipMalloc(&out, sizeof(unsigned) * 64));
+  CHECK(hipMemcpy(table, h.data(), sizeof(unsigned) * len, hipMemcpyHostToDevice));
+  std::printf("kernel | us per launch (HIP graph) | us per launch (stream)\n");
+  double gu, su;
+  launch_us([](hipStream_t s) { hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, s); }, gu, su);
+  std::printf("empty, 1 workgroup | %.2f | %.2f\n", gu, su);
+  std::fflush(stdout);
+  for (int vec = 0; vec < 2; ++vec)
+    for (int n : {0, 1, 2, 4, 8, 16, 32}) {
+      launch_us(
+          [=](hipStream_t s) {
+            hipLaunchKernelGGL(vec ? chase<true> : chase<false>, dim3(1), dim3(1), 0, s,
+                               (const unsigned*)table, mask, n, out);
+          },
+          gu, su);
+      std::printf("%d dependent %s loads + 1 store | %.2f | %.2f\n", n, vec ? "vector" : "scalar",
+                  gu, su);
+      std::fflush(stdout);
+    }
+  CHECK(hipFree(table));
+  CHECK(hipFree(out));
+}
+
 // --------------------------------------------- 5. L2 -> LDS tile staging
 // Loads only: every workgroup (8 waves, one per CU) streams the A and B
 // rows of 256 x 256 output tiles of the grouped FP8 MoE prefill shape (A
@@ -517,6 +665,15 @@ int main() {
   std::printf("\n## 4. HBM copy, 1 GiB, 16-byte loads/stores\n");
   std::printf("GB/s (read + write) | %.0f\n", run_copy(cus));
   std::fflush(stdout);
+
+  std::printf("\n## 6. HBM read only, 1 GiB, 16-byte loads\n");
+  std::printf("loads in flight per lane | workgroups (256 threads) per CU | GB/s\n");
+  std::printf("4 | 8 | %.0f\n", run_read<4>(cus, 8));
+  std::printf("8 | 8 | %.0f\n", run_read<8>(cus, 8));
+  std::printf("4 | 16 | %.0f\n", run_read<4>(cus, 16));
+  std::fflush(stdout);
+  std::printf("\n## 7. Launch floor and dependent-load round trip (100 launches)\n");
+  run_latency();
 
   std::printf("\n## 5. L2 -> LDS staging of 256x256 tiles (loads only), grouped FP8 MoE prefill shape\n");
   std::printf("(2 tiles per CU x 56 K steps of 128; 64 KB per step per CU)\n");
