@@ -94,5 +94,32 @@ FGG_HD uint32_t w4a16_act_voff(uint32_t row, int lc, int gc, int K) {
   return gc * 256 + lc * 8 < K ? row * (uint32_t)K * 2u + (uint32_t)(gc * 512 + lc * 16) : kSkip;
 }
 
+// Weights (packed E2M1 rows of Kp = K / 2 bytes, one row per output
+// column): a staged group holds a wave's 32 weight rows x 128 bytes (256
+// codes each), row w (0..31) at 128 w, its 16-byte chunk c (0..7) at
+// physical chunk c ^ w4a16_wkey(w).  A fragment read gives lane l row
+// 16 b + l % 16 and chunk 2 (l / 16) + h; under the 16-lane read grouping
+// the key (row bit 1 as key bit 0, row bit 2 as key bit 2) gives each
+// cycle's lanes 16 distinct bank groups.
+FGG_HD int w4a16_wkey(int row) { return ((row >> 1) & 1) | (((row >> 2) & 1) << 2); }
+FGG_HD int w4a16_w_lds_off(int row, int chunk) {
+  return row * 128 + ((chunk ^ w4a16_wkey(row)) << 4);
+}
+// Chunk lc (16 bytes, 32 codes) of group g of weight row `row`; chunks at
+// or past the row's end (the half-full last group when K is an odd
+// multiple of 128) read zeros.
+FGG_HD uint32_t w4a16_w_voff(uint32_t row, int lc, int g, uint32_t Kp) {
+  const uint32_t b = (uint32_t)g * 128u + (uint32_t)lc * 16u;
+  return b < Kp ? row * Kp + b : kSkip;
+}
+// The 16 scale bytes of group g of weight row `row` (rows of Ks = K / 16
+// bytes), the whole offset in the VGPR: the half-full last group's second
+// half reads the next row's first codes, or zeros past the buffer's end
+// (the range check goes dword by dword); the kernel zeroes the scales of
+// the lanes past K.
+FGG_HD uint32_t w4a16_s_voff(uint32_t row, int g, uint32_t Ks) {
+  return row * Ks + (uint32_t)g * 16u;
+}
+
 }  // namespace off
 }  // namespace fgg

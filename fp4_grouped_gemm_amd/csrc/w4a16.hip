@@ -8,24 +8,25 @@
 //
 // Design: with a few rows per expert the weights dominate the traffic (each
 // weight byte is used by those few rows only), so the kernel streams B once
-// from HBM with many loads in flight and keeps the dequantisation VALU work
-// of one wave overlapped with the load waits of the others.
+// from HBM with direct-to-LDS loads of whole 128-byte lines, which stream
+// faster than loads into registers, and overlaps the dequantisation of one
+// group with the loads of the next.
 //  * One workgroup (4 waves) per (expert, 128-column block); wave w owns
 //    columns 32 w .. 32 w + 31 (two MFMA column blocks) over all of K, so
 //    no partial sums cross waves.  Wave 0 first compacts the rows routed to
 //    the expert into LDS (ballot + popcount, in row order; expert 0's
 //    workgroups also zero the padding rows found); a workgroup whose expert
 //    has no rows stops there and never reads that expert's weights.
-//  * Rows run 32 at a time (two MFMA row blocks sharing each dequantised
-//    weight fragment).  Their activations, 32 rows x 256 K per group, go
-//    through a 4-stage LDS ring with direct-to-LDS loads (no registers),
-//    shared by the four waves; 16-byte chunks are XOR-swizzled by row so a
-//    fragment read hits 16 distinct chunk positions.
-//  * Weights stream through a 4-slot register ring, 3 groups ahead: per
-//    group a lane loads 32 packed bytes (64 weights of one column) and their
-//    four E4M3 scale codes per column block.  Every group issues the same
-//    loads (past the last group they reload it and add exact zeros through
-//    a zero scale), so one explicit count waits for the oldest group.
+//  * K runs in groups of 256.  Rows run 32 at a time (two MFMA row blocks
+//    sharing each dequantised weight fragment).  Their activations, 32 rows
+//    x 256 K per group, go through a 2-stage LDS ring shared by the four
+//    waves; each wave's weights, 32 rows of 128 packed bytes plus their 16
+//    scale bytes per group, through a 2-slot LDS ring of its own.  Both are
+//    filled by direct-to-LDS loads (no registers): a weight load moves 8
+//    whole lines.  16-byte chunks are XOR-swizzled by row so that fragment
+//    reads hit 16 distinct bank groups per cycle.  Group i + 1 is issued as
+//    group i starts, so one group's loads are in flight while the previous
+//    one is computed (about 70 KB per CU with two workgroups per CU).
 //  * Weights are dequantised exactly to BF16 in registers (q * s has at most
 //    6 significant bits and lies in [2^-10, 2688]): the E2M1 pair convert with
 //    scale 1.0, an FP32 multiply by the block scale, and the upper halves of
@@ -55,31 +56,16 @@ constexpr int kGroup = 256;            // K per group: 8 MFMAs of K = 32
 constexpr int kWords = kGroup / 32;    // 32-bit words of packed weights per lane per group
 constexpr int kChunks = kGroup / 8;    // 16-byte activation chunks per row per group
 constexpr int kScan = 1024;            // m_indices entries compacted per scan
-constexpr int kAStages = 4;            // LDS ring of activation groups
-constexpr int kBSlots = 4;             // register ring of weight groups
-constexpr int kAhead = kBSlots - 1;    // weight groups issued ahead
+constexpr int kStages = 2;             // depth of both LDS rings
 constexpr int kAStage = kRows * kGroup * 2;         // bytes per activation stage
 constexpr int kADma = kAStage / 16 / kThreads;      // 16-byte loads per thread
+constexpr int kWRows = 16 * kCB;                    // weight rows (columns) per wave
+constexpr int kWCode = kWRows * kGroup / 2;         // packed bytes per wave per group
+constexpr int kWDma = kWCode / 1024;                // whole-line loads per wave per group
+constexpr int kWSlot = kWCode + 1024;               // + the scale bytes' load (64 lanes x 16 B)
 static_assert(kCols == 2 * 64, "a zero row is one 4-byte store per lane");
-static_assert(kBSlots % kAStages == 0, "an unrolled block of kBSlots groups starts at stage 0");
 static_assert(kADma * 16 * kThreads == kAStage, "activation staging split");
-// Loads per group per wave: activation DMAs, then per column block the
-// weight bytes (16 bytes per load) and the scale codes.
-constexpr int kLoadsPerGroup = kADma + kCB * (kWords / 4 + 1);
-// Step i issues the activations of group i + kAStages - 1, then the weights
-// of group i + kAhead.  So group i's weights go out kLead steps before its
-// activations (or right after them, kLead = 0), and when step i waits, the
-// later of the two is followed by the weights of its own step (kLead > 0)
-// and by the kAStages - 2 steps in between.
-constexpr int kLead = kAhead - kAStages + 1;
-static_assert(kLead >= 0, "weights must not trail their activations");
-constexpr int kWaitAfter =
-    (kLead > 0 ? kCB * (kWords / 4 + 1) : 0) + (kAStages - 2) * kLoadsPerGroup;
-
-struct Weights {
-  i32x4 b[kCB][kWords / 4];  // 64 E2M1 codes of column c at k0 + 64 q
-  uint32_t s[kCB];           // their four E4M3 scale codes
-};
+static_assert(kWRows * 16 <= 1024, "a wave's scale bytes fit one load");
 
 // The two codes of byte H times s, as a BF16 pair.  q * s has at most 6
 // significant bits, so its FP32 value carries no bits below the top 16 and
@@ -116,63 +102,65 @@ static_assert(kChunks == kRows && kGroup * 2 == 512, "the chunk swizzle uses the
 static_assert(kGroup == 256, "off::w4a16_act_voff assumes groups of 256 values");
 
 struct Ctx {
-  const uint8_t* bcol[kCB];   // weight row of this lane's column, per column block
-  const uint8_t* scol[kCB];   // its scale codes
   i32x4 ra;                   // activation buffer resource (whole A)
+  i32x4 rw, rs;               // this wave's 32 weight rows and their scale rows
   uint32_t a_row[kADma];      // this lane's activation chunks: their rows
-  int a_lc[kADma];            // and logical chunks (8 values each) within a group
+  int a_lc[kADma];            // and logical chunks (8 values) within a group
   uint32_t lds_a[kADma];      // their LDS destinations (stage 0)
+  int w_lc[kWDma];            // this lane's weight chunk per whole-line load
+  uint32_t Kp, Ks;
   int ngroups;
   int K;
   int q;
 };
 
-// Issue group g's activation chunks into LDS stage g % kAStages (group index
-// clamped to the last one past the end).  The whole offset is a VGPR offset,
-// which the buffer range check sees; a chunk at or past K (the half-full
-// last group when K is an odd multiple of 128) loads zeros from past the
-// buffer end instead of the next row's values, so no value outside the
-// row's K ever meets a weight (0 x Inf would be NaN).
-__device__ __forceinline__ void load_a(const Ctx& c, uint8_t* ring, int g) {
-  const int gc = min(g, c.ngroups - 1);
-  const uint32_t st = (uint32_t)((g % kAStages) * kAStage);
+// Issue group g's activation chunks into LDS stage g % kStages.  The whole
+// offset is a VGPR offset, which the buffer range check sees; a chunk at or
+// past K (the half-full last group when K is an odd multiple of 128) loads
+// zeros from past the buffer end instead of the next row's values, so no
+// value outside the row's K ever meets a weight (0 x Inf would be NaN).
+__device__ __forceinline__ void load_a(const Ctx& c, int g) {
+  const uint32_t st = (uint32_t)((g % kStages) * kAStage);
 #pragma unroll
   for (int u = 0; u < kADma; ++u)
-    dma16(c.ra, c.lds_a[u] + st, off::w4a16_act_voff(c.a_row[u], c.a_lc[u], gc, c.K), 0);
-  (void)ring;
+    dma16(c.ra, c.lds_a[u] + st, off::w4a16_act_voff(c.a_row[u], c.a_lc[u], g, c.K), 0);
 }
 
-// Group g's weights of this lane: K = k0 + 64 q .. + 63.  When K is an odd
-// multiple of 128 the last group is half full; lanes past K load the
-// group's first valid piece instead (never past the row) and are zeroed by
-// lane_valid.
-__device__ __forceinline__ void load_b(const Ctx& c, Weights& w, int g) {
-  const int k0 = min(g, c.ngroups - 1) * kGroup;
-  const int kq = k0 + 64 * c.q < c.K ? k0 + 64 * c.q : k0;
+// Issue group g's weights of this wave into its slot `slot`: load j moves
+// rows 8 j .. 8 j + 7, lane l fetching 16 bytes of row 8 j + l / 8 into
+// physical chunk l % 8; then the rows' 16 scale bytes, lanes 0..31 one row
+// each (the other lanes load zeros into the slot's spare half).
+__device__ __forceinline__ void load_w(const Ctx& c, uint32_t slot, int g, int lane) {
 #pragma unroll
-  for (int b = 0; b < kCB; ++b) {
-#pragma unroll
-    for (int h = 0; h < kWords / 4; ++h)
-      w.b[b][h] = *reinterpret_cast<const i32x4*>(c.bcol[b] + kq / 2 + 16 * h);
-    w.s[b] = *reinterpret_cast<const uint32_t*>(c.scol[b] + kq / 16);
-  }
+  for (int j = 0; j < kWDma; ++j)
+    dma16(c.rw, slot + 1024u * j, off::w4a16_w_voff((uint32_t)(8 * j + lane / 8), c.w_lc[j], g, c.Kp), 0);
+  dma16(c.rs, slot + kWCode, lane < kWRows ? off::w4a16_s_voff((uint32_t)lane, g, c.Ks) : kSkip, 0);
 }
 
 __device__ __forceinline__ bool lane_valid(const Ctx& c, int g) {
-  return g < c.ngroups && g * kGroup + 64 * c.q < c.K;
+  return g * kGroup + 64 * c.q < c.K;
 }
 
-// MFMAs of one group: activations from LDS stage `a`, weights from `w`;
-// RB row blocks (the second is skipped when the chunk has at most 16 rows).
-// Each activation fragment is read once per k slice and serves both column
+// MFMAs of one group: activations from LDS stage `a`, this wave's weights
+// from its slot `w`; RB row blocks (the second is skipped when the chunk has
+// at most 16 rows).  Lane (c, q) takes the 64 codes k0 + 64 q .. + 63 of
+// weight row 16 b + c (chunks 2 q and 2 q + 1) and their four scale codes;
+// each activation fragment is read once per k slice and serves both column
 // blocks.
 template <int RB>
-__device__ __forceinline__ void mma_group(const uint8_t* a, const Weights& w, bool valid, int lane,
+__device__ __forceinline__ void mma_group(const uint8_t* a, const uint8_t* w, bool valid, int lane,
                                           f32x4 acc[kRB][kCB]) {
   const int r = lane & 15, q = lane >> 4;
+  i32x4 wb[kCB][2];
   uint32_t sc[kCB];
 #pragma unroll
-  for (int b = 0; b < kCB; ++b) sc[b] = valid ? w.s[b] : 0u;  // code 0 = scale 0: exact zeros
+  for (int b = 0; b < kCB; ++b) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      wb[b][h] = *reinterpret_cast<const i32x4*>(w + off::w4a16_w_lds_off(16 * b + r, 2 * q + h));
+    const uint32_t s = *reinterpret_cast<const uint32_t*>(w + kWCode + (16 * b + r) * 16 + 4 * q);
+    sc[b] = valid ? s : 0u;  // code 0 = scale 0: exact zeros past K
+  }
 #pragma unroll
   for (int t = 0; t < kWords; ++t) {
     // k0 + 64 q + 8 t .. + 8: chunk 8 q + t of the lane's activation rows and
@@ -184,7 +172,7 @@ __device__ __forceinline__ void mma_group(const uint8_t* a, const Weights& w, bo
 #pragma unroll
     for (int b = 0; b < kCB; ++b) {
       const float s = __builtin_amdgcn_cvt_f32_fp8((int)((sc[b] >> (8 * (t / 2))) & 0xFFu), 0);
-      const bf16x8 bf = dequant8((uint32_t)w.b[b][t / 4][t % 4], s);
+      const bf16x8 bf = dequant8((uint32_t)wb[b][t / 4][t % 4], s);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
         acc[rb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, af[rb], acc[rb][b], 0, 0, 0);
@@ -192,39 +180,38 @@ __device__ __forceinline__ void mma_group(const uint8_t* a, const Weights& w, bo
   }
 }
 
-// One group i = g0 + I of the ring: wait until group i's activations and
-// weights have landed, publish the stage, refill the rings (activations of
-// group i + kAStages - 1 into the stage group i - 1 used, weights of group
-// i + kAhead into the slot group i - 1 used), then compute group i.
-template <int RB, int I>
-__device__ __forceinline__ void group_step(const Ctx& c, uint8_t* ring, Weights (&w)[kBSlots],
-                                           int g0, int lane, f32x4 acc[kRB][kCB]) {
-  const int i = g0 + I;
-  wait_vmem<kWaitAfter>();
-  lds_barrier();
-  load_a(c, ring, i + kAStages - 1);
-  load_b(c, w[(I + kAhead) % kBSlots], i + kAhead);
-  __builtin_amdgcn_sched_barrier(0);
-  mma_group<RB>(ring + (I % kAStages) * kAStage, w[I % kBSlots], lane_valid(c, i), lane, acc);
-  __builtin_amdgcn_sched_barrier(0);
+// The K loop of one chunk of rows: group 0 was issued by the caller; each
+// group waits for its loads (this wave's; the barrier then publishes every
+// wave's activation chunks), issues the next group into the other stage and
+// slot (their readers finished with the previous group before the
+// barrier), then computes.
+template <int RB>
+__device__ __forceinline__ void k_loop(const Ctx& c, uint8_t* ring, uint8_t* wslots, int wave,
+                                       int lane, f32x4 acc[kRB][kCB]) {
+  const uint32_t wbase = lds_addr(wslots);
+  for (int i = 0; i < c.ngroups; ++i) {
+    wait_vmem<0>();
+    lds_barrier();
+    if (i + 1 < c.ngroups) {
+      load_a(c, i + 1);
+      load_w(c, wbase + (uint32_t)(((i + 1) % kStages) * kWSlot), i + 1, lane);
+    }
+    mma_group<RB>(ring + (i % kStages) * kAStage, wslots + (i % kStages) * kWSlot,
+                  lane_valid(c, i), lane, acc);
+  }
+  (void)wave;
 }
 
-template <int RB, int... I>
-__device__ __forceinline__ void group_steps(const Ctx& c, uint8_t* ring, Weights (&w)[kBSlots],
-                                            int g0, int lane, f32x4 acc[kRB][kCB],
-                                            std::integer_sequence<int, I...>) {
-  (group_step<RB, I>(c, ring, w, g0, lane, acc), ...);
-}
-
-// Two waves per SIMD at least (one wave's dequantisation overlaps another's
-// load waits): at most 256 registers per lane.
+// Two workgroups per CU (76 KB of LDS each): two waves per SIMD, at most
+// 256 registers per lane.
 __global__ __launch_bounds__(kThreads, 2) void w4a16_kernel(const uint16_t* __restrict__ A,
                                                          const uint8_t* __restrict__ B,
                                                          const uint8_t* __restrict__ b_scale,
                                                          const int32_t* __restrict__ m_indices,
                                                          float gb, uint16_t* __restrict__ C,
                                                          int M, int N, int K, int G) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kAStages * kAStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * kAStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t wring[kWaves][kStages * kWSlot];
   __shared__ int rows[kScan];
   __shared__ int nrows;
 
@@ -240,13 +227,16 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_kernel(const uint16_t* __re
   c.q = lane >> 4;
   c.ngroups = (K + kGroup - 1) / kGroup;
   c.K = K;
+  c.Kp = Kp;
+  c.Ks = Ks;
   c.ra = rsrc(A, (uint32_t)((size_t)M * K * 2));
+  // this wave's weight rows (output columns n0 + 32 w ..) of expert g
+  const size_t wrow0 = (size_t)g * N + n0 + kWRows * wave;
+  c.rw = rsrc(B + wrow0 * Kp, (uint32_t)kWRows * Kp);
+  c.rs = rsrc(b_scale + wrow0 * Ks, (uint32_t)kWRows * Ks);
 #pragma unroll
-  for (int b = 0; b < kCB; ++b) {
-    const size_t col = (size_t)g * N + n0 + 32 * wave + 16 * b + (lane & 15);
-    c.bcol[b] = B + col * Kp;
-    c.scol[b] = b_scale + col * Ks;
-  }
+  for (int j = 0; j < kWDma; ++j) c.w_lc[j] = (lane % 8) ^ off::w4a16_wkey(8 * j + lane / 8);
+  uint8_t* wslots = wring[wave];
 
   for (int scan0 = 0; scan0 < M; scan0 += kScan) {
     // Compact the rows of this expert among m_indices[scan0, scan0 + kScan).
@@ -294,25 +284,13 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_kernel(const uint16_t* __re
 #pragma unroll
         for (int b = 0; b < kCB; ++b) acc[rb][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-      // Prologue in the steady-state order: the weights of the first kLead
-      // groups, then (activations j, weights j + kLead).
-      Weights w[kBSlots];
-#pragma unroll
-      for (int j = 0; j < kLead; ++j) load_b(c, w[j], j);
-#pragma unroll
-      for (int j = 0; j < kAStages - 1; ++j) {
-        load_a(c, ring, j);
-        load_b(c, w[j + kLead], j + kLead);
-      }
-      if (count - c0 > 16) {
-        for (int g0 = 0; g0 < c.ngroups; g0 += kBSlots)
-          group_steps<2>(c, ring, w, g0, lane, acc, std::make_integer_sequence<int, kBSlots>{});
-      } else {
-        for (int g0 = 0; g0 < c.ngroups; g0 += kBSlots)
-          group_steps<1>(c, ring, w, g0, lane, acc, std::make_integer_sequence<int, kBSlots>{});
-      }
-      wait_vmem<0>();  // no load into the ring may outlive the chunk
-      lds_barrier();
+      load_a(c, 0);
+      load_w(c, lds_addr(wslots), 0, lane);
+      if (count - c0 > 16)
+        k_loop<2>(c, ring, wslots, wave, lane, acc);
+      else
+        k_loop<1>(c, ring, wslots, wave, lane, acc);
+      lds_barrier();  // every wave is done with the rings before the next chunk
 
       // Lane holds C[row c0 + 16 rb + l % 16][n0 + 32 w + 16 b + 4 (l / 16) + t].
 #pragma unroll

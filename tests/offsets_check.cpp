@@ -4,7 +4,7 @@
 // short and long K), and every access whose VGPR offset passes the range
 // check must lie inside the row it is meant for and inside the buffer; an
 // access that fails the check reads zeros and touches nothing.  The FP8
-// tiles' and the W4A16 activation stage's LDS layouts are checked too: the
+// tiles' and the W4A16 activation and weight stages' LDS layouts are checked too: the
 // loads put every chunk where the fragment reads look for it, and those
 // reads are free of bank conflicts.
 //
@@ -145,6 +145,52 @@ static void check_w4a16_layout() {
       }
 }
 
+// W4A16 weight staging: a wave's rows of Kp packed bytes (Ks scale bytes),
+// every whole-line load and scale load of every group.  Used code bytes
+// stay inside their row; chunks past the row's end read zeros.  Scale
+// loads must keep their used bytes (those of k below K) inside the row;
+// the rest may run into the next row or, past the buffer's end, read zeros.
+static void check_w4a16_weights(int rows, int K) {
+  const uint32_t Kp = K / 2, Ks = K / 16;
+  const int ngroups = (K + 255) / 256;
+  const uint64_t crec = (uint64_t)rows * Kp, srec = (uint64_t)rows * Ks;
+  for (int g = 0; g < ngroups; ++g)
+    for (int row = 0; row < rows; ++row) {
+      for (int lc = 0; lc < 8; ++lc)
+        access(w4a16_w_voff((uint32_t)row, lc, g, Kp), 0, 16, crec, (uint64_t)row * Kp,
+               (uint64_t)(row + 1) * Kp, "w4a16 weight codes");
+      const uint64_t used = Ks - 16ull * g < 16 ? Ks - 16ull * g : 16;
+      access(w4a16_s_voff((uint32_t)row, g, Ks), 0, used, srec, (uint64_t)row * Ks,
+             (uint64_t)(row + 1) * Ks, "w4a16 weight scales (used bytes)");
+    }
+}
+
+// Where the whole-line loads put each weight chunk (load j, lane l: row
+// 8 j + l / 8, physical chunk l % 8, logical chunk (l % 8) ^ key) against
+// where the fragment reads look for it, and the reads' banks.
+static void check_w4a16_weight_layout() {
+  for (int j = 0; j < 4; ++j)
+    for (int l = 0; l < 64; ++l) {
+      const int row = 8 * j + l / 8, lc = (l % 8) ^ w4a16_wkey(row);
+      ++layout_checked;
+      if (w4a16_w_lds_off(row, lc) != 1024 * j + 16 * l && ++bad <= 10)
+        std::printf("W4A16 weight layout: load %d lane %d misplaced\n", j, l);
+    }
+  for (int b = 0; b < 2; ++b)
+    for (int h = 0; h < 2; ++h)
+      for (int cyc = 0; cyc < 4; ++cyc) {
+        int seen = 0;
+        for (int lane = 0; lane < 64; ++lane) {
+          const int par = ((lane >> 2) ^ (lane >> 3) ^ (lane >> 4)) & 1;
+          if (((lane >> 5) & 1) * 2 + par != cyc) continue;
+          seen |= 1 << ((w4a16_w_lds_off(16 * b + (lane & 15), 2 * (lane >> 4) + h) / 16) % 16);
+        }
+        ++layout_checked;
+        if (seen != 0xffff && ++bad <= 10)
+          std::printf("W4A16 weight read b %d h %d cycle %d: bank conflict\n", b, h, cyc);
+      }
+}
+
 static void check_fp4(int BM, int rows, int K) {
   const uint32_t Kp = K / 2, Ks = K / 16;
   const int nks = K / 64;
@@ -201,6 +247,9 @@ int main() {
   for (int K : {128, 384, 640, 1408, 8192})
     for (int M : {1, 2, 33, 1025}) check_w4a16(M, K);
   check_w4a16_layout();
+  for (int K : {128, 384, 640, 1408, 8192})
+    for (int rows : {1, 2, 31, 32}) check_w4a16_weights(rows, K);
+  check_w4a16_weight_layout();
   std::printf("offsets: %lld accesses checked in range, %lld skipped by the range check, %lld LDS "
               "layout and bank checks, %lld failed\n", checked, skipped, layout_checked, bad);
   return bad == 0 ? 0 : 1;
