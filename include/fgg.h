@@ -326,11 +326,11 @@ typedef struct {
   int max_workgroups;  /* > 0: cap the persistent grid (testing / tuning)    */
   int run_split;       /* grouped calls: 0 automatic, < 0 never, > 0 always.
                         * Split mode runs each expert pass of a row window as
-                        * its own workgroup (min(G, tile rows) items per
-                        * tile) instead of one after the other; automatic
-                        * mode uses it when every item runs at once on the
-                        * device (small M: latency).  Results are identical
-                        * either way.                                         */
+                        * its own workgroup (G items per tile, item r running
+                        * expert r if the window holds a row of it) instead
+                        * of one after the other; automatic mode uses it when
+                        * every item runs at once on the device (small M:
+                        * latency).  Results are identical either way.       */
   int run_align;       /* grouped calls: > 0 promises that every expert run
                         * starts at a row index that is a multiple of
                         * run_align (MoE alignment padding); the ranker then
