@@ -67,6 +67,9 @@ CASES = {
     "grouped_unsorted": lambda: _grouped(np.random.default_rng(5).integers(-1, 4, 301), G=4),
     "grouped_out_of_range": lambda: _grouped([0, 9, -3, 1] * 50, G=2),
     "grouped_run_of_one": lambda: _grouped([0] * 60 + [1] + [2] * 90, G=3),
+    # more experts than tile rows (split mode: item r runs expert r)
+    "grouped_more_experts_than_rows": lambda: _grouped(
+        np.random.default_rng(12).integers(-1, 300, 400), G=300),
     # K loops of 6, 10, 14 and 12 steps of 64: every exit position of the
     # eight-step unrolled loop and of the four-step scale groups
     "dense_k384": lambda: _dense(130, 256, 384, seed=6),
@@ -95,7 +98,8 @@ def test_grouped_single_expert_equals_dense_bitwise():
 
 
 @pytest.mark.parametrize("case", ["grouped_runs", "grouped_unsorted", "grouped_out_of_range",
-                                  "grouped_run_of_one", "grouped_all_padding", "grouped_k896"])
+                                  "grouped_run_of_one", "grouped_all_padding", "grouped_k896",
+                                  "grouped_more_experts_than_rows"])
 def test_run_split_modes_agree_bitwise(case):
     """Split mode (each expert pass of a window its own workgroup) against
     one workgroup per window: same bits, and within the oracle's tolerance."""

@@ -49,6 +49,9 @@ EDGE = {
     "unsorted_rows": lambda: _prob(np.random.default_rng(4).integers(-1, 5, 333), G=5),
     "out_of_range_ids": lambda: _prob([0, 7, -5, 1, 2, 1 << 30, -1, 0] * 40, G=3),
     "many_experts_one_window": lambda: _prob(np.arange(40) % 20, G=20),
+    # more experts than tile rows: split mode's item r runs expert r, so items
+    # past the tile height must find their rows too
+    "more_experts_than_rows": lambda: _prob(np.random.default_rng(11).integers(-1, 300, 400), G=300),
     "K128_N128": lambda: _prob([0] * 10 + [1] * 10, N=128, K=128),
     "N_not_tile_multiple": lambda: _prob([0] * 100 + [1] * 200, N=384, K=256),
 }
@@ -64,7 +67,8 @@ def test_edge_cases(case, tile):
 
 
 SPLIT_CASES = ["run_of_one", "run_across_windows", "empty_experts", "unsorted_rows",
-               "out_of_range_ids", "many_experts_one_window", "all_padding", "N_not_tile_multiple"]
+               "out_of_range_ids", "many_experts_one_window", "all_padding", "N_not_tile_multiple",
+               "more_experts_than_rows"]
 
 
 @pytest.mark.parametrize("case", SPLIT_CASES + ["p2_m777_g8", "c1_tiny_fp8"])
