@@ -65,6 +65,10 @@ WORKLOADS = {
                               desc="8 NVFP4 problems of different shapes in one launch: "
                                    "multinomial(16384) rows, (N, K) alternately (4096, 7168) and "
                                    "(7168, 2048)"),
+    "p8_problems_fp8": dict(kind="fp8_problems",
+                            desc="8 block-scaled FP8 problems of different shapes in one launch: "
+                                 "multinomial(16384) rows, (N, K) alternately (4096, 7168) and "
+                                 "(7168, 2048)"),
     # Latency shapes of the flashinfer#7877 page's timing table: launch-bound,
     # the interesting figure is ms_per_step.
     "p2_unaligned": dict(kind="fp8", desc="small grouped FP8, G=2, M=65, N=128, K=128"),
@@ -93,6 +97,7 @@ KERNEL_SOURCES = {
     "fp8": ("fp8_grouped.hip", "common.h", "offsets.h"),
     "fp4": ("fp4.hip", "common.h", "offsets.h"),
     "fp4_problems": ("fp4.hip", "common.h", "offsets.h"),
+    "fp8_problems": ("fp8_grouped.hip", "common.h", "offsets.h"),
     "quant_fp8": ("quant.hip", "common.h"),
     "quant_nvfp4": ("quant.hip", "common.h"),
     "quant_nvfp4_static": ("quant.hip", "common.h"),
@@ -536,8 +541,8 @@ def bench_w4a16(args, torch):
 
 
 def bench_problems(args, torch):
-    """A batch of dense NVFP4 problems of different shapes, one
-    fp4_gemm_problems launch per step."""
+    """A batch of dense NVFP4 (fp4_gemm_problems) or block-scaled FP8
+    (fp8_gemm_problems) problems of different shapes, one launch per step."""
     import fp4_grouped_gemm_amd as fgg
     import oracle
     from fp4_grouped_gemm_amd.util import c_to_f64, to_device as to_dev
@@ -551,35 +556,46 @@ def bench_problems(args, torch):
     probs = p["problems"]
     ds = [to_dev(q) for q in probs]
     outs = [torch.empty((q["M"], q["N"]), dtype=torch.bfloat16, device="cuda") for q in probs]
-    batch = [(d["A"], d["B"], d["a_scale"], d["b_scale"], q["alpha"]) for d, q in zip(ds, probs)]
+    fp8 = p["kind"] == "fp8_problems"
+    if fp8:
+        batch = [(d["A"], d["B"][0], d["a_scale"], d["b_scale"][0]) for d in ds]
+        run_batch = fgg.fp8_gemm_problems
+    else:
+        batch = [(d["A"], d["B"], d["a_scale"], d["b_scale"], q["alpha"])
+                 for d, q in zip(ds, probs)]
+        run_batch = fgg.fp4_gemm_problems
     kw = {} if args.tile is None else {"tile_id": args.tile}
     for _ in range(args.warmup):
-        fgg.fp4_gemm_problems(batch, outs, **kw)
-    ms, ms_other = time_modes(torch, lambda: fgg.fp4_gemm_problems(batch, outs, **kw),
+        run_batch(batch, outs, **kw)
+    ms, ms_other = time_modes(torch, lambda: run_batch(batch, outs, **kw),
                               args.steps, args.timing, args.single_timing)
     ms_launch = ms
     flops = sum(2.0 * q["M"] * q["N"] * q["K"] for q in probs)
-    cold = cold_cache_entry(torch, lambda: fgg.fp4_gemm_problems(batch, outs, **kw), args, flops,
+    cold = cold_cache_entry(torch, lambda: run_batch(batch, outs, **kw), args, flops,
                             "TFLOPS", 1e-12)
     tflops = flops / (ms * 1e-3) / 1e12
     tflops_launch = flops / (ms_launch * 1e-3) / 1e12
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "nvfp4_e2m1",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3" if fp8 else "nvfp4_e2m1",
         "data": "synthetic (seeded NumPy; quantised on the host, resident in HBM)",
         "config": {"workload": args.workload, "desc": WORKLOADS[args.workload]["desc"],
                    "problems": [[q["M"], q["N"], q["K"]] for q in probs],
                    "tile": args.tile, "timing": TIMING[args.timing],
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(tflops_launch, 2), "peak": PEAK["fp4"],
-                     "peak_dtype": "fp4", "unit": "TFLOP/s",
-                     "frac": round(tflops_launch / PEAK["fp4"], 4),
-                     "traffic": measured_traffic(args.workload, kernel_source_hash(args.workload)),
-                     "mfma_dtype": "fp16", "frac_of_fp16_peak": round(tflops_launch / PEAK["fp16"], 4),
-                     "us_per_launch": round(ms_launch * 1e3, 2)},
         "kernel_source_sha": kernel_source_hash(args.workload),
     }
+    peak = "fp8" if fp8 else "fp4"
+    out["roofline"] = {"bound": "mfma", "achieved": round(tflops_launch, 2), "peak": PEAK[peak],
+                       "peak_dtype": peak, "unit": "TFLOP/s",
+                       "frac": round(tflops_launch / PEAK[peak], 4),
+                       "traffic": measured_traffic(args.workload, kernel_source_hash(args.workload)),
+                       "mfma_dtype": peak if fp8 else "fp16",
+                       "us_per_launch": round(ms_launch * 1e3, 2)}
+    if not fp8:
+        out["roofline"]["frac_of_fp16_peak"] = round(tflops_launch / PEAK["fp16"], 4)
     out["ms_per_step_" + OTHER[args.timing]] = (None if ms_other is None
                                                    else round(ms_other, 5))
     out["cold_cache"] = cold
@@ -593,8 +609,12 @@ def bench_problems(args, torch):
                 rows = np.arange(c0, min(c0 + 128, q["M"]))
                 if rows.size == 0:
                     continue
-                r = oracle.fp4_gemm(q["A"], q["B"], q["a_scale"], q["b_scale"], q["alpha"],
-                                    rows=rows)
+                if fp8:
+                    r = oracle.grouped_fp8_gemm(q["A"], q["B"], q["a_scale"], q["b_scale"],
+                                                q["m_indices"], rows=rows)
+                else:
+                    r = oracle.fp4_gemm(q["A"], q["B"], q["a_scale"], q["b_scale"], q["alpha"],
+                                        rows=rows)
                 ok &= oracle.check_tolerance(c_to_f64(C)[rows], r)["ok"]
                 fl += 2.0 * rows.size * q["N"] * q["K"]
                 nrows += rows.size
@@ -926,7 +946,7 @@ def main():
         bench_w4a16(args, torch)
         return
 
-    if WORKLOADS[args.workload]["kind"] == "fp4_problems":
+    if WORKLOADS[args.workload]["kind"] in ("fp4_problems", "fp8_problems"):
         bench_problems(args, torch)
         return
 

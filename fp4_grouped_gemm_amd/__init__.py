@@ -19,7 +19,8 @@ import os
 __all__ = [
     "grouped_fp8_gemm", "fp4_gemm", "grouped_fp4_gemm", "quantize_fp8_1x128",
     "quantize_nvfp4", "grouped_fp8_gemm_tune", "fp4_gemm_tune", "grouped_fp4_gemm_tune",
-    "tuned_tile", "tune_clear", "fp4_gemm_problems", "grouped_w4a16_gemm", "rank_tiles",
+    "tuned_tile", "tune_clear", "fp4_gemm_problems", "fp8_gemm_problems", "grouped_w4a16_gemm",
+    "rank_tiles",
     "num_tiles",
     "device_info", "library_path", "load_library", "FP8", "FP4",
 ]
@@ -61,6 +62,12 @@ class _Fp4Problem(ctypes.Structure):
                 ("N", ctypes.c_int), ("K", ctypes.c_int), ("alpha", ctypes.c_float)]
 
 
+class _Fp8Problem(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("a_scale", ctypes.c_void_p),
+                ("b_scale", ctypes.c_void_p), ("C", ctypes.c_void_p), ("M", ctypes.c_int),
+                ("N", ctypes.c_int), ("K", ctypes.c_int)]
+
+
 class _Options(ctypes.Structure):
     _fields_ = [("tile_id", ctypes.c_int), ("max_workgroups", ctypes.c_int),
                 ("run_split", ctypes.c_int), ("run_align", ctypes.c_int)]
@@ -95,6 +102,8 @@ def load_library():
         ("grouped_fp4_gemm_alpha", [P, P, P, P, P, P, P, I, I, I, I, P]),
         ("grouped_fp4_gemm_alpha_ex", [P, P, P, P, P, P, P, I, I, I, I, OPT, P]),
         ("fp4_gemm_problems", [ctypes.POINTER(_Fp4Problem), I, P]),
+        ("fp8_gemm_problems", [ctypes.POINTER(_Fp8Problem), I, P]),
+        ("fp8_gemm_problems_ex", [ctypes.POINTER(_Fp8Problem), I, OPT, P]),
         ("fp4_gemm_problems_ex", [ctypes.POINTER(_Fp4Problem), I, OPT, P]),
         ("grouped_w4a16_gemm", [P, P, P, P, F, P, I, I, I, I, P]),
         ("grouped_fp8_gemm_tune", [P, P, P, P, P, P, I, I, I, I, I, I, REP, OPT, P]),
@@ -376,6 +385,45 @@ def fp4_gemm_problems(problems, outs=None, *, tile_id=None, max_workgroups=0, st
         Cs.append(C)
     with torch.cuda.device(dev):
         _check(load_library().fp4_gemm_problems_ex(arr, len(problems),
+                                                   _opts(tile_id, max_workgroups),
+                                                   _stream_ptr(stream, dev)))
+    return Cs
+
+
+def fp8_gemm_problems(problems, outs=None, *, tile_id=None, max_workgroups=0, stream=None):
+    """A batch of dense block-scaled FP8 GEMMs of different shapes in one
+    launch (C ABI fp8_gemm_problems).  ``problems``: sequence of (A [M, K],
+    B [N, K], a_scale [M, K/128] float32, b_scale [N/128, K/128] float32),
+    A and B holding E4M3FN codes; returns the list of C tensors (bfloat16)."""
+    torch = _torch()
+    if not 1 <= len(problems) <= MAX_PROBLEMS:
+        raise ValueError(f"need 1 to {MAX_PROBLEMS} problems, got {len(problems)}")
+    arr = (_Fp8Problem * len(problems))()
+    Cs, dev = [], None
+    for g, (A, B, a_scale, b_scale) in enumerate(problems):
+        A, B = _bytes(A, "A"), _bytes(B, "B")
+        if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
+            raise ValueError(f"problem {g}: A must be [M, K] and B [N, K]")
+        M, K = A.shape
+        N = B.shape[0]
+        if a_scale.dtype != torch.float32 or b_scale.dtype != torch.float32:
+            raise ValueError(f"problem {g}: a_scale and b_scale must be float32")
+        if tuple(a_scale.shape) != (M, K // 128) or tuple(b_scale.shape) != (N // 128, K // 128):
+            raise ValueError(f"problem {g}: scale shapes must be ({M}, {K // 128}) and "
+                             f"({N // 128}, {K // 128})")
+        d = A.device
+        for t, n in ((B, "B"), (a_scale, "a_scale"), (b_scale, "b_scale")):
+            _dev(t, n, d)
+        if dev is None:
+            dev = d
+        elif d != dev:
+            raise ValueError("all problems must be on one device")
+        C = _out(None if outs is None else outs[g], M, N, d)
+        arr[g] = _Fp8Problem(A.data_ptr(), B.data_ptr(), a_scale.data_ptr(), b_scale.data_ptr(),
+                             C.data_ptr(), M, N, K)
+        Cs.append(C)
+    with torch.cuda.device(dev):
+        _check(load_library().fp8_gemm_problems_ex(arr, len(problems),
                                                    _opts(tile_id, max_workgroups),
                                                    _stream_ptr(stream, dev)))
     return Cs

@@ -193,12 +193,14 @@ int tuned_tile(int kind, int M, int N, int K, int G) {
 // this shape, else the ranker's top choice.
 // Tile config for a problem batch: the ranker's terms summed over the
 // problems (useful over computed elements, busy fraction of the last wave of
-// tiles, per-CU efficiency of the shape).
-int rank_problems(const fgg::Fp4ProblemSet& set, int num_cus) {
+// tiles, per-CU efficiency of the shape).  Set: Fp4ProblemSet or
+// Fp8ProblemSet; tiles: the kind's config table.
+template <class Set>
+int rank_problems(const Set& set, int num_cus, int num_tiles, const fgg::TileCfg& (*tile_of)(int)) {
   int best = 0;
   double best_score = -1.0;
-  for (int i = 0; i < fgg::fp4_num_tiles(); ++i) {
-    const fgg::TileCfg& t = fgg::fp4_tile(i);
+  for (int i = 0; i < num_tiles; ++i) {
+    const fgg::TileCfg& t = tile_of(i);
     double useful = 0.0, computed = 0.0;
     long long tiles = 0;
     for (int g = 0; g < set.count; ++g) {
@@ -554,7 +556,7 @@ fgg_status fp4_gemm_problems_ex(const fgg_fp4_problem* problems, int count,
       return fail(FGG_EINVAL, fn, "tile_id %d out of range [0, %d)", opt->tile_id, fgg::fp4_num_tiles());
     tile = opt->tile_id;
   } else {
-    tile = rank_problems(set, d->num_cus);
+    tile = rank_problems(set, d->num_cus, fgg::fp4_num_tiles(), fgg::fp4_tile);
   }
   return launched(fn, fgg::launch_fp4_problems(set, tile, launch_opts(opt, d),
                                                static_cast<hipStream_t>(stream)));
@@ -562,6 +564,44 @@ fgg_status fp4_gemm_problems_ex(const fgg_fp4_problem* problems, int count,
 
 fgg_status fp4_gemm_problems(const fgg_fp4_problem* problems, int count, void* stream) {
   return fp4_gemm_problems_ex(problems, count, nullptr, stream);
+}
+
+fgg_status fp8_gemm_problems_ex(const fgg_fp8_problem* problems, int count,
+                                const fgg_options* opt, void* stream) {
+  const char* fn = "fp8_gemm_problems";
+  if (!problems) return fail(FGG_EINVAL, fn, "problems is null");
+  if (count < 1 || count > FGG_MAX_PROBLEMS)
+    return fail(FGG_EINVAL, fn, "requires 1 <= count <= %d, got %d", FGG_MAX_PROBLEMS, count);
+  fgg::Fp8ProblemSet set;
+  std::memset(&set, 0, sizeof(set));
+  set.count = count;
+  for (int g = 0; g < count; ++g) {
+    const fgg_fp8_problem& q = problems[g];
+    char where[64];
+    std::snprintf(where, sizeof(where), "%s (problem %d)", fn, g);
+    fgg_status st = check_common(where, q.A, q.B, q.a_scale, q.b_scale, q.C, q.M, q.N, q.K, 1,
+                                 false, nullptr, 4);
+    if (st != FGG_OK) return st;
+    set.p[g] = fgg::Fp8Problem{static_cast<const uint8_t*>(q.A), static_cast<const uint8_t*>(q.B),
+                               q.a_scale, q.b_scale, static_cast<uint16_t*>(q.C), q.M, q.N, q.K};
+  }
+  fgg_status st;
+  const DeviceFacts* d = current_device(fn, &st);
+  if (!d) return st;
+  int tile = -1;
+  if (opt && opt->tile_id >= 0) {
+    if (opt->tile_id >= fgg::fp8_num_tiles())
+      return fail(FGG_EINVAL, fn, "tile_id %d out of range [0, %d)", opt->tile_id, fgg::fp8_num_tiles());
+    tile = opt->tile_id;
+  } else {
+    tile = rank_problems(set, d->num_cus, fgg::fp8_num_tiles(), fgg::fp8_tile);
+  }
+  return launched(fn, fgg::launch_fp8_problems(set, tile, launch_opts(opt, d),
+                                               static_cast<hipStream_t>(stream)));
+}
+
+fgg_status fp8_gemm_problems(const fgg_fp8_problem* problems, int count, void* stream) {
+  return fp8_gemm_problems_ex(problems, count, nullptr, stream);
 }
 
 fgg_status grouped_w4a16_gemm(const void* A, const void* B, const void* b_scale,

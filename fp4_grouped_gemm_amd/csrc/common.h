@@ -56,6 +56,21 @@ struct Fp4ProblemSet {
   int count;
 };
 
+// A batch of dense block-scaled FP8 problems, passed by value likewise.
+struct Fp8Problem {
+  const uint8_t* A;        // [M, K] E4M3FN
+  const uint8_t* B;        // [N, K] E4M3FN
+  const float* a_scale;    // [M, K/128]
+  const float* b_scale;    // [N/128, K/128]
+  uint16_t* C;             // [M, N]
+  int M, N, K;
+};
+struct Fp8ProblemSet {
+  Fp8Problem p[kMaxProblems];
+  int tile_start[kMaxProblems + 1];  // filled by the launcher
+  int count;
+};
+
 // Number of compiled configs and their descriptions.
 int fp8_num_tiles();
 const TileCfg& fp8_tile(int id);
@@ -104,6 +119,8 @@ inline int split_items(int mode, bool grouped, int G, int BM, long long tiles, i
 hipError_t launch_fp8(const Fp8Args& a, int tile_id, const LaunchOpts& o, hipStream_t s);
 hipError_t launch_fp4(const Fp4Args& a, int tile_id, const LaunchOpts& o, hipStream_t s);
 hipError_t launch_fp4_problems(const Fp4ProblemSet& set, int tile_id, const LaunchOpts& o,
+                               hipStream_t s);
+hipError_t launch_fp8_problems(const Fp8ProblemSet& set, int tile_id, const LaunchOpts& o,
                                hipStream_t s);
 hipError_t launch_w4a16(const W4A16Args& a, hipStream_t s);
 // rows (may be null): output row r quantises input row rows[r] of X's T

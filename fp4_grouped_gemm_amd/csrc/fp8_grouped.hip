@@ -34,6 +34,7 @@
 #include "common.h"
 #include "offsets.h"
 
+#include <algorithm>
 #include <climits>
 
 namespace fgg {
@@ -275,6 +276,78 @@ __device__ __forceinline__ void kstep(Pass<T>& ps, const uint8_t* rd, uint8_t* w
   if ((kb & 63) == 63 && kb + 1 < ps.nkb) ps.load_b_scales(kb + 1, lane);
 }
 
+// The K loop of one pass (buffer resources, offsets and the b_scale row
+// set, accumulators zeroed).  Step 0's tiles and the b_scale row travel
+// together, unless their A tiles (a_pre) or B tiles and b_scale row (b_pre)
+// were issued early, with the steps the ring holds; the b_scale row is
+// waited for at once (load_b_scales), which also waits for step 0.  With 3
+// stages, step 1 is issued after that wait.
+template <class T>
+__device__ __forceinline__ void k_loop(Pass<T>& ps, uint8_t* lds0, uint8_t* lds1, uint8_t* lds2,
+                                       float* sa0, float* sa1, bool a_pre, bool b_pre, int lane,
+                                       int wave, int wm, int wn) {
+  const int nkb = ps.nkb;
+  if (!a_pre) {
+    ps.stage_a(lds0, 0, wave);
+    ps.stage_scales(sa0, 0, wave, lane);
+  }
+  if (!b_pre) {
+    ps.stage_b(lds0, 0, wave);
+    ps.load_b_scales(0, lane);
+  }
+  wait_vmem<0>();
+  asm volatile("" ::"v"(ps.bs_vec));
+  if constexpr (T::STAGES == 2) {
+    lds_barrier();
+    // K steps two at a time (LDS stage parity), scale chunks of SA_BLK
+    // steps alternate between sa0 and sa1.
+    for (int kb = 0; kb < nkb; kb += 2) {
+      const bool odd_chunk = ((unsigned)kb / T::SA_BLK) & 1;
+      float* sa_rd = odd_chunk ? sa1 : sa0;
+      float* sa_wr = odd_chunk ? sa0 : sa1;
+      kstep<T>(ps, lds0, lds1, sa_rd, sa_wr, kb, lane, wave, wm, wn);
+      if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa_rd, sa_wr, kb + 1, lane, wave, wm, wn);
+    }
+  } else {
+    if (nkb > 1) {
+      if (!a_pre) ps.stage_a(lds1, 1, wave);
+      if (!b_pre) ps.stage_b(lds1, 1, wave);
+    }
+    lds_barrier();
+    // Six steps per iteration: stage = kb % 3 and scale chunk kb / 3
+    // (alternating sa0 / sa1) are then known at compile time.
+    for (int kb = 0; kb < nkb; kb += 6) {
+      kstep<T>(ps, lds0, lds2, sa0, sa1, kb, lane, wave, wm, wn);
+      if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa0, sa1, kb + 1, lane, wave, wm, wn);
+      if (kb + 2 < nkb) kstep<T>(ps, lds2, lds1, sa0, sa1, kb + 2, lane, wave, wm, wn);
+      if (kb + 3 < nkb) kstep<T>(ps, lds0, lds2, sa1, sa0, kb + 3, lane, wave, wm, wn);
+      if (kb + 4 < nkb) kstep<T>(ps, lds1, lds0, sa1, sa0, kb + 4, lane, wave, wm, wn);
+      if (kb + 5 < nkb) kstep<T>(ps, lds2, lds1, sa1, sa0, kb + 5, lane, wave, wm, wn);
+    }
+  }
+}
+
+// Store the pass's rows of the accumulators as BF16: row r of the tile
+// (global row row0 + r) when store_row(r) holds, columns below N.  Lane
+// holds C[m][n .. n + 3].
+template <class T, class RowOk>
+__device__ __forceinline__ void epilogue(const Pass<T>& ps, uint16_t* C, int row0, int wcol0, int N,
+                                         int wm, int lane, RowOk store_row) {
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i) {
+    const int rl = wm * T::WM + i * 16 + (lane & 15);
+    if (!store_row(rl)) continue;
+    uint16_t* crow = C + (size_t)(row0 + rl) * N;
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) {
+      const int n = wcol0 + j * 16 + 4 * (lane >> 4);
+      if (n < N)
+        *reinterpret_cast<uint2*>(crow + n) =
+            pack_bf16x4(ps.acc[i][j][0], ps.acc[i][j][1], ps.acc[i][j][2], ps.acc[i][j][3]);
+    }
+  }
+}
+
 template <class T>
 __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
@@ -418,72 +491,78 @@ __global__ __launch_bounds__(T::THREADS) void fp8_grouped_kernel(
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) ps.acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-      // Step 0's tiles and the b_scale row travel together (unless issued
-      // early); the b_scale row is waited for at once (load_b_scales), which
-      // also waits for step 0.  With 3 stages, step 1 is issued after that
-      // wait.
-      if (!a_pre) {
-        ps.stage_a(lds0, 0, wave);
-        ps.stage_scales(sa0, 0, wave, lane);
-      }
-      if (!b_pre) {
-        ps.stage_b(lds0, 0, wave);
-        ps.load_b_scales(0, lane);
-      }
-      wait_vmem<0>();
-      asm volatile("" ::"v"(ps.bs_vec));
-      if constexpr (T::STAGES == 2) {
-        a_pre = false;
-        lds_barrier();
-        // K steps two at a time (LDS stage parity), scale chunks of SA_BLK
-        // steps alternate between sa0 and sa1.
-        for (int kb = 0; kb < nkb; kb += 2) {
-          const bool odd_chunk = ((unsigned)kb / T::SA_BLK) & 1;
-          float* sa_rd = odd_chunk ? sa1 : sa0;
-          float* sa_wr = odd_chunk ? sa0 : sa1;
-          kstep<T>(ps, lds0, lds1, sa_rd, sa_wr, kb, lane, wave, wm, wn);
-          if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa_rd, sa_wr, kb + 1, lane, wave, wm, wn);
-        }
-      } else {
-        if (nkb > 1) {
-          if (!a_pre) ps.stage_a(lds1, 1, wave);
-          if (!b_pre) ps.stage_b(lds1, 1, wave);
-        }
-        a_pre = b_pre = false;
-        lds_barrier();
-        // Six steps per iteration: stage = kb % 3 and scale chunk kb / 3
-        // (alternating sa0 / sa1) are then known at compile time.
-        for (int kb = 0; kb < nkb; kb += 6) {
-          kstep<T>(ps, lds0, lds2, sa0, sa1, kb, lane, wave, wm, wn);
-          if (kb + 1 < nkb) kstep<T>(ps, lds1, lds0, sa0, sa1, kb + 1, lane, wave, wm, wn);
-          if (kb + 2 < nkb) kstep<T>(ps, lds2, lds1, sa0, sa1, kb + 2, lane, wave, wm, wn);
-          if (kb + 3 < nkb) kstep<T>(ps, lds0, lds2, sa1, sa0, kb + 3, lane, wave, wm, wn);
-          if (kb + 4 < nkb) kstep<T>(ps, lds1, lds0, sa1, sa0, kb + 4, lane, wave, wm, wn);
-          if (kb + 5 < nkb) kstep<T>(ps, lds2, lds1, sa1, sa0, kb + 5, lane, wave, wm, wn);
-        }
-      }
+      k_loop<T>(ps, lds0, lds1, lds2, sa0, sa1, a_pre, b_pre, lane, wave, wm, wn);
+      a_pre = b_pre = false;
 
-      // Epilogue: this expert's rows only.  Lane holds C[m][n .. n+3].
-#pragma unroll
-      for (int i = 0; i < T::TM; ++i) {
-        const int rl = wm * T::WM + i * 16 + (lane & 15);
-        const int gr = row0 + rl;
-        if (gr >= M || ids[rl] != e) continue;
-        uint16_t* crow = C + (size_t)gr * N;
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) {
-          const int n = wcol0 + j * 16 + 4 * (lane >> 4);
-          if (n < N)
-            *reinterpret_cast<uint2*>(crow + n) =
-                pack_bf16x4(ps.acc[i][j][0], ps.acc[i][j][1], ps.acc[i][j][2], ps.acc[i][j][3]);
-        }
-      }
+      // Epilogue: this expert's rows only.
+      epilogue<T>(ps, C, row0, wcol0, N, wm, lane,
+                  [&](int rl) { return row0 + rl < M && ids[rl] == e; });
     }
     // No pass ran (a window of padding rows only, or a split item whose
     // expert has no row in the window): the early loads are still writing
     // the stages; let them land before the stages change hands or the
     // workgroup ends.
     if (a_pre || b_pre) wait_vmem<0>();
+  }
+}
+
+// A batch of independent dense FP8 GEMMs of different shapes in one launch
+// (the cutlass#3124 page's grouped block-scaled GEMM, "Intro": problems with
+// their own M, N and K).  Work item t belongs to the problem whose range
+// [tile_start[g], tile_start[g + 1]) holds it; inside a problem, tiles follow
+// the XCD-aware map_tile order.  Every tile is one pass of the same K loop
+// and epilogue as the grouped kernel's, with the problem's own K, offsets
+// and b_scale row; rows and columns past the problem's M and N read zeros
+// and are not stored.
+template <class T>
+__global__ __launch_bounds__(T::THREADS) void fp8_problems_kernel(const Fp8ProblemSet set,
+                                                                  int group_w) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[T::STAGES > 2 ? T::STAGE : 16];
+  __shared__ __attribute__((aligned(256))) float sa0[T::BM * T::SA_ROW];
+  __shared__ __attribute__((aligned(256))) float sa1[T::BM * T::SA_ROW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WAVES_N;
+  const int wn = wave % T::WAVES_N;
+  const int total = set.tile_start[set.count];
+  Pass<T> ps;
+
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    int g = 0;
+    while (g + 1 < set.count && set.tile_start[g + 1] <= tile) ++g;
+    const Fp8Problem& p = set.p[g];
+    const int M = p.M, N = p.N, K = p.K;
+    const int num_windows = (M + T::BM - 1) / T::BM;
+    const int num_ntiles = (N + T::BN - 1) / T::BN;
+    int window, ntile;
+    map_tile(tile - set.tile_start[g], set.tile_start[g + 1] - set.tile_start[g], num_windows,
+             num_ntiles, group_w, window, ntile);
+    const int row0 = window * T::BM;
+    const int col0 = ntile * T::BN;
+    const int rows_a = min(T::BM, M - row0);
+    const int rows_b = min(T::BN, N - col0);
+    const int wcol0 = col0 + wn * T::WN;
+
+    __syncthreads();  // the previous tile is done with the stages
+    ps.K = (uint32_t)K;
+    ps.nkb = K >> 7;
+    ps.lane_off = off::fp8_lane_off(wave, lane, (uint32_t)K);
+    ps.ra = rsrc(p.A + (size_t)row0 * K, (uint32_t)rows_a * (uint32_t)K);
+    ps.rsa = rsrc(p.a_scale + (size_t)row0 * ps.nkb, (uint32_t)rows_a * (uint32_t)ps.nkb * 4u);
+    ps.a_groups = ~0ull;
+    ps.active = wm * T::WM < rows_a;  // a wave whose rows are all past M computes nothing
+    ps.set_expert(p.B, p.b_scale, 0, N, col0, wcol0, rows_b);
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) ps.acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    k_loop<T>(ps, lds0, lds1, lds2, sa0, sa1, false, false, lane, wave, wm, wn);
+    epilogue<T>(ps, p.C, row0, wcol0, N, wm, lane, [&](int rl) { return rl < rows_a; });
   }
 }
 
@@ -528,12 +607,52 @@ hipError_t launch_cfg(const Fp8Args& a, const LaunchOpts& o, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Tile ranges of a problem batch for tile shape BM x BN.
+inline long long problem_tiles(Fp8ProblemSet& set, int BM, int BN) {
+  long long total = 0;
+  for (int g = 0; g < set.count; ++g) {
+    set.tile_start[g] = (int)total;
+    total += (long long)((set.p[g].M + BM - 1) / BM) * ((set.p[g].N + BN - 1) / BN);
+    if (total > INT_MAX) return -1;
+  }
+  set.tile_start[set.count] = (int)total;
+  return total;
+}
+
+template <class T>
+hipError_t launch_problems_cfg(Fp8ProblemSet set, const LaunchOpts& o, hipStream_t s) {
+  const long long total = problem_tiles(set, T::BM, T::BN);
+  if (total < 0) return hipErrorInvalidValue;
+  if (total == 0) return hipSuccess;
+  int grid = (int)total;
+  if (o.max_wg > 0 && o.max_wg < grid) grid = o.max_wg;
+  hipLaunchKernelGGL(fp8_problems_kernel<T>, dim3(grid), dim3(T::THREADS), 0, s, set, 4);
+  return hipGetLastError();
+}
+
 }  // namespace fp8_detail
 
 using namespace fp8_detail;
 
 int fp8_num_tiles() { return (int)(sizeof(kFp8Tiles) / sizeof(kFp8Tiles[0])); }
 const TileCfg& fp8_tile(int id) { return kFp8Tiles[id]; }
+
+hipError_t launch_fp8_problems(const Fp8ProblemSet& in, int tile_id, const LaunchOpts& o,
+                               hipStream_t s) {
+  if (in.count < 1 || in.count > kMaxProblems) return hipErrorInvalidValue;
+  // Longest K loops first (the order of the problems does not change any
+  // result): workgroups that draw the short tiles last even out the finish.
+  Fp8ProblemSet set = in;
+  std::stable_sort(set.p, set.p + set.count,
+                   [](const Fp8Problem& a, const Fp8Problem& b) { return a.K > b.K; });
+  switch (tile_id) {
+    case 0: return launch_problems_cfg<Cfg0>(set, o, s);
+    case 1: return launch_problems_cfg<Cfg1>(set, o, s);
+    case 2: return launch_problems_cfg<Cfg2>(set, o, s);
+    case 3: return launch_problems_cfg<Cfg3>(set, o, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_fp8(const Fp8Args& a, int tile_id, const LaunchOpts& o, hipStream_t s) {
   switch (tile_id) {

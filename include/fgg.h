@@ -167,6 +167,29 @@ typedef struct {
 fgg_status fp4_gemm_problems(const fgg_fp4_problem* problems, int count, void* stream);
 
 /*
+ * fp8_gemm_problems -- a batch of independent dense block-scaled FP8 GEMMs
+ * whose M, N and K may all differ, in one launch (the same "Intro" of the
+ * cutlass#3124 page, which names no number format; here the library's main
+ * FP8 form).  Problem g computes
+ *   C_g[i, n] = sum_kb a_scale_g[i, kb] * b_scale_g[n/128, kb] * sum_{k in kb} A_g[i,k] B_g[n,k]
+ * with the arithmetic of grouped_fp8_gemm at G = 1 with every row routed to
+ * expert 0 (so the same bits on the same tile config).  Descriptors, count,
+ * capture and error reporting as for fp4_gemm_problems; every problem must
+ * meet grouped_fp8_gemm's requirements (as at G = 1).  Problems must not
+ * write overlapping C.
+ */
+typedef struct {
+  const void* A;         /* [M, K] E4M3FN codes                               */
+  const void* B;         /* [N, K] E4M3FN codes                               */
+  const float* a_scale;  /* [M, K/128] FP32                                   */
+  const float* b_scale;  /* [N/128, K/128] FP32                               */
+  void* C;               /* [M, N] BF16, written in full                      */
+  int M, N, K;
+} fgg_fp8_problem;
+
+fgg_status fp8_gemm_problems(const fgg_fp8_problem* problems, int count, void* stream);
+
+/*
  * grouped_w4a16_gemm -- grouped GEMM of BF16 activations with NVFP4 weights
  * (W4A16), BF16 out: the decode / small-M path of the onnxruntime#29824 page
  * ("Code analysis 1": FP4 weights with 16-bit activations, dequantised).
@@ -357,6 +380,8 @@ fgg_status grouped_fp4_gemm_alpha_ex(const void* A, const void* B, const void* a
                                      const fgg_options* opt, void* stream);
 /* run_split is ignored (a batch has no routing). */
 fgg_status fp4_gemm_problems_ex(const fgg_fp4_problem* problems, int count,
+                                const fgg_options* opt, void* stream);
+fgg_status fp8_gemm_problems_ex(const fgg_fp8_problem* problems, int count,
                                 const fgg_options* opt, void* stream);
 
 /* ------------------------------------------------------------------------

@@ -166,6 +166,29 @@ def test_problem_batch_and_expert_alpha_validation():
     assert st == 1 and lib.fgg_last_error().decode().startswith("grouped_fp4_gemm_alpha:")
 
 
+def test_fp8_problem_batch_validation():
+    lib = fgg.load_library()
+    arr = (fgg._Fp8Problem * 3)()
+    for g in range(3):
+        arr[g] = fgg._Fp8Problem(P, P, P, P, P, 100, 256, 512)
+    assert lib.fp8_gemm_problems(arr, 0, None) == 1
+    assert "count" in lib.fgg_last_error().decode()
+    assert lib.fp8_gemm_problems(arr, fgg.MAX_PROBLEMS + 1, None) == 1
+    arr[1].K = 200
+    st = lib.fp8_gemm_problems(arr, 3, None)
+    msg = lib.fgg_last_error().decode()
+    assert st == 1 and "problem 1" in msg and "K % 128" in msg
+    arr[1].K = 512
+    arr[2].N = 192
+    st = lib.fp8_gemm_problems(arr, 3, None)
+    msg = lib.fgg_last_error().decode()
+    assert st == 2 and "problem 2" in msg  # N % 128 != 0: unsupported
+    arr[2].N = 256
+    arr[0].b_scale = P + 2
+    assert lib.fp8_gemm_problems(arr, 3, None) == 3
+    assert lib.fgg_last_error().decode().startswith("fp8_gemm_problems (problem 0):")
+
+
 def test_w4a16_validation():
     lib = fgg.load_library()
     st = lib.grouped_w4a16_gemm(P, P, P, P, 1.0, P, 16, 256, 200, 2, None)

@@ -26,6 +26,8 @@ are the MoE-shaped problems the kernels are measured and checked on:
                        grouped GEMM over different M, N, K): expert g has
                        multinomial(16384, uniform) rows and alternately
                        (N, K) = (4096, 7168) and (7168, 2048), seed 0
+  p8_problems_fp8      the same batch recipe with dense block-scaled FP8
+                       problems (fp8_gemm_problems), seed 0
 
 Padding rows (m_indices = -1) hold ordinary random data so that a kernel which
 wrongly computes them is caught.
@@ -217,11 +219,19 @@ def make(name: str, seed: int | None = None) -> dict:
             N, K = (4096, 7168) if g % 2 == 0 else (7168, 2048)
             probs.append(nvfp4_problem(None, int(m), N, K, 1, rng))
         return dict(kind="fp4_problems", problems=probs, G=len(probs))
+    if name == "p8_problems_fp8":
+        rng = np.random.default_rng(0 if seed is None else seed)
+        counts = rng.multinomial(16384, [1 / 8] * 8)
+        probs = []
+        for g, m in enumerate(counts):
+            N, K = (4096, 7168) if g % 2 == 0 else (7168, 2048)
+            probs.append(fp8_problem(np.zeros(int(m), np.int32), N, K, 1, rng))
+        return dict(kind="fp8_problems", problems=probs, G=len(probs))
     raise KeyError(name)
 
 
 def real_rows(problem: dict) -> int:
-    if problem["kind"] == "fp4_problems":
+    if problem["kind"] in ("fp4_problems", "fp8_problems"):
         return sum(q["M"] for q in problem["problems"])
     idx = problem.get("m_indices")
     if idx is None:
