@@ -851,6 +851,40 @@ def tput_sweep(args, torch):
     print(json.dumps(out), flush=True)
 
 
+def round_sweep(args, torch):
+    """Launch time against the number of tile rounds (tiles / workgroup
+    slots) on dense problems whose column count grows one round in eight at
+    a time: what a partly filled last round of tiles costs, for the ranker's
+    round term.  256x256 tiles, M = 2048 (8 row windows), N = 256 nt."""
+    import fp4_grouped_gemm_amd as fgg
+    from fp4_grouped_gemm_amd.util import run, to_device as to_dev
+    from workloads import fp8_problem, nvfp4_problem
+    cus = fgg.device_info()["num_cus"]
+    out = {"metric": "launch time against tile rounds, 256x256 tiles", "num_cus": cus,
+           "kinds": {}}
+    for kind, name, K in ((fgg.FP8, "fp8", 7168), (fgg.FP4, "fp4", 4608)):
+        rows = []
+        for nt in range(cus // 8, 2 * cus // 8 + 1, cus // 64):
+            rng = np.random.default_rng(nt)
+            N = 256 * nt
+            print(f"[bench] round sweep {name} N={N}", file=sys.stderr, flush=True)
+            if kind == fgg.FP8:
+                p = fp8_problem(np.zeros(2048, np.int32), N, K, 1, rng)
+            else:
+                p = nvfp4_problem(None, 2048, N, K, 1, rng)
+            d = to_dev(p)
+            C = torch.empty((p["M"], p["N"]), dtype=torch.bfloat16, device="cuda")
+            call = lambda: run(p, d, out=C, tile_id=0)  # noqa: E731
+            for _ in range(3):
+                call()
+            ms = min(time_launches(torch, call, 10, True)[0] for _ in range(3))
+            rows.append(dict(N=N, tiles=8 * nt, rounds=8 * nt / cus, us=round(ms * 1e3, 1)))
+            del d, C, p
+            torch.cuda.empty_cache()
+        out["kinds"][name] = dict(M=2048, K=K, rows=rows)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -881,6 +915,9 @@ def main():
                          "configs (the library's *_tune calls), report heuristic top-1 against "
                          "the best of the k, and the geomean loss; one JSON line")
     ap.add_argument("--top-k", type=int, default=4)
+    ap.add_argument("--round-sweep", action="store_true",
+                    help="time dense 256x256-tiled problems from one to two rounds of tiles in "
+                         "eighths (what a partly filled last round costs); one JSON line")
     ap.add_argument("--tput-sweep", action="store_true",
                     help="time every tile config on problems that fill whole waves for all of "
                          "them and print each config's throughput relative to the best (the "
@@ -940,6 +977,10 @@ def main():
 
     if args.tput_sweep:
         tput_sweep(args, torch)
+        return
+
+    if args.round_sweep:
+        round_sweep(args, torch)
         return
 
     if WORKLOADS[args.workload]["kind"] == "w4a16":

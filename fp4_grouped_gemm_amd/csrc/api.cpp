@@ -119,6 +119,19 @@ fgg_status check_common(const char* fn, const void* A, const void* B, const void
 }
 
 // ------------------------------------------------------------------ ranker
+// Time of `tiles` tiles on `slots` workgroup slots, in rounds of full-slot
+// time.  A partly filled last round, with a fraction f of the slots busy,
+// costs about kPartialRound + (1 - kPartialRound) f of a full round: its
+// workgroups run little faster than a full round's.  Measured on MI355X
+// (bench.py --round-sweep: 256x256 tiles of dense FP8 and NVFP4 problems
+// from one to two rounds in eighths; least-squares fits 0.66 and 0.61).
+constexpr double kPartialRound = 0.65;
+double round_cost(long long tiles, long long slots) {
+  const long long full = tiles / slots, rem = tiles % slots;
+  return (double)full +
+         (rem ? kPartialRound + (1.0 - kPartialRound) * (double)rem / (double)slots : 0.0);
+}
+
 // Score of a tile config, the tile-efficiency x wave-quantisation form of
 // the flashinfer#3948 page ("Code analysis 2"): m_eff * n_eff * throughput /
 // num_waves, with the terms defined for this device:
@@ -129,7 +142,8 @@ fgg_status check_common(const char* fn, const void* A, const void* B, const void
 //   n_eff     = N / (ceil(N / BN) * BN);
 //   num_waves = ceil(tiles / (CUs * wg_per_cu)), and the page's division by
 //               num_waves is normalised to the fraction of workgroup slots
-//               busy, tiles / (num_waves * CUs * wg_per_cu);
+//               busy, tiles / (rounds * CUs * wg_per_cu), where a partly
+//               filled last round counts by round_cost above, not whole;
 //   throughput= per-CU efficiency of the tile shape.
 // The page's 2-CTA and cluster-multicast factors have no gfx950 counterpart.
 float score_tile(const fgg::TileCfg& t, int M, int N, int G, int num_cus, int run_align,
@@ -145,9 +159,9 @@ float score_tile(const fgg::TileCfg& t, int M, int N, int G, int num_cus, int ru
   const long long tiles = row_tiles * ntiles;
   const long long slots = (long long)std::max(1, num_cus) * t.wg_per_cu;
   const long long num_waves = (tiles + slots - 1) / slots;
-  const double busy = (double)tiles / (double)(num_waves * slots);
   if (variant == FGG_SCORE_LITERAL)  // the page's printed form, for comparison
     return (float)(std::min(1.0, m_eff) * n_eff * t.tput / ((double)num_waves * t.block_n));
+  const double busy = (double)tiles / (round_cost(tiles, slots) * (double)slots);
   return (float)(std::min(1.0, m_eff) * n_eff * busy * t.tput);
 }
 
@@ -192,8 +206,8 @@ int tuned_tile(int kind, int M, int N, int K, int G) {
 // Tile for a call: the explicit option, else the recorded tuning result for
 // this shape, else the ranker's top choice.
 // Tile config for a problem batch: the ranker's terms summed over the
-// problems (useful over computed elements, busy fraction of the last wave of
-// tiles, per-CU efficiency of the shape).  Set: Fp4ProblemSet or
+// problems (useful over computed elements, busy fraction of the slots over
+// the rounds of tiles, per-CU efficiency of the shape).  Set: Fp4ProblemSet or
 // Fp8ProblemSet; tiles: the kind's config table.
 template <class Set>
 int rank_problems(const Set& set, int num_cus, int num_tiles, const fgg::TileCfg& (*tile_of)(int)) {
@@ -211,8 +225,8 @@ int rank_problems(const Set& set, int num_cus, int num_tiles, const fgg::TileCfg
       computed += (double)tg * t.block_m * t.block_n * set.p[g].K;
     }
     const long long slots = (long long)std::max(1, num_cus) * t.wg_per_cu;
-    const long long waves = (tiles + slots - 1) / slots;
-    const double score = useful / computed * ((double)tiles / (double)(waves * slots)) * t.tput;
+    const double busy = (double)tiles / (round_cost(tiles, slots) * (double)slots);
+    const double score = useful / computed * busy * t.tput;
     if (score > best_score) {
       best_score = score;
       best = i;

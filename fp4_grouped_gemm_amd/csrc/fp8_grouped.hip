@@ -569,20 +569,22 @@ __global__ __launch_bounds__(T::THREADS) void fp8_problems_kernel(const Fp8Probl
 // Compiled tile shapes.  `tput` is the relative per-CU throughput the ranker
 // uses, measured on MI355X by timing every shape on an 8192 x 8192 x 7168
 // problem that each of them tiles into whole waves of the 256 CUs (so the
-// ranker's other terms are 1): 2212, 1694, 1744 and 1375 TFLOPS (256x256
-// fastest per CU; the 4-wave shapes run one wave per SIMD and hide less
-// latency).  wg_per_cu follows from LDS use (the 3-stage shapes take
-// 100-153 KB, so one workgroup per CU).
+// ranker's other terms are 1): 2181, 1861, 1831 and 1416 TFLOPS.  256x256
+// is fastest per CU; the 128x128 shape runs one wave per SIMD and hides less
+// latency.  The 256x128 and 128x256 shapes run 8 waves of 64x64 (two per
+// SIMD): faster than 4 waves of 64x128 (1694 and 1744 TFLOPS), though each
+// wave reads more LDS bytes per MFMA.  wg_per_cu follows from LDS use (the
+// 3-stage shapes take 100-153 KB, so one workgroup per CU).
 using Cfg0 = Fp8Cfg<256, 256, 4, 2, 2, 8, 8>;  // 8 waves, 64x128 per wave, 2 x 64 KB stages
-using Cfg1 = Fp8Cfg<256, 128, 4, 1, 3, 3, 4>;  // 4 waves, 64x128 per wave, 3 x 48 KB stages
-using Cfg2 = Fp8Cfg<128, 256, 2, 2, 3, 3, 4>;  // 4 waves, 64x128 per wave, 3 x 48 KB stages
+using Cfg1 = Fp8Cfg<256, 128, 4, 2, 3, 3, 4>;  // 8 waves, 64x64 per wave,  3 x 48 KB stages
+using Cfg2 = Fp8Cfg<128, 256, 2, 4, 3, 3, 4>;  // 8 waves, 64x64 per wave,  3 x 48 KB stages
 using Cfg3 = Fp8Cfg<128, 128, 2, 2, 3, 3, 4>;  // 4 waves, 64x64 per wave,  3 x 32 KB stages
 
 const TileCfg kFp8Tiles[] = {
     {0, 256, 256, 8, 1, 1.00f},
-    {1, 256, 128, 4, 1, 0.77f},
-    {2, 128, 256, 4, 1, 0.79f},
-    {3, 128, 128, 4, 1, 0.62f},
+    {1, 256, 128, 8, 1, 0.85f},
+    {2, 128, 256, 8, 1, 0.84f},
+    {3, 128, 128, 4, 1, 0.65f},
 };
 
 template <class T>

@@ -228,7 +228,7 @@ static void check_w4a16(int M, int K) {
 }
 
 int main() {
-  const Fp8Cfg fp8[] = {{256, 256, 8, 8, 8}, {256, 128, 4, 3, 4}, {128, 256, 4, 3, 4},
+  const Fp8Cfg fp8[] = {{256, 256, 8, 8, 8}, {256, 128, 8, 3, 4}, {128, 256, 8, 3, 4},
                         {128, 128, 4, 3, 4}};
   for (const Fp8Cfg& c : fp8) {
     check_fp8_layout(c, c.BM);
