@@ -885,6 +885,49 @@ def round_sweep(args, torch):
     print(json.dumps(out), flush=True)
 
 
+def routing_sweep(args, torch):
+    """Grouped FP8 launch time of one 8192 x 4096 x 7168 problem under
+    different row routings, per tile config: what windows holding an expert
+    boundary cost.  Dense (one expert), runs of 2048/1024/256 rows aligned
+    to the 256-row windows, and two-expert runs of 128, 64 and 32 rows
+    alternating (every 256-row window then takes two passes, each filling
+    half of the window's rows, spread evenly (128) or not (64, 32) over the
+    wave rows), and c2's shape of boundary: 8 runs of 1024 shifted by 100
+    rows, so 7 of the 32 windows hold a boundary."""
+    import fp4_grouped_gemm_amd as fgg
+    from fp4_grouped_gemm_amd.util import to_device as to_dev
+    from workloads import fp8_problem
+    M, N, K = 8192, 4096, 7168
+    rows = np.arange(M)
+    routings = {
+        "dense": np.zeros(M, np.int32),
+        "runs1024_aligned": (rows // 1024).astype(np.int32),
+        "alt256": ((rows // 256) % 2).astype(np.int32),
+        "alt128": ((rows // 128) % 2).astype(np.int32),
+        "alt64": ((rows // 64) % 2).astype(np.int32),
+        "alt32": ((rows // 32) % 2).astype(np.int32),
+        "runs1024_shift100": np.minimum((rows + 100) // 1024, 7).astype(np.int32),
+    }
+    p = fp8_problem(np.zeros(M, np.int32), N, K, 8, np.random.default_rng(0))
+    d = to_dev(p)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    out = {"metric": "grouped FP8 launch time against the row routing", "M": M, "N": N, "K": K,
+           "tiles": {}}
+    for tile in range(fgg.num_tiles(fgg.FP8)):
+        row = {}
+        for name, ids in routings.items():
+            print(f"[bench] routing sweep tile {tile} {name}", file=sys.stderr, flush=True)
+            mi = torch.from_numpy(ids).cuda()
+            call = lambda: fgg.grouped_fp8_gemm(d["A"], d["B"], d["a_scale"], d["b_scale"], mi,  # noqa: E731
+                                                out=C, tile_id=tile)
+            for _ in range(3):
+                call()
+            ms = min(time_launches(torch, call, 10, True)[0] for _ in range(3))
+            row[name] = round(ms * 1e3, 1)
+        out["tiles"][str(tile)] = row
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -918,6 +961,9 @@ def main():
     ap.add_argument("--round-sweep", action="store_true",
                     help="time dense 256x256-tiled problems from one to two rounds of tiles in "
                          "eighths (what a partly filled last round costs); one JSON line")
+    ap.add_argument("--routing-sweep", action="store_true",
+                    help="time grouped FP8 on one shape under routings with and without expert "
+                         "boundaries inside the row windows, per tile config; one JSON line")
     ap.add_argument("--tput-sweep", action="store_true",
                     help="time every tile config on problems that fill whole waves for all of "
                          "them and print each config's throughput relative to the best (the "
@@ -981,6 +1027,10 @@ def main():
 
     if args.round_sweep:
         round_sweep(args, torch)
+        return
+
+    if args.routing_sweep:
+        routing_sweep(args, torch)
         return
 
     if WORKLOADS[args.workload]["kind"] == "w4a16":
