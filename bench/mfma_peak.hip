@@ -61,7 +61,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // ------------------------------------------------------------ 1. issue rate
-enum Shape { F8_16x16x128 = 0, F8_32x32x64 = 1, F16_16x16x32 = 2, F16_32x32x16 = 3 };
+enum Shape { F8_16x16x128 = 0, F8_32x32x64 = 1, F16_16x16x32 = 2, F16_32x32x16 = 3, F4_16x16x128 = 4 };
 constexpr int kChains = 8;
 
 template <int S>
@@ -70,6 +70,7 @@ template <> struct Acc<F8_16x16x128> { typedef f32x4 T; static constexpr double 
 template <> struct Acc<F8_32x32x64> { typedef f32x16 T; static constexpr double flop = 2.0 * 32 * 32 * 64; };
 template <> struct Acc<F16_16x16x32> { typedef f32x4 T; static constexpr double flop = 2.0 * 16 * 16 * 32; };
 template <> struct Acc<F16_32x32x16> { typedef f32x16 T; static constexpr double flop = 2.0 * 32 * 32 * 16; };
+template <> struct Acc<F4_16x16x128> { typedef f32x4 T; static constexpr double flop = 2.0 * 16 * 16 * 128; };
 
 template <int S>
 __device__ __forceinline__ typename Acc<S>::T mfma(typename Acc<S>::T c, i32x8 a8, f16x8 a16) {
@@ -77,6 +78,8 @@ __device__ __forceinline__ typename Acc<S>::T mfma(typename Acc<S>::T c, i32x8 a
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, a8, c, 0, 0, 0, 127, 0, 127);
   else if constexpr (S == F8_32x32x64)
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, a8, c, 0, 0, 0, 127, 0, 127);
+  else if constexpr (S == F4_16x16x128)  // E2M1 x E2M1 (format code 4), unit scales
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, a8, c, 4, 4, 0, 127, 0, 127);
   else if constexpr (S == F16_16x16x32)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a16, a16, c, 0, 0, 0);
   else
@@ -623,6 +626,72 @@ double run_stage(const unsigned char* A, const unsigned char* B, int* out, int c
   return ms * 1e3 / reps;  // us per launch
 }
 
+// ------------------------------------------------------ 8. VALU issue rate
+// Each wave: 8 independent chains of one instruction, `iters` rounds; the
+// output of a round is the next round's input (a chain per register), so
+// the loop measures issue throughput once the chains cover the latency.
+enum ValuOp { CVT_F16_FP4 = 0, CVT_F32_FP4 = 1, PK_MUL_F16 = 2, MUL_F32 = 3, CVT_F16_FP8 = 4, CVT_BF16_F32 = 5, PERM = 6 };
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+template <int OP>
+__global__ __launch_bounds__(512) void valu_rate(unsigned* out, long long* cyc, int iters) {
+  unsigned w[kChains];
+  for (int c = 0; c < kChains; ++c) w[c] = 0x3C003C00u + threadIdx.x * 7u + (unsigned)c;
+  const f16x2v kh = {(_Float16)1.0009765625f, (_Float16)1.0009765625f};
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) {
+      if constexpr (OP == CVT_F16_FP4)
+        w[c] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[c], 1.0f, 0));
+      else if constexpr (OP == CVT_F32_FP4)
+        w[c] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[c], 1.0f, 0)[0]);
+      else if constexpr (OP == PK_MUL_F16)
+        w[c] = __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2v, w[c]) * kh);
+      else if constexpr (OP == MUL_F32)
+        w[c] = __builtin_bit_cast(unsigned, __builtin_bit_cast(float, w[c]) * 1.0000001f);
+      else if constexpr (OP == CVT_F16_FP8)
+        w[c] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[c], 1.0f, false));
+      else if constexpr (OP == CVT_BF16_F32) {  // two FP32 values -> a rounded BF16 pair
+        const float f = __builtin_bit_cast(float, w[c]);
+        w[c] = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2v){f, f}, bf16x2v));
+      } else
+        w[c] = __builtin_amdgcn_perm(w[c], w[c] + 1u, 0x07060302u);
+    }
+  }
+  const long long t1 = __builtin_amdgcn_s_memtime();
+  unsigned x = 0;
+  for (int c = 0; c < kChains; ++c) x ^= w[c];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = x;
+  if ((threadIdx.x & 63) == 0) cyc[blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)] = t1 - t0;
+}
+
+// Cycles per instruction per SIMD (waves_per_simd waves each issuing
+// iters x kChains of them).
+template <int OP>
+double run_valu(int cus, int waves_per_simd) {
+  const int threads = 256 * waves_per_simd;
+  const int iters = 4000;
+  const int nw = cus * threads / 64;
+  unsigned* out;
+  long long* cyc;
+  CHECK(hipMalloc(&out, sizeof(unsigned) * cus * threads));
+  CHECK(hipMalloc(&cyc, sizeof(long long) * nw));
+  hipLaunchKernelGGL(valu_rate<OP>, dim3(cus), dim3(threads), 0, 0, out, cyc, 200);  // warm-up
+  CHECK(hipDeviceSynchronize());
+  hipLaunchKernelGGL(valu_rate<OP>, dim3(cus), dim3(threads), 0, 0, out, cyc, iters);
+  CHECK(hipDeviceSynchronize());
+  std::vector<long long> c(nw);
+  CHECK(hipMemcpy(c.data(), cyc, sizeof(long long) * nw, hipMemcpyDeviceToHost));
+  double cs = 0;
+  for (int i = 0; i < nw; ++i) cs += (double)c[i];
+  CHECK(hipFree(out));
+  CHECK(hipFree(cyc));
+  return cs / nw / ((double)iters * kChains * waves_per_simd);
+}
+
 int main() {
   hipDeviceProp_t p;
   CHECK(hipGetDeviceProperties(&p, 0));
@@ -632,13 +701,15 @@ int main() {
   std::fflush(stdout);
   const char* names[] = {"v_mfma_scale_f32_16x16x128_f8f6f4 (FP8)",
                          "v_mfma_scale_f32_32x32x64_f8f6f4 (FP8)",
-                         "v_mfma_f32_16x16x32_f16", "v_mfma_f32_32x32x16_f16"};
+                         "v_mfma_f32_16x16x32_f16", "v_mfma_f32_32x32x16_f16",
+                         "v_mfma_scale_f32_16x16x128_f8f6f4 (FP4 E2M1)"};
   std::printf("\n## 1. MFMA issue rate (8 independent chains per wave, every CU)\n");
   std::printf("instruction | waves/SIMD | cycles per MFMA per SIMD | shader clock GHz | PFLOP/s\n");
   for (int w = 1; w <= 2; ++w) {
-    RateResult r[4] = {run_rate<F8_16x16x128>(cus, w), run_rate<F8_32x32x64>(cus, w),
-                       run_rate<F16_16x16x32>(cus, w), run_rate<F16_32x32x16>(cus, w)};
-    for (int s = 0; s < 4; ++s)
+    RateResult r[5] = {run_rate<F8_16x16x128>(cus, w), run_rate<F8_32x32x64>(cus, w),
+                       run_rate<F16_16x16x32>(cus, w), run_rate<F16_32x32x16>(cus, w),
+                       run_rate<F4_16x16x128>(cus, w)};
+    for (int s = 0; s < 5; ++s)
       std::printf("%s | %d | %.1f | %.2f | %.2f\n", names[s], w, r[s].cyc_per_mfma, r[s].ghz,
                   r[s].pflops);
     std::fflush(stdout);
@@ -674,6 +745,20 @@ int main() {
   std::fflush(stdout);
   std::printf("\n## 7. Launch floor and dependent-load round trip (100 launches)\n");
   run_latency();
+
+  std::printf("\n## 8. VALU issue rate (8 independent chains per wave, every CU)\n");
+  std::printf("instruction | cycles per instruction per SIMD, 1 wave/SIMD | 2 waves/SIMD\n");
+  auto vrow = [](const char* name, double a, double b) {
+    std::printf("%s | %.1f | %.1f\n", name, a, b);
+    std::fflush(stdout);
+  };
+  vrow("v_cvt_scalef32_pk_f16_fp4", run_valu<CVT_F16_FP4>(cus, 1), run_valu<CVT_F16_FP4>(cus, 2));
+  vrow("v_cvt_scalef32_pk_f32_fp4", run_valu<CVT_F32_FP4>(cus, 1), run_valu<CVT_F32_FP4>(cus, 2));
+  vrow("v_cvt_scalef32_pk_f16_fp8", run_valu<CVT_F16_FP8>(cus, 1), run_valu<CVT_F16_FP8>(cus, 2));
+  vrow("v_pk_mul_f16", run_valu<PK_MUL_F16>(cus, 1), run_valu<PK_MUL_F16>(cus, 2));
+  vrow("v_mul_f32", run_valu<MUL_F32>(cus, 1), run_valu<MUL_F32>(cus, 2));
+  vrow("v_cvt_pk_bf16_f32", run_valu<CVT_BF16_F32>(cus, 1), run_valu<CVT_BF16_F32>(cus, 2));
+  vrow("v_perm_b32 (+ v_add_u32)", run_valu<PERM>(cus, 1), run_valu<PERM>(cus, 2));
 
   std::printf("\n## 5. L2 -> LDS staging of 256x256 tiles (loads only), grouped FP8 MoE prefill shape\n");
   std::printf("(2 tiles per CU x 56 K steps of 128; 64 KB per step per CU)\n");

@@ -70,9 +70,9 @@ static_assert(kWRows * 16 <= 1024, "a wave's scale bytes fit one load");
 // The two codes of byte H times s, as a BF16 pair.  q * s has at most 6
 // significant bits, so its FP32 value carries no bits below the top 16 and
 // BF16 is that upper half exactly: a byte permute takes the upper halves of
-// the two products (no rounding convert, which issues at a quarter of the
-// multiply rate).  A NaN scale code gives the quiet NaN 0x7FC00000, whose
-// upper half is a BF16 NaN.
+// the two products (one instruction per pair, as a rounding convert would
+// be; no rounding is needed).  A NaN scale code gives the quiet NaN
+// 0x7FC00000, whose upper half is a BF16 NaN.
 template <int H>
 __device__ __forceinline__ void dequant2(uint32_t word, float s, bf16x8& r) {
   const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, H);  // byte H
