@@ -692,6 +692,57 @@ double run_valu(int cus, int waves_per_simd) {
   return cs / nw / ((double)iters * kChains * waves_per_simd);
 }
 
+// ------------------------------------- 9. MFMAs with VALU work between them
+// Each wave: 8 independent FP16 16x16x32 MFMA chains and, after each MFMA,
+// V independent v_pk_mul_f16 on registers the MFMAs do not touch: whether
+// VALU instructions issue in the shadow of the matrix pipe.
+template <int V>
+__global__ __launch_bounds__(512) void mfma_valu(float* out, long long* cyc, int iters) {
+  f32x4 acc[kChains];
+  for (int c = 0; c < kChains; ++c) acc[c] = f32x4{};
+  f16x8 a16;
+  for (int i = 0; i < 8; ++i) a16[i] = (_Float16)0.25f;
+  f16x2v h[8];
+  for (int i = 0; i < 8; ++i) h[i] = (f16x2v){(_Float16)(1.0f + 0.01f * i), (_Float16)1.0f};
+  const f16x2v k = {(_Float16)1.0009765625f, (_Float16)1.0009765625f};
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) {
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a16, a16, acc[c], 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < V; ++v) h[(c * V + v) & 7] = h[(c * V + v) & 7] * k;
+    }
+  }
+  const long long t1 = __builtin_amdgcn_s_memtime();
+  float s = 0.f;
+  for (int c = 0; c < kChains; ++c) s += acc[c][0];
+  for (int i = 0; i < 8; ++i) s += (float)h[i][0];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+  if ((threadIdx.x & 63) == 0) cyc[blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)] = t1 - t0;
+}
+
+// Cycles per MFMA per SIMD at two waves per SIMD.
+template <int V>
+double run_mfma_valu(int cus) {
+  const int threads = 512, iters = 4000, nw = cus * threads / 64;
+  float* out;
+  long long* cyc;
+  CHECK(hipMalloc(&out, sizeof(float) * cus * threads));
+  CHECK(hipMalloc(&cyc, sizeof(long long) * nw));
+  hipLaunchKernelGGL(mfma_valu<V>, dim3(cus), dim3(threads), 0, 0, out, cyc, 200);  // warm-up
+  CHECK(hipDeviceSynchronize());
+  hipLaunchKernelGGL(mfma_valu<V>, dim3(cus), dim3(threads), 0, 0, out, cyc, iters);
+  CHECK(hipDeviceSynchronize());
+  std::vector<long long> c(nw);
+  CHECK(hipMemcpy(c.data(), cyc, sizeof(long long) * nw, hipMemcpyDeviceToHost));
+  double cs = 0;
+  for (int i = 0; i < nw; ++i) cs += (double)c[i];
+  CHECK(hipFree(out));
+  CHECK(hipFree(cyc));
+  return cs / nw / ((double)iters * kChains * 2);
+}
+
 int main() {
   hipDeviceProp_t p;
   CHECK(hipGetDeviceProperties(&p, 0));
@@ -759,6 +810,15 @@ int main() {
   vrow("v_mul_f32", run_valu<MUL_F32>(cus, 1), run_valu<MUL_F32>(cus, 2));
   vrow("v_cvt_pk_bf16_f32", run_valu<CVT_BF16_F32>(cus, 1), run_valu<CVT_BF16_F32>(cus, 2));
   vrow("v_perm_b32 (+ v_add_u32)", run_valu<PERM>(cus, 1), run_valu<PERM>(cus, 2));
+
+  std::printf("\n## 9. FP16 MFMAs with independent VALU work between them (2 waves/SIMD)\n");
+  std::printf("v_pk_mul_f16 per MFMA | cycles per MFMA per SIMD\n");
+  std::printf("0 | %.1f\n", run_mfma_valu<0>(cus));
+  std::printf("1 | %.1f\n", run_mfma_valu<1>(cus));
+  std::printf("2 | %.1f\n", run_mfma_valu<2>(cus));
+  std::printf("3 | %.1f\n", run_mfma_valu<3>(cus));
+  std::printf("4 | %.1f\n", run_mfma_valu<4>(cus));
+  std::fflush(stdout);
 
   std::printf("\n## 5. L2 -> LDS staging of 256x256 tiles (loads only), grouped FP8 MoE prefill shape\n");
   std::printf("(2 tiles per CU x 56 K steps of 128; 64 KB per step per CU)\n");
