@@ -270,6 +270,11 @@ __global__ __launch_bounds__(512) void gemm_loop(float* out, long long* cyc, int
   const long long t0 = __builtin_amdgcn_s_memtime();
   for (int step = 0; step < steps; ++step) {
     i32x8 bf = bf0;
+    // Without LDS reads the fragments would not change from column to
+    // column or step to step, and with the promotion (MFMA results not
+    // chained) the compiler would share and hoist the MFMAs: vary one B
+    // word per step and per column block.
+    if constexpr (!(MODE & 1) && (MODE & 4)) bf[0] ^= step & 1;
     if constexpr (MODE & 1) {
       bf = frag(B, wn * 128, lane);
 #pragma unroll
@@ -285,6 +290,7 @@ __global__ __launch_bounds__(512) void gemm_loop(float* out, long long* cyc, int
         if (i == 0) {
           if (j > 0) bf = bnext;
           if ((MODE & 1) && j + 1 < TN) bnext = frag(B, wn * 128 + (j + 1) * 16, lane);
+          if (!(MODE & 1) && (MODE & 4) && j + 1 < TN) bnext[1] ^= 1 << (j + 1);
         }
         if constexpr (MODE & 4)
           ring[t % (LAG + 1)] =
