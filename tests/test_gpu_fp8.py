@@ -54,6 +54,10 @@ EDGE = {
     "more_experts_than_rows": lambda: _prob(np.random.default_rng(11).integers(-1, 300, 400), G=300),
     "K128_N128": lambda: _prob([0] * 10 + [1] * 10, N=128, K=128),
     "N_not_tile_multiple": lambda: _prob([0] * 100 + [1] * 200, N=384, K=256),
+    # K steps a multiple of the 3-stage loop's six-step unroll, and an odd
+    # count below it, each with a run boundary inside a window
+    "K768_six_steps": lambda: _prob([0] * 70 + [1] * 90, K=768),
+    "K384_three_steps": lambda: _prob([0] * 130 + [1] * 70, K=384),
 }
 
 
